@@ -1,0 +1,455 @@
+// libspec C ABI: argument validation, workspace layout and kernel dispatch.
+// Every compute call validates on the host first and launches nothing on an
+// error.  No call allocates device memory or synchronises the host.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "../../include/spec.h"
+#include "spec_kernels.h"
+
+using namespace spec;
+
+struct spec_model {
+    spec_model_desc d;
+    spec_weights w;
+    int D;      // (hq + 2 hkv) * hd
+    int qd;     // hq * hd
+    int xs;     // activation element size (4 f32, 2 bf16)
+};
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+spec_status fail(spec_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+spec_status hip_fail(hipError_t e, const char *where) {
+    return fail(SPEC_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace layout for R activation rows and sets of at most G layers.
+struct Carve {
+    size_t h, h0, abuf, xn, q, o, act, pacc, pml, pval, pidx, total;
+};
+
+Carve carve(const spec_model *m, int batch, int max_m, int G) {
+    const size_t R = (size_t)batch * max_m;
+    const size_t d = m->d.d_model, xs = m->xs;
+    const size_t hq = m->d.n_q_heads, hd = m->d.head_dim;
+    const size_t prow = R < 64 ? R : 64;
+    const size_t nparts = (size_t)gemv_grid((m->d.vocab + 1) / 2);
+    Carve c{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+    c.h = take(R * d * 4);
+    c.h0 = take(R * d * 4);
+    c.abuf = take((size_t)G * R * d * 4);
+    c.xn = take((size_t)G * R * d * xs);
+    c.q = take((size_t)G * R * hq * hd * 4);
+    c.o = take((size_t)G * R * hq * hd * xs);
+    c.act = take(R * (size_t)m->d.d_ffn * xs);
+    c.pacc = take((size_t)attention_split_max() * G * prow * hq * hd * 4);
+    c.pml = take((size_t)attention_split_max() * G * prow * hq * 2 * 4);
+    c.pval = take((size_t)batch * nparts * 4);
+    c.pidx = take((size_t)batch * nparts * 4);
+    c.total = off;
+    return c;
+}
+
+template <typename P> P *at(void *ws, size_t off) { return reinterpret_cast<P *>(reinterpret_cast<char *>(ws) + off); }
+
+const void *layer_ptr(const void *base, size_t layer, size_t elems_per_layer, int xs) {
+    return reinterpret_cast<const char *>(base) + layer * elems_per_layer * xs;
+}
+
+// Everything a forward over R = batch * mseq rows needs.
+struct Fwd {
+    const spec_model *m;
+    const spec_kv *kv;
+    int batch, mseq, max_pos;
+    RowMap rows;
+    void *ws;
+    Carve c;
+    hipStream_t s;
+};
+
+// Weight-streaming product over rows chunked by the kernel's row limit.
+hipError_t gemv_chunked(const spec_model *m, GemvParams p, int Mtot, hipStream_t s) {
+    const int mr = gemv_max_rows();
+    const int grid = gemv_grid(p.n_units);
+    for (int m0 = 0; m0 < Mtot; m0 += mr) {
+        p.m0 = m0;
+        p.M = (Mtot - m0) < mr ? (Mtot - m0) : mr;
+        hipError_t e = launch_gemv(m->d.dtype, p, grid, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// One stage: attention of the set [l0, l0 + n) on the stage input h0, then
+// the set's MLPs.  A stage of one layer is the ordinary decoder layer.
+hipError_t run_stage(const Fwd &f, int l0, int n, int mlp_mode) {
+    const spec_model *m = f.m;
+    const spec_model_desc &d = m->d;
+    const int R = f.batch * f.mseq;
+    const int dm = d.d_model, D = m->D, qd = m->qd, xs = m->xs;
+    const bool par = mlp_mode == SPEC_MLP_PARALLEL && n > 1;
+    float *h = at<float>(f.ws, f.c.h);
+    float *h0 = at<float>(f.ws, f.c.h0);
+    float *abuf = at<float>(f.ws, f.c.abuf);
+    void *xn = at<char>(f.ws, f.c.xn);
+    float *q = at<float>(f.ws, f.c.q);
+    void *o = at<char>(f.ws, f.c.o);
+    void *act = at<char>(f.ws, f.c.act);
+    hipError_t e;
+
+    // 1. one RMS of h0, N gains -> xn[i]
+    NormParams np{};
+    np.h = h; np.add = nullptr; np.src0 = nullptr; np.h0copy = par ? h0 : nullptr;
+    np.gains = m->w.attn_norm + (size_t)l0 * dm;
+    np.n_gains = n; np.gain_stride = dm;
+    np.xn = xn; np.xn_sel_stride = (int64_t)R * dm;
+    np.M = R; np.d = dm; np.eps = d.rms_eps; np.gather_mseq = 0; np.gather_ntok = nullptr;
+    if ((e = launch_norm(d.dtype, np, f.s)) != hipSuccess) return e;
+
+    // 2. grouped QKV + RoPE + KV append over the N layers' concatenated rows
+    GemvParams gp{};
+    gp.W = layer_ptr(m->w.wqkv, l0, (size_t)D * dm, xs);
+    gp.K = dm; gp.n_units = n * D / 2; gp.pair_block = d.head_dim; gp.rows_per_sel = D;
+    gp.X = xn; gp.x_sel_stride = (int64_t)R * dm;
+    gp.bias = m->w.bqkv ? m->w.bqkv + (size_t)l0 * D : nullptr;
+    gp.epi = EPI_QKV_ROPE;
+    gp.q_out = q; gp.q_sel_stride = (int64_t)R * qd;
+    gp.kc = f.kv->k; gp.vc = f.kv->v; gp.layer0 = l0; gp.batch = f.batch;
+    gp.hq = d.n_q_heads; gp.hkv = d.n_kv_heads; gp.hd = d.head_dim; gp.rope_theta = d.rope_theta;
+    gp.rows = f.rows;
+    if ((e = gemv_chunked(m, gp, R, f.s)) != hipSuccess) return e;
+
+    // 3. grouped attention
+    AttnParams ap{};
+    ap.q = q; ap.q_sel_stride = (int64_t)R * qd;
+    ap.kc = f.kv->k; ap.vc = f.kv->v; ap.layer0 = l0; ap.n_group = n; ap.batch = f.batch;
+    ap.hq = d.n_q_heads; ap.hkv = d.n_kv_heads; ap.hd = d.head_dim; ap.capacity = f.kv->capacity;
+    ap.rows = f.rows; ap.max_pos = f.max_pos;
+    ap.splits = attention_splits(n, f.batch, d.n_q_heads, d.n_kv_heads, f.mseq, f.max_pos);
+    ap.o = o; ap.o_sel_stride = (int64_t)R * qd;
+    ap.part_acc = at<float>(f.ws, f.c.pacc); ap.part_ml = at<float>(f.ws, f.c.pml); ap.Mtot = R;
+    if ((e = launch_attention(d.dtype, ap, f.s)) != hipSuccess) return e;
+
+    // 4. grouped O projection -> a_i
+    gp = GemvParams{};
+    gp.W = layer_ptr(m->w.wo, l0, (size_t)dm * qd, xs);
+    gp.K = qd; gp.n_units = n * dm / 2; gp.pair_block = 2; gp.rows_per_sel = dm;
+    gp.X = o; gp.x_sel_stride = (int64_t)R * qd;
+    gp.epi = EPI_STORE; gp.out = abuf; gp.out_ld = dm; gp.out_sel_stride = (int64_t)R * dm;
+    if ((e = gemv_chunked(m, gp, R, f.s)) != hipSuccess) return e;
+
+    // 5. MLPs in set order
+    for (int i = 0; i < n; ++i) {
+        const int l = l0 + i;
+        np = NormParams{};
+        np.h = h; np.add = abuf + (size_t)i * R * dm; np.src0 = par ? h0 : nullptr; np.h0copy = nullptr;
+        np.gains = m->w.ffn_norm + (size_t)l * dm; np.n_gains = 1; np.gain_stride = dm;
+        np.xn = xn; np.xn_sel_stride = 0; np.M = R; np.d = dm; np.eps = d.rms_eps;
+        if ((e = launch_norm(d.dtype, np, f.s)) != hipSuccess) return e;
+
+        gp = GemvParams{};
+        gp.W = layer_ptr(m->w.w_gate_up, l, (size_t)2 * d.d_ffn * dm, xs);
+        gp.K = dm; gp.n_units = d.d_ffn; gp.pair_block = 2 * d.d_ffn; gp.rows_per_sel = 2 * d.d_ffn;
+        gp.X = xn; gp.x_sel_stride = 0;
+        gp.epi = EPI_SILU_MUL; gp.act = act; gp.act_ld = d.d_ffn;
+        if ((e = gemv_chunked(m, gp, R, f.s)) != hipSuccess) return e;
+
+        gp = GemvParams{};
+        gp.W = layer_ptr(m->w.w_down, l, (size_t)dm * d.d_ffn, xs);
+        gp.K = d.d_ffn; gp.n_units = dm / 2; gp.pair_block = 2; gp.rows_per_sel = dm;
+        gp.X = act; gp.x_sel_stride = 0;
+        gp.epi = EPI_RESID_ADD; gp.out = h; gp.out_ld = dm;
+        if ((e = gemv_chunked(m, gp, R, f.s)) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// Final norm (optionally of the last valid row of each sequence) + lm head.
+hipError_t run_head(const Fwd &f, bool last_only, const int32_t *ntok, float *logits, int64_t logits_ld,
+                    float inv_temp, uint64_t seed, const int32_t *samp_pos, const int32_t *samp_ntok,
+                    int32_t *token_out, int token_stride) {
+    const spec_model *m = f.m;
+    const int dm = m->d.d_model;
+    const int R = f.batch * f.mseq;
+    const int Mh = last_only ? f.batch : R;
+    NormParams np{};
+    np.h = at<float>(f.ws, f.c.h);
+    np.gains = m->w.final_norm; np.n_gains = 1; np.gain_stride = dm;
+    np.xn = at<char>(f.ws, f.c.xn); np.xn_sel_stride = 0; np.M = Mh; np.d = dm; np.eps = m->d.rms_eps;
+    np.gather_mseq = last_only ? f.mseq : 0; np.gather_ntok = ntok;
+    hipError_t e = launch_norm(m->d.dtype, np, f.s);
+    if (e != hipSuccess) return e;
+    GemvParams gp{};
+    gp.W = m->w.lm_head; gp.K = dm; gp.n_units = m->d.vocab / 2; gp.pair_block = 2; gp.rows_per_sel = m->d.vocab;
+    gp.X = np.xn; gp.x_sel_stride = 0;
+    gp.epi = token_out ? EPI_LOGITS : EPI_STORE;
+    gp.out = logits; gp.out_ld = logits_ld; gp.out_sel_stride = 0;
+    gp.inv_temp = inv_temp; gp.seed = seed; gp.samp_pos = samp_pos; gp.samp_ntok = samp_ntok;
+    gp.part_val = at<float>(f.ws, f.c.pval); gp.part_idx = at<int32_t>(f.ws, f.c.pidx);
+    const int grid = gemv_grid(gp.n_units);
+    if (!token_out && !logits) return hipSuccess;
+    if ((e = gemv_chunked(m, gp, Mh, f.s)) != hipSuccess) return e;
+    if (token_out) return launch_sample_reduce(gp.part_val, gp.part_idx, grid, Mh, token_out, token_stride, f.s);
+    return hipSuccess;
+}
+
+spec_status check_model(const spec_model *m, const spec_kv *kv, int batch) {
+    if (!m) return fail(SPEC_ERR_INVALID_ARG, "model is NULL");
+    if (!kv || !kv->k || !kv->v) return fail(SPEC_ERR_INVALID_ARG, "kv cache pointers are NULL");
+    if (batch < 1 || batch > kv->batch) return fail(SPEC_ERR_SHAPE, "batch %d outside [1, kv batch %d]", batch, kv->batch);
+    if (kv->capacity < 1) return fail(SPEC_ERR_SHAPE, "kv capacity %d < 1", kv->capacity);
+    return SPEC_OK;
+}
+
+spec_status check_ws(const spec_model *m, int batch, int max_m, int G, void *ws, size_t ws_bytes) {
+    const size_t need = spec_workspace_bytes(m, batch, max_m, G);
+    if (!ws || ws_bytes < need)
+        return fail(SPEC_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+    return SPEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *spec_version(void) { return "0.1.0 gfx950"; }
+const char *spec_last_error(void) { return g_err; }
+
+const char *spec_status_string(spec_status s) {
+    switch (s) {
+    case SPEC_OK: return "ok";
+    case SPEC_ERR_INVALID_ARG: return "invalid argument";
+    case SPEC_ERR_SHAPE: return "unsupported shape";
+    case SPEC_ERR_VOCAB_MISMATCH: return "draft and base vocabularies differ";
+    case SPEC_ERR_PLAN: return "invalid layer plan";
+    case SPEC_ERR_CAPACITY: return "KV capacity exceeded";
+    case SPEC_ERR_WORKSPACE: return "workspace too small";
+    case SPEC_ERR_HIP: return "HIP error";
+    case SPEC_ERR_UNSUPPORTED: return "unsupported";
+    }
+    return "unknown status";
+}
+
+spec_status spec_model_create(const spec_model_desc *desc, const spec_weights *w, spec_model **out) {
+    if (!desc || !w || !out) return fail(SPEC_ERR_INVALID_ARG, "NULL argument");
+    const spec_model_desc &d = *desc;
+    if (d.n_layers < 1 || d.d_model < 8 || d.n_q_heads < 1 || d.n_kv_heads < 1 || d.d_ffn < 8 || d.vocab < 2)
+        return fail(SPEC_ERR_SHAPE, "non-positive model dimension");
+    if (d.dtype != SPEC_F32 && d.dtype != SPEC_BF16) return fail(SPEC_ERR_INVALID_ARG, "dtype %d", d.dtype);
+    if (d.head_dim != 16 && d.head_dim != 32 && d.head_dim != 64 && d.head_dim != 128)
+        return fail(SPEC_ERR_UNSUPPORTED, "head_dim %d not in {16, 32, 64, 128}", d.head_dim);
+    if (d.n_q_heads % d.n_kv_heads) return fail(SPEC_ERR_SHAPE, "n_q_heads %% n_kv_heads != 0");
+    if (d.d_model % 8 || d.d_ffn % 8 || (d.n_q_heads * d.head_dim) % 8)
+        return fail(SPEC_ERR_SHAPE, "d_model, d_ffn and n_q_heads*head_dim must be multiples of 8");
+    if (d.d_model > 16384) return fail(SPEC_ERR_UNSUPPORTED, "d_model %d > 16384", d.d_model);
+    if (d.vocab % 2) return fail(SPEC_ERR_SHAPE, "vocab must be even");
+    if (d.has_qkv_bias && !w->bqkv) return fail(SPEC_ERR_INVALID_ARG, "has_qkv_bias but bqkv is NULL");
+    if (!w->embed || !w->attn_norm || !w->wqkv || !w->wo || !w->ffn_norm || !w->w_gate_up || !w->w_down ||
+        !w->final_norm || !w->lm_head)
+        return fail(SPEC_ERR_INVALID_ARG, "a weight pointer is NULL");
+    if (!(d.rms_eps > 0.f) || !(d.rope_theta > 1.f)) return fail(SPEC_ERR_INVALID_ARG, "rms_eps / rope_theta");
+    spec_model *m = new spec_model;
+    m->d = d;
+    m->w = *w;
+    if (!d.has_qkv_bias) m->w.bqkv = nullptr;
+    m->D = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim;
+    m->qd = d.n_q_heads * d.head_dim;
+    m->xs = d.dtype == SPEC_BF16 ? 2 : 4;
+    *out = m;
+    return SPEC_OK;
+}
+
+void spec_model_destroy(spec_model *m) { delete m; }
+
+spec_status spec_check_pair(const spec_model *draft, const spec_model *base) {
+    if (!draft || !base) return fail(SPEC_ERR_INVALID_ARG, "NULL model");
+    if (draft->d.vocab != base->d.vocab)
+        return fail(SPEC_ERR_VOCAB_MISMATCH, "draft vocab %d != base vocab %d", draft->d.vocab, base->d.vocab);
+    return SPEC_OK;
+}
+
+spec_status spec_default_group_plan(int L, int N, int32_t *offs, int max_offsets, int *n_stages_out) {
+    if (L < 1 || N < 1 || !offs || !n_stages_out) return fail(SPEC_ERR_INVALID_ARG, "bad plan arguments");
+    // set starts: layer 0, every intermediate layer l with l / N != (l - 1) / N
+    // (and layer 1), the last layer; then the end marker L
+    std::vector<int32_t> u;
+    u.push_back(0);
+    for (int l = 1; l < L - 1; ++l)
+        if (l == 1 || l / N != (l - 1) / N) u.push_back(l);
+    if (L > 1) u.push_back(L - 1);
+    u.push_back(L);
+    if ((int)u.size() > max_offsets) return fail(SPEC_ERR_INVALID_ARG, "offsets buffer too small (%zu)", u.size());
+    for (size_t i = 0; i < u.size(); ++i) offs[i] = u[i];
+    *n_stages_out = (int)u.size() - 1;
+    return SPEC_OK;
+}
+
+size_t spec_workspace_bytes(const spec_model *m, int batch, int max_m, int max_group) {
+    if (!m || batch < 1 || max_m < 1 || max_group < 1) return 0;
+    return carve(m, batch, max_m, max_group).total;
+}
+
+spec_status spec_draft_group_step(const spec_model *draft, const spec_kv *kv, const int32_t *plan_offsets,
+                                  int n_stages, int flags, int batch, const int32_t *tokens, int tokens_stride,
+                                  const int32_t *positions, int max_pos, float inv_temperature, uint64_t seed,
+                                  float *logits_out, int64_t logits_stride, int32_t *token_out,
+                                  int token_out_stride, void *workspace, size_t ws_bytes, void *stream) {
+    spec_status st = check_model(draft, kv, batch);
+    if (st) return st;
+    if (!plan_offsets || n_stages < 1) return fail(SPEC_ERR_PLAN, "empty plan");
+    if (flags != SPEC_MLP_SEQUENTIAL && flags != SPEC_MLP_PARALLEL) return fail(SPEC_ERR_INVALID_ARG, "flags %d", flags);
+    if (plan_offsets[0] != 0 || plan_offsets[n_stages] != draft->d.n_layers)
+        return fail(SPEC_ERR_PLAN, "plan must cover layers 0..%d", draft->d.n_layers - 1);
+    int G = 1;
+    for (int s = 0; s < n_stages; ++s) {
+        const int n = plan_offsets[s + 1] - plan_offsets[s];
+        if (n < 1) return fail(SPEC_ERR_PLAN, "stage %d is empty or out of order", s);
+        if (n > G) G = n;
+    }
+    if (!tokens || !positions || !token_out) return fail(SPEC_ERR_INVALID_ARG, "NULL tokens/positions/token_out");
+    if (tokens_stride < 1 || token_out_stride < 1) return fail(SPEC_ERR_INVALID_ARG, "strides must be >= 1");
+    if (logits_out && logits_stride < draft->d.vocab) return fail(SPEC_ERR_INVALID_ARG, "logits_stride < vocab");
+    if (max_pos < 0 || max_pos >= kv->capacity)
+        return fail(SPEC_ERR_CAPACITY, "max_pos %d outside KV capacity %d", max_pos, kv->capacity);
+    if (!(inv_temperature >= 0.f)) return fail(SPEC_ERR_INVALID_ARG, "inv_temperature must be >= 0");
+    if ((st = check_ws(draft, batch, 1, G, workspace, ws_bytes))) return st;
+
+    Fwd f{draft, kv, batch, 1, max_pos, RowMap{positions, nullptr, 1, kv->capacity}, workspace,
+          carve(draft, batch, 1, G), (hipStream_t)stream};
+    hipError_t e = launch_embed(draft->d.dtype, draft->w.embed, draft->d.vocab, draft->d.d_model, tokens,
+                                tokens_stride, 0, batch, 1, at<float>(workspace, f.c.h), f.s);
+    if (e != hipSuccess) return hip_fail(e, "embed");
+    for (int s = 0; s < n_stages; ++s) {
+        e = run_stage(f, plan_offsets[s], plan_offsets[s + 1] - plan_offsets[s], flags);
+        if (e != hipSuccess) return hip_fail(e, "draft stage");
+    }
+    e = run_head(f, false, nullptr, logits_out, logits_stride, inv_temperature, seed, positions, nullptr,
+                 token_out, token_out_stride);
+    if (e != hipSuccess) return hip_fail(e, "draft head");
+    return SPEC_OK;
+}
+
+static spec_status precise_forward(const spec_model *m, const spec_kv *kv, int batch, const int32_t *tokens,
+                                   const int32_t *start_pos, const int32_t *n_tokens, int mseq, int max_pos,
+                                   void *ws, hipStream_t s, Fwd &f) {
+    f = Fwd{m, kv, batch, mseq, max_pos, RowMap{start_pos, n_tokens, mseq, kv->capacity}, ws,
+            carve(m, batch, mseq, 1), s};
+    hipError_t e = launch_embed(m->d.dtype, m->w.embed, m->d.vocab, m->d.d_model, tokens, mseq, 1, batch, mseq,
+                                at<float>(ws, f.c.h), s);
+    if (e != hipSuccess) return hip_fail(e, "embed");
+    for (int l = 0; l < m->d.n_layers; ++l) {
+        e = run_stage(f, l, 1, SPEC_MLP_SEQUENTIAL);
+        if (e != hipSuccess) return hip_fail(e, "layer");
+    }
+    return SPEC_OK;
+}
+
+spec_status spec_calibrate_kv(const spec_model *draft, const spec_kv *kv, int batch, const int32_t *tokens,
+                              const int32_t *start_pos, const int32_t *n_tokens, int max_m, int max_pos,
+                              float inv_temperature, uint64_t seed, float *last_logits_out, int32_t *token_out,
+                              int token_out_stride, void *workspace, size_t ws_bytes, void *stream) {
+    spec_status st = check_model(draft, kv, batch);
+    if (st) return st;
+    if (!tokens || !start_pos || !token_out) return fail(SPEC_ERR_INVALID_ARG, "NULL tokens/start_pos/token_out");
+    if (max_m < 1) return fail(SPEC_ERR_INVALID_ARG, "max_m %d < 1", max_m);
+    if (token_out_stride < 1) return fail(SPEC_ERR_INVALID_ARG, "token_out_stride < 1");
+    if (max_pos < 0 || max_pos >= kv->capacity)
+        return fail(SPEC_ERR_CAPACITY, "max_pos %d outside KV capacity %d", max_pos, kv->capacity);
+    if (!(inv_temperature >= 0.f)) return fail(SPEC_ERR_INVALID_ARG, "inv_temperature must be >= 0");
+    if ((st = check_ws(draft, batch, max_m, 1, workspace, ws_bytes))) return st;
+    Fwd f;
+    if ((st = precise_forward(draft, kv, batch, tokens, start_pos, n_tokens, max_m, max_pos, workspace,
+                              (hipStream_t)stream, f)))
+        return st;
+    hipError_t e = run_head(f, true, n_tokens, last_logits_out, draft->d.vocab, inv_temperature, seed, start_pos,
+                            n_tokens ? n_tokens : nullptr, token_out, token_out_stride);
+    if (e != hipSuccess) return hip_fail(e, "calibrate head");
+    return SPEC_OK;
+}
+
+spec_status spec_verify_forward(const spec_model *base, const spec_kv *kv, int batch, const int32_t *tokens,
+                                const int32_t *start_pos, int m, int max_pos, float *logits_out, void *workspace,
+                                size_t ws_bytes, void *stream) {
+    spec_status st = check_model(base, kv, batch);
+    if (st) return st;
+    if (!tokens || !start_pos) return fail(SPEC_ERR_INVALID_ARG, "NULL tokens/start_pos");
+    if (m < 1) return fail(SPEC_ERR_INVALID_ARG, "m %d < 1", m);
+    if (max_pos < 0 || max_pos >= kv->capacity)
+        return fail(SPEC_ERR_CAPACITY, "max_pos %d outside KV capacity %d", max_pos, kv->capacity);
+    if ((st = check_ws(base, batch, m, 1, workspace, ws_bytes))) return st;
+    Fwd f;
+    if ((st = precise_forward(base, kv, batch, tokens, start_pos, nullptr, m, max_pos, workspace,
+                              (hipStream_t)stream, f)))
+        return st;
+    if (logits_out) {
+        hipError_t e = run_head(f, false, nullptr, logits_out, base->d.vocab, 0.f, 0, nullptr, nullptr, nullptr, 1);
+        if (e != hipSuccess) return hip_fail(e, "verify head");
+    }
+    return SPEC_OK;
+}
+
+size_t spec_accept_workspace_bytes(int batch, int k, int vocab) {
+    if (batch < 1 || k < 0 || vocab < 2) return 0;
+    const size_t nch = accept_chunks(vocab);
+    size_t t = 0;
+    t += align_up((size_t)batch * (2 * k + 1) * nch * 2 * 4);
+    t += align_up((size_t)batch * (2 * k + 1) * nch * 4);
+    t += align_up((size_t)batch * nch * 2 * 4);
+    t += align_up((size_t)batch * nch * 2 * 4);
+    t += align_up((size_t)batch * 2 * 4);
+    return t;
+}
+
+spec_status spec_accept_resample(int batch, int k, int vocab, const float *p_logits, const float *q_logits,
+                                 const int32_t *draft_tokens, int draft_stride, const int32_t *round_pos,
+                                 float inv_temperature, uint64_t seed, int32_t *n_accepted_out, int32_t *next_token_out,
+                                 int next_token_stride, int32_t *commit_out, void *workspace, size_t ws_bytes,
+                                 void *stream) {
+    if (batch < 1 || k < 0 || vocab < 2) return fail(SPEC_ERR_SHAPE, "batch %d, k %d, vocab %d", batch, k, vocab);
+    if (k > 64) return fail(SPEC_ERR_UNSUPPORTED, "k %d > 64", k);
+    if (!p_logits || !round_pos || !n_accepted_out || !next_token_out)
+        return fail(SPEC_ERR_INVALID_ARG, "NULL p_logits/round_pos/outputs");
+    if (k > 0 && !draft_tokens) return fail(SPEC_ERR_INVALID_ARG, "NULL draft_tokens");
+    if (k > 0 && draft_stride < k) return fail(SPEC_ERR_INVALID_ARG, "draft_stride %d < k %d", draft_stride, k);
+    if (k > 0 && inv_temperature != 0.f && !q_logits) return fail(SPEC_ERR_INVALID_ARG, "NULL q_logits");
+    if (!(inv_temperature >= 0.f)) return fail(SPEC_ERR_INVALID_ARG, "inv_temperature must be >= 0");
+    if (next_token_stride < 1) return fail(SPEC_ERR_INVALID_ARG, "next_token_stride < 1");
+    const size_t need = spec_accept_workspace_bytes(batch, k, vocab);
+    if (!workspace || ws_bytes < need) return fail(SPEC_ERR_WORKSPACE, "workspace %zu < %zu", ws_bytes, need);
+    AcceptParams p{};
+    p.batch = batch; p.k = k; p.vocab = vocab; p.nchunk = accept_chunks(vocab);
+    p.p_logits = p_logits; p.q_logits = q_logits; p.drafts = draft_tokens; p.draft_stride = draft_stride; p.round_pos = round_pos;
+    p.inv_temp = inv_temperature; p.seed = seed;
+    size_t off = 0;
+    const size_t nch = p.nchunk;
+    p.stats = at<float>(workspace, off); off += align_up((size_t)batch * (2 * k + 1) * nch * 2 * 4);
+    p.stats_idx = at<int32_t>(workspace, off); off += align_up((size_t)batch * (2 * k + 1) * nch * 4);
+    p.cand_val = at<float>(workspace, off); off += align_up((size_t)batch * nch * 2 * 4);
+    p.cand_idx = at<int32_t>(workspace, off); off += align_up((size_t)batch * nch * 2 * 4);
+    p.decision = at<int32_t>(workspace, off);
+    p.n_acc_out = n_accepted_out; p.next_out = next_token_out; p.next_stride = next_token_stride;
+    p.commit_out = commit_out;
+    hipError_t e = launch_accept(p, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "accept");
+    return SPEC_OK;
+}
+
+}  // extern "C"
