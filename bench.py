@@ -1,0 +1,227 @@
+"""Benchmark: accepted tokens/s of layer-parallel speculative decoding at
+batch 1 on one MI355X, with draft-step and verify HBM rooflines.
+
+Workload (default): Llama-3.2-1B-shaped draft (16 layers, d 2048, 32/8 heads,
+ffn 8192) with a Llama-3-8B-shaped base (32 layers, d 4096, 32/8 heads, ffn
+14336), bf16, vocab 128256, N(0, 0.02) random-init weights; 512-token seeded
+uniform-random prompt; k = 5 draft tokens per round; layer-parallel set size
+N = 2 (paper plan); batch 1; greedy.
+
+A step is one speculative round: k-1 layer-parallel draft steps, the k+1-token
+base verification, accept / resample, and the calibration pass.  `value` is
+committed tokens per second over the K timed rounds (inputs and KV resident in
+HBM).  Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def draft_step_bytes(sh, ctx):
+    """Algorithmic HBM bytes of one draft step (batch 1): every weight byte
+    read once (layers + lm head; the embedding row is negligible) plus the KV
+    read at context ctx."""
+    es = 2 if sh.dtype == 1 else 4
+    d, L = sh.d_model, sh.n_layers
+    per_layer = sh.qkv_rows * d + d * sh.q_dim + 3 * sh.d_ffn * d
+    w = (L * per_layer + sh.vocab * d) * es
+    kv = 2 * L * sh.n_kv_heads * sh.head_dim * es * ctx
+    return w + kv
+
+
+def verify_bytes(sh, ctx):
+    return draft_step_bytes(sh, ctx)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="llama-1b-8b")
+    ap.add_argument("--temperature", type=float, default=0.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-vanilla", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer-parallel path here "
+              f"is a single-GPU build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from layer_speculative_decoding_amd import api
+    from layer_speculative_decoding_amd.runtime import SpecDecoder, VanillaDecoder
+    from oracle.plan import default_group_plan, plan_offsets
+    from synth import get_config, make_prompts, make_weights
+
+    cfg = get_config(args.config)
+    if cfg.batch != 1:
+        log("note: this config has batch", cfg.batch)
+    K, W = args.steps, args.warmup
+    k = cfg.k
+    dev = "cuda"
+    torch.cuda.init()
+    log(f"config {cfg.name}: generating weights on the GPU")
+    t0 = time.time()
+    dw = make_weights(cfg.draft, cfg.seed_draft, device=dev)
+    bw = make_weights(cfg.base, cfg.seed_base, device=dev)
+    torch.cuda.synchronize()
+    log(f"  weights ready in {time.time() - t0:.1f}s")
+    sets = default_group_plan(cfg.draft.n_layers, cfg.group_size)
+    offs = plan_offsets(sets)
+    P = cfg.prompt_len
+    rounds_cap = W + K + 4
+    cap = P + rounds_cap * (k + 1) + k + 2
+    prompts = make_prompts(cfg.draft.vocab, P, cfg.batch, cfg.prompt_seed)
+    inv_t = 0.0 if args.temperature == 0 else 1.0 / args.temperature
+    dec = SpecDecoder(cfg.draft, dw, cfg.base, bw, cfg.batch, cap, k, offs, P, inv_t, cfg.sample_seed)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    e0, e1 = ev(), ev()
+    e0.record()
+    dec.prefill(prompts)
+    e1.record()
+    torch.cuda.synchronize()
+    prefill_ms = e0.elapsed_time(e1)
+    log(f"  prefill (base {P - 1} + draft {P} tokens): {prefill_ms:.1f} ms")
+
+    big = 1 << 30
+    for _ in range(W):
+        dec.step(big)
+    torch.cuda.synchronize()
+
+    # timed region: K whole rounds; phase events recorded on the same stream
+    n_before = sum(len(o) for o in dec.out)
+    ph = {"draft": [], "verify": [], "accept": [], "calib": []}
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(K):
+        marks = [ev() for _ in range(5)]
+        dec.step(big, marks)
+        ph["draft"].append((marks[0], marks[1]))
+        ph["verify"].append((marks[1], marks[2]))
+        ph["accept"].append((marks[2], marks[3]))
+        ph["calib"].append((marks[3], marks[4]))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    tokens = sum(len(o) for o in dec.out) - n_before
+    ms = {key: float(np.mean([a.elapsed_time(b) for a, b in v])) for key, v in ph.items()}
+    acc_rate = (tokens - K * cfg.batch) / (K * cfg.batch * k)
+    ctx = P + (W + K // 2) * (1 + acc_rate * k)
+    d_step_ms = ms["draft"] / max(k - 1, 1)
+    d_bytes = draft_step_bytes(cfg.draft, ctx)
+    v_bytes = verify_bytes(cfg.base, ctx)
+    d_gbs = d_bytes / (d_step_ms * 1e-3) / 1e9
+    v_gbs = v_bytes / (ms["verify"] * 1e-3) / 1e9
+    value = tokens / elapsed
+    log(f"  {K} rounds: {tokens} tokens in {elapsed * 1e3:.1f} ms -> {value:.1f} tok/s; "
+        f"acceptance {acc_rate:.3f}")
+    log(f"  phases (ms/round): " + ", ".join(f"{a} {b:.3f}" for a, b in ms.items()))
+    log(f"  draft step {d_step_ms * 1e3:.0f} us, {d_gbs:.0f} GB/s ({d_gbs / HBM_PEAK_GBS:.1%} of 8 TB/s); "
+        f"verify {ms['verify'] * 1e3:.0f} us, {v_gbs:.0f} GB/s")
+
+    vanilla = None
+    if not args.no_vanilla:
+        vd = VanillaDecoder(cfg.base, bw, cfg.batch, P + 64 + 2, P, inv_t, cfg.sample_seed)
+        vd.generate(prompts, 4)
+        nv = 48
+        vd.generate(prompts, nv)          # decode loop timed apart from its prefill
+        vanilla_tok_s = nv / vd.decode_s
+        vanilla = round(vanilla_tok_s, 2)
+        log(f"  vanilla decoding ~{vanilla_tok_s:.1f} tok/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, dw, bw, offs, k, P, inv_t)
+
+    out = {
+        "metric": "accepted tokens/s at batch 1; draft-step us and HBM GB/s vs peak (1B->8B shapes)",
+        "value": round(value, 3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(elapsed * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.draft.dtype == 1 else "f32",
+        "data": "synthetic (seeded random-init weights, uniform-random prompt)",
+        "config": {"workload": f"{cfg.name}: draft {cfg.draft.n_layers}L d{cfg.draft.d_model} -> base "
+                               f"{cfg.base.n_layers}L d{cfg.base.d_model}, V {cfg.draft.vocab}, P {P}, k {k}, "
+                               f"N {cfg.group_size}, batch {cfg.batch}, T {args.temperature}",
+                   "plan": offs, "global_batch": cfg.batch, "seq_len": P},
+        "acceptance_rate": round(acc_rate, 4),
+        "draft_step_us": round(d_step_ms * 1e3, 1),
+        "verify_us": round(ms["verify"] * 1e3, 1),
+        "accept_us": round(ms["accept"] * 1e3, 1),
+        "calibrate_us": round(ms["calib"] * 1e3, 1),
+        "prefill_ms": round(prefill_ms, 2),
+        "vanilla_tokens_per_s": vanilla,
+        "roofline": {"bound": "hbm", "kernel": "spec_draft_group_step (one draft step, all launches)",
+                     "achieved": round(d_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(d_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(d_bytes)},
+        "roofline_verify": {"bound": "hbm", "achieved": round(v_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(v_gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": int(v_bytes)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, dw, bw, offs, k, P, inv_t):
+    """The oracle, timed on the host cores on a bounded sample: one full
+    speculative round of the same workload (full-depth float32 models, context
+    P) with an unfilled KV cache (values do not change the work)."""
+    import torch
+    from oracle import sampling
+    from oracle.model import KVCache, OracleModel, forward, fuzzy_step
+    from oracle.plan import offsets_to_sets
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    log(f"  cpu baseline: converting weights to float32 on the host ({cores} cores)")
+    t0 = time.time()
+    od = OracleModel.from_torch(cfg.draft, dw, np.float32)
+    ob = OracleModel.from_torch(cfg.base, bw, np.float32)
+    log(f"    converted in {time.time() - t0:.1f}s")
+    sets = offsets_to_sets(offs)
+    cap = P + k + 4
+    dkv = KVCache(cfg.draft, 1, cap, np.float32)
+    bkv = KVCache(cfg.base, 1, cap, np.float32)
+    rng = np.random.default_rng(0)
+    toks = rng.integers(0, cfg.draft.vocab, size=k + 1)
+    t = P - 1
+    ts = time.perf_counter()
+    qs = [rng.normal(size=cfg.draft.vocab).astype(np.float32)]   # q_1 comes from the previous calibration
+    for j in range(1, k):
+        qs.append(fuzzy_step(od, dkv, 0, int(toks[j]), t + j, sets))
+    pl = forward(ob, bkv, 0, list(toks), range(t, t + k + 1), logits="all")
+    a, y, _ = sampling.accept_resample(pl, np.stack(qs), list(toks[1:]), t, inv_t, cfg.sample_seed, 0)
+    forward(od, dkv, 0, list(toks[1:a + 1]) + [y], range(t + 1, t + a + 2), logits="last")
+    dt = time.perf_counter() - ts
+    log(f"    one oracle round: {dt:.2f}s")
+    del od, ob
+    return {"value": round((a + 1) / dt, 5), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"one speculative round of {cfg.name} (k={k}, context {P}, float32 NumPy, full depth; "
+                      f"{a + 1} token(s) emitted in {dt:.2f}s)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -14,6 +14,7 @@ so a round has k-1 fuzzy steps; generation stops at exactly `new_tokens`.
 """
 from __future__ import annotations
 
+import time
 from dataclasses import dataclass, field
 from typing import List, Optional
 
@@ -30,6 +31,8 @@ class RoundRecord:
     tokens: np.ndarray          # [B][k+1]: x_t, d_1..d_k
     n_acc: np.ndarray           # [B]
     y: np.ndarray               # [B]
+    q_logits: Optional[np.ndarray] = None   # [B][k][V]
+    p_logits: Optional[np.ndarray] = None   # [B][k+1][V]
 
 
 class SpecDecoder:
@@ -115,15 +118,29 @@ class SpecDecoder:
                                  self.tab[0], self.inv_temp, self.seed, self.n_acc, self.vtok[:, 0], k + 1,
                                  self.commit, self.ws)
 
-    def step(self, new_tokens: int) -> bool:
-        """One round; returns True while some sequence still needs tokens."""
+    def step(self, new_tokens: int, marks=None) -> bool:
+        """One round; returns True while some sequence still needs tokens.
+
+        marks: optional list of 5 timing events recorded on the stream at the
+        round's phase boundaries (start, after drafting, after verify, after
+        accept, after calibration)."""
         k, B = self.k, self.B
         self._upload_positions()
+        if marks:
+            marks[0].record()
         self.draft_phase()
+        if marks:
+            marks[1].record()
         self.verify_phase()
+        if marks:
+            marks[2].record()
         if self.record:
             tok_before = self.vtok.to("cpu").numpy().copy()
+            ql = self.q_logits.cpu().numpy().copy()
+            pl = self.p_logits.cpu().numpy().copy()
         self.accept_phase()
+        if marks:
+            marks[3].record()
         bh = self.back_host
         bh[:, 0].copy_(self.n_acc, non_blocking=True)
         bh[:, 1:k + 2].copy_(self.commit, non_blocking=True)
@@ -132,7 +149,7 @@ class SpecDecoder:
         com = bh[:, 1:k + 2].numpy().copy()
         if self.record:
             self.records.append(RoundRecord(list(self.t), tok_before, a.copy(),
-                                            np.array([com[b, a[b]] for b in range(B)])))
+                                            np.array([com[b, a[b]] for b in range(B)]), ql, pl))
         more = False
         th = self.tab_host
         for b in range(B):
@@ -144,11 +161,15 @@ class SpecDecoder:
             self.t[b] += int(a[b]) + 1
             more = more or len(self.out[b]) < new_tokens
         if not more:
+            if marks:
+                marks[4].record()
             return False
         self.tab[k:].copy_(th[k:], non_blocking=True)
         api.spec_calibrate_kv(self.draft, self.dkv, B, self.commit, self.tab[k], self.tab[k + 1], k + 1,
                               max(self.t), self.inv_temp, self.seed, self.q_logits[:, 0], self.vtok[:, 1],
                               k + 1, self.ws)
+        if marks:
+            marks[4].record()
         return True
 
     def generate(self, prompts: np.ndarray, new_tokens: int) -> List[List[int]]:
@@ -190,6 +211,8 @@ class VanillaDecoder:
         self.tok[:, 0].copy_(toks[:, P - 1])
         self.pos.fill_(P - 1)
         hist = torch.zeros(B, new_tokens, dtype=torch.int32, device=self.dev)
+        torch.cuda.current_stream().synchronize()
+        t0 = time.perf_counter()
         for i in range(new_tokens):
             t = P - 1 + i
             api.spec_verify_forward(self.base, self.bkv, B, self.tok, self.pos, 1, t, self.logits, self.ws)
@@ -197,4 +220,6 @@ class VanillaDecoder:
                                      self.seed, self.n_acc, hist[:, i], new_tokens, None, self.ws)
             self.tok[:, 0].copy_(hist[:, i])
             self.pos.add_(1)
-        return hist.cpu().numpy().tolist()
+        out = hist.cpu().numpy().tolist()
+        self.decode_s = time.perf_counter() - t0
+        return out

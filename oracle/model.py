@@ -45,7 +45,7 @@ def to_numpy_weights(w: dict, ftype=np.float64) -> Dict[str, Optional[np.ndarray
     """Convert a dict of torch tensors (any float dtype) to float arrays."""
     out = {}
     for k, t in w.items():
-        out[k] = None if t is None else t.detach().to("cpu").float().numpy().astype(ftype)
+        out[k] = None if t is None else t.detach().to("cpu").float().numpy().astype(ftype, copy=False)
     return out
 
 

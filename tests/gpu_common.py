@@ -34,3 +34,16 @@ def ws(nbytes):
 
 def say(*a):
     print(*a, flush=True)
+
+
+def exclusion(zg, zo, inv_temp):
+    """Margin below which a sampled / arg-max decision may legitimately differ.
+
+    Both sides maximise score = z * s + G with identical Gumbel noise G (the
+    same Philox words; s = 1/T, or 1 for greedy), so if every score differs by
+    less than half the oracle's top-2 gap, the arg-max must agree.  The bound
+    is twice the measured score discrepancy (plus float32 log rounding), and
+    never below MARGIN."""
+    s = 1.0 if inv_temp == 0.0 else inv_temp
+    dz = float(np.max(np.abs(np.asarray(zg, np.float64) - np.asarray(zo, np.float64))))
+    return max(MARGIN, 2.0 * (s * dz + 1e-5))
