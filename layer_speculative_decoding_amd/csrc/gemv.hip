@@ -99,7 +99,7 @@ __device__ __forceinline__ void epilogue(const GemvParams &p, int u, int r0, int
         }
         float s0 = y0, s1 = y1;
         if (p.inv_temp != 0.0f) {
-            const int pos = p.samp_pos[gm] + (p.samp_ntok ? p.samp_ntok[gm] : 1);
+            const int pos = p.samp_pos[gm] + (p.samp_ntok ? p.samp_ntok[gm] : p.samp_nconst);
             float g[4];
             gumbel4(p.seed, (uint32_t)gm, (uint32_t)pos, kDraft, (uint32_t)(r0 >> 2), g);
             s0 = y0 * p.inv_temp + g[r0 & 3];

@@ -185,7 +185,7 @@ hipError_t run_stage(const Fwd &f, int l0, int n, int mlp_mode) {
 // Final norm (optionally of the last valid row of each sequence) + lm head.
 hipError_t run_head(const Fwd &f, bool last_only, const int32_t *ntok, float *logits, int64_t logits_ld,
                     float inv_temp, uint64_t seed, const int32_t *samp_pos, const int32_t *samp_ntok,
-                    int32_t *token_out, int token_stride) {
+                    int samp_nconst, int32_t *token_out, int token_stride) {
     const spec_model *m = f.m;
     const int dm = m->d.d_model;
     const int R = f.batch * f.mseq;
@@ -203,6 +203,7 @@ hipError_t run_head(const Fwd &f, bool last_only, const int32_t *ntok, float *lo
     gp.epi = token_out ? EPI_LOGITS : EPI_STORE;
     gp.out = logits; gp.out_ld = logits_ld; gp.out_sel_stride = 0;
     gp.inv_temp = inv_temp; gp.seed = seed; gp.samp_pos = samp_pos; gp.samp_ntok = samp_ntok;
+    gp.samp_nconst = samp_nconst;
     gp.part_val = at<float>(f.ws, f.c.pval); gp.part_idx = at<int32_t>(f.ws, f.c.pidx);
     const int grid = gemv_grid(gp.n_units);
     if (!token_out && !logits) return hipSuccess;
@@ -341,7 +342,8 @@ spec_status spec_draft_group_step(const spec_model *draft, const spec_kv *kv, co
         e = run_stage(f, plan_offsets[s], plan_offsets[s + 1] - plan_offsets[s], flags);
         if (e != hipSuccess) return hip_fail(e, "draft stage");
     }
-    e = run_head(f, false, nullptr, logits_out, logits_stride, inv_temperature, seed, positions, nullptr,
+    // the sampled token is the one at position positions[b] + 1
+    e = run_head(f, false, nullptr, logits_out, logits_stride, inv_temperature, seed, positions, nullptr, 1,
                  token_out, token_out_stride);
     if (e != hipSuccess) return hip_fail(e, "draft head");
     return SPEC_OK;
@@ -379,8 +381,10 @@ spec_status spec_calibrate_kv(const spec_model *draft, const spec_kv *kv, int ba
     if ((st = precise_forward(draft, kv, batch, tokens, start_pos, n_tokens, max_m, max_pos, workspace,
                               (hipStream_t)stream, f)))
         return st;
+    // the sampled token is the one after the last calibrated position:
+    // start_pos[b] + n_tokens[b] (n_tokens NULL: every sequence has max_m)
     hipError_t e = run_head(f, true, n_tokens, last_logits_out, draft->d.vocab, inv_temperature, seed, start_pos,
-                            n_tokens ? n_tokens : nullptr, token_out, token_out_stride);
+                            n_tokens, max_m, token_out, token_out_stride);
     if (e != hipSuccess) return hip_fail(e, "calibrate head");
     return SPEC_OK;
 }
@@ -400,7 +404,7 @@ spec_status spec_verify_forward(const spec_model *base, const spec_kv *kv, int b
                               (hipStream_t)stream, f)))
         return st;
     if (logits_out) {
-        hipError_t e = run_head(f, false, nullptr, logits_out, base->d.vocab, 0.f, 0, nullptr, nullptr, nullptr, 1);
+        hipError_t e = run_head(f, false, nullptr, logits_out, base->d.vocab, 0.f, 0, nullptr, nullptr, 0, nullptr, 1);
         if (e != hipSuccess) return hip_fail(e, "verify head");
     }
     return SPEC_OK;

@@ -50,11 +50,12 @@ struct GemvParams {
     float rope_theta;
     RowMap rows;
     // LOGITS epilogue: sampling row m is sequence m0 + m; the decided
-    // position is samp_pos[b] + (samp_ntok ? samp_ntok[b] : 1).
+    // position is samp_pos[b] + (samp_ntok ? samp_ntok[b] : samp_nconst).
     float inv_temp;
     uint64_t seed;
     const int32_t *samp_pos;
     const int32_t *samp_ntok;
+    int samp_nconst;
     float *part_val;       // [M][gridDim.x]
     int32_t *part_idx;
 };
