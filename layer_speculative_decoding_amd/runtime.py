@@ -153,11 +153,15 @@ class SpecDecoder:
         more = False
         th = self.tab_host
         for b in range(B):
-            emitted = [int(x) for x in com[b, :a[b] + 1]]
             room = new_tokens - len(self.out[b])
-            self.out[b].extend(emitted[:max(room, 0)])
             th[k, b] = self.t[b] + 1
             th[k + 1, b] = a[b] + 1
+            if room <= 0:
+                # finished sequence: its lane keeps running with the batch but
+                # is frozen at its position, so it never outgrows the cache
+                continue
+            emitted = [int(x) for x in com[b, :a[b] + 1]]
+            self.out[b].extend(emitted[:room])
             self.t[b] += int(a[b]) + 1
             more = more or len(self.out[b]) < new_tokens
         if not more:
