@@ -366,13 +366,15 @@ static spec_status precise_forward(const spec_model *m, const spec_kv *kv, int b
 
 spec_status spec_calibrate_kv(const spec_model *draft, const spec_kv *kv, int batch, const int32_t *tokens,
                               const int32_t *start_pos, const int32_t *n_tokens, int max_m, int max_pos,
-                              float inv_temperature, uint64_t seed, float *last_logits_out, int32_t *token_out,
-                              int token_out_stride, void *workspace, size_t ws_bytes, void *stream) {
+                              float inv_temperature, uint64_t seed, float *last_logits_out, int64_t logits_stride,
+                              int32_t *token_out, int token_out_stride, void *workspace, size_t ws_bytes,
+                              void *stream) {
     spec_status st = check_model(draft, kv, batch);
     if (st) return st;
     if (!tokens || !start_pos || !token_out) return fail(SPEC_ERR_INVALID_ARG, "NULL tokens/start_pos/token_out");
     if (max_m < 1) return fail(SPEC_ERR_INVALID_ARG, "max_m %d < 1", max_m);
     if (token_out_stride < 1) return fail(SPEC_ERR_INVALID_ARG, "token_out_stride < 1");
+    if (last_logits_out && logits_stride < draft->d.vocab) return fail(SPEC_ERR_INVALID_ARG, "logits_stride < vocab");
     if (max_pos < 0 || max_pos >= kv->capacity)
         return fail(SPEC_ERR_CAPACITY, "max_pos %d outside KV capacity %d", max_pos, kv->capacity);
     if (!(inv_temperature >= 0.f)) return fail(SPEC_ERR_INVALID_ARG, "inv_temperature must be >= 0");
@@ -383,7 +385,7 @@ spec_status spec_calibrate_kv(const spec_model *draft, const spec_kv *kv, int ba
         return st;
     // the sampled token is the one after the last calibrated position:
     // start_pos[b] + n_tokens[b] (n_tokens NULL: every sequence has max_m)
-    hipError_t e = run_head(f, true, n_tokens, last_logits_out, draft->d.vocab, inv_temperature, seed, start_pos,
+    hipError_t e = run_head(f, true, n_tokens, last_logits_out, logits_stride, inv_temperature, seed, start_pos,
                             n_tokens, max_m, token_out, token_out_stride);
     if (e != hipSuccess) return hip_fail(e, "calibrate head");
     return SPEC_OK;

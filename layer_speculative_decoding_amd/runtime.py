@@ -86,7 +86,7 @@ class SpecDecoder:
             pre = toks[:, :P - 1].contiguous()
             api.spec_verify_forward(self.base, self.bkv, B, pre, zero, P - 1, P - 2, None, self.ws)
         api.spec_calibrate_kv(self.draft, self.dkv, B, toks, zero, None, P, P - 1, self.inv_temp, self.seed,
-                              self.q_logits[:, 0], self.vtok[:, 1], self.k + 1, self.ws)
+                              self.q_logits[:, 0], self.k * self.V, self.vtok[:, 1], self.k + 1, self.ws)
         self.vtok[:, 0].copy_(toks[:, P - 1])
         self.t = [P - 1] * B
         self.out = [[] for _ in range(B)]
@@ -170,8 +170,8 @@ class SpecDecoder:
             return False
         self.tab[k:].copy_(th[k:], non_blocking=True)
         api.spec_calibrate_kv(self.draft, self.dkv, B, self.commit, self.tab[k], self.tab[k + 1], k + 1,
-                              max(self.t), self.inv_temp, self.seed, self.q_logits[:, 0], self.vtok[:, 1],
-                              k + 1, self.ws)
+                              max(self.t), self.inv_temp, self.seed, self.q_logits[:, 0], k * self.V,
+                              self.vtok[:, 1], k + 1, self.ws)
         if marks:
             marks[4].record()
         return True

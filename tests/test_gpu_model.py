@@ -54,7 +54,8 @@ def test_calibrate_prefill_matches_oracle(name, inv_temp):
     w = ws(api.spec_workspace_bytes(gm, B, P, 1))
     logits = torch.zeros(B, shape.vocab, device="cuda")
     tok = torch.zeros(B, dtype=torch.int32, device="cuda")
-    api.spec_calibrate_kv(gm, gkv, B, i32(prompts), i32([0] * B), None, P, P - 1, inv_temp, 99, logits, tok, 1, w)
+    api.spec_calibrate_kv(gm, gkv, B, i32(prompts), i32([0] * B), None, P, P - 1, inv_temp, 99, logits,
+                          shape.vocab, tok, 1, w)
     torch.cuda.synchronize()
     zg, tg = logits.cpu().numpy(), tok.cpu().numpy()
     for b in range(B):
@@ -80,7 +81,8 @@ def test_calibrate_ragged_matches_oracle(name):
     say(f"calibrate ragged {name}")
     w = ws(api.spec_workspace_bytes(gm, B, P + M, 1))
     tok = torch.zeros(B, dtype=torch.int32, device="cuda")
-    api.spec_calibrate_kv(gm, gkv, B, i32(prompts[:, :P]), i32([0] * B), None, P, P - 1, 0.0, 1, None, tok, 1, w)
+    api.spec_calibrate_kv(gm, gkv, B, i32(prompts[:, :P]), i32([0] * B), None, P, P - 1, 0.0, 1, None, 0, tok, 1,
+                          w)
     for b in range(B):
         forward(om, okv, b, prompts[b, :P], range(P), logits=None)
     ntok = np.array([1, 4, 6], dtype=np.int32)
@@ -88,7 +90,7 @@ def test_calibrate_ragged_matches_oracle(name):
     logits = torch.zeros(B, shape.vocab, device="cuda")
     before = gkv.k.float().cpu().numpy().copy()
     api.spec_calibrate_kv(gm, gkv, B, i32(prompts[:, P:]), i32(start), i32(ntok), M, P + M - 1, 1.0, 7, logits,
-                          tok, 1, w)
+                          shape.vocab, tok, 1, w)
     torch.cuda.synchronize()
     zg, tg = logits.cpu().numpy(), tok.cpu().numpy()
     after = gkv.k.float().cpu().numpy()
@@ -162,7 +164,7 @@ def test_draft_group_step_matches_oracle(name, mlp, inv_temp):
             forward(om, okv, b, prompts[b, :lens[b]], range(lens[b]), logits=None)
         # batched ragged prefill through calibrate (n_tokens per sequence)
         api.spec_calibrate_kv(gm, gkv, B, i32(prompts[:, :P]), i32([0] * B), i32(lens), P, P - 1, 0.0, 0, None,
-                              tok, 1, w)
+                              0, tok, 1, w)
         cur = prompts[:, P].copy()
         pos = lens.copy()
         for step in range(3):
