@@ -155,15 +155,19 @@ class SpecDecoder:
         for b in range(B):
             room = new_tokens - len(self.out[b])
             th[k, b] = self.t[b] + 1
-            th[k + 1, b] = a[b] + 1
+            th[k + 1, b] = 0
             if room <= 0:
-                # finished sequence: its lane keeps running with the batch but
-                # is frozen at its position, so it never outgrows the cache
+                # finished sequence: its lane keeps running with the batch,
+                # frozen at its position (no calibration rows), so it never
+                # outgrows the cache
                 continue
             emitted = [int(x) for x in com[b, :a[b] + 1]]
             self.out[b].extend(emitted[:room])
+            if len(self.out[b]) >= new_tokens:
+                continue
+            th[k + 1, b] = a[b] + 1
             self.t[b] += int(a[b]) + 1
-            more = more or len(self.out[b]) < new_tokens
+            more = True
         if not more:
             if marks:
                 marks[4].record()
