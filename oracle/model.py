@@ -79,6 +79,12 @@ class KVCache:
 
 
 # ----------------------------------------------------------------- primitives
+def linear(x, W):
+    """x W^T for x [n][in], W [out][in] (computed as (W x^T)^T so that NumPy
+    hands the row-major weight to BLAS as is)."""
+    return (W @ x.T).T
+
+
 def rmsnorm(x, g, eps):
     ms = np.mean(x * x, axis=-1, keepdims=True)
     return x / np.sqrt(ms + eps) * g
@@ -127,7 +133,7 @@ def attn_part(m: OracleModel, cache: KVCache, l: int, b: int, h_in, positions):
     sh, w = m.shape, m.w
     hq, hkv, hd = sh.n_q_heads, sh.n_kv_heads, sh.head_dim
     x = m.rnd(rmsnorm(h_in, w["attn_norm"][l], sh.rms_eps))
-    qkv = x @ w["wqkv"][l].T
+    qkv = linear(x, w["wqkv"][l])
     if w.get("bqkv") is not None:
         qkv = qkv + w["bqkv"][l]
     n = h_in.shape[0]
@@ -141,16 +147,16 @@ def attn_part(m: OracleModel, cache: KVCache, l: int, b: int, h_in, positions):
         cache.v[l, b, :, p] = m.rnd(v[r])
     o = attention(q, cache.k[l, b], cache.v[l, b], positions, hkv)
     o = m.rnd(o.reshape(n, hq * hd))
-    return o @ w["wo"][l].T
+    return linear(o, w["wo"][l])
 
 
 def mlp_part(m: OracleModel, l: int, h_in):
     sh, w = m.shape, m.w
     f = sh.d_ffn
     y = m.rnd(rmsnorm(h_in, w["ffn_norm"][l], sh.rms_eps))
-    gu = y @ w["w_gate_up"][l].T
+    gu = linear(y, w["w_gate_up"][l])
     act = m.rnd(silu(gu[:, :f]) * gu[:, f:])
-    return act @ w["w_down"][l].T
+    return linear(act, w["w_down"][l])
 
 
 def embed(m: OracleModel, tokens):
@@ -159,7 +165,7 @@ def embed(m: OracleModel, tokens):
 
 def final_logits(m: OracleModel, h):
     x = m.rnd(rmsnorm(h, m.w["final_norm"], m.shape.rms_eps))
-    return x @ m.w["lm_head"].T
+    return linear(x, m.w["lm_head"])
 
 
 # ----------------------------------------------------------------- forwards
