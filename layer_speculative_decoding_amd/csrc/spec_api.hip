@@ -5,6 +5,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -85,10 +86,41 @@ struct Fwd {
     hipStream_t s;
 };
 
-// Weight-streaming product over rows chunked by the kernel's row limit.
-hipError_t gemv_chunked(const spec_model *m, GemvParams p, int Mtot, hipStream_t s) {
+// Activation-row count from which bf16 products use the matrix-core kernel
+// (SPEC_MFMA_MIN_ROWS overrides; the VALU GEMV serves fewer rows and float32).
+int mfma_min_rows() {
+    static int v = [] {
+        const char *e = getenv("SPEC_MFMA_MIN_ROWS");
+        return e ? atoi(e) : 2;
+    }();
+    return v;
+}
+
+// Weight-streaming product over Mtot activation rows, chunked by the kernel's
+// row limit.  *grid_out receives the grid of the launches (the number of
+// sampling partials per row for EPI_LOGITS).
+hipError_t gemv_chunked(const spec_model *m, GemvParams p, int Mtot, hipStream_t s, int *grid_out = nullptr) {
+    GemvParams q = p;
+    q.M = Mtot < 32 ? Mtot : 32;
+    const bool mfma = m->d.dtype == SPEC_BF16 && Mtot >= mfma_min_rows() && gemm_mfma_supported(q) &&
+                      !(p.epi == EPI_LOGITS && Mtot > 8);
+    if (mfma) {
+        q.n_units = p.n_units / 16;           // row pairs -> pairs of 16-row blocks
+        const int grid = gemm_mfma_grid(q.n_units);
+        const int ks = gemm_mfma_splits(q.n_units, p.K);
+        if (grid_out) *grid_out = grid;
+        const int mr = gemm_mfma_max_rows();
+        for (int m0 = 0; m0 < Mtot; m0 += mr) {
+            q.m0 = m0;
+            q.M = (Mtot - m0) < mr ? (Mtot - m0) : mr;
+            hipError_t e = launch_gemm_mfma(q, grid, ks, s);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
     const int mr = gemv_max_rows();
     const int grid = gemv_grid(p.n_units);
+    if (grid_out) *grid_out = grid;
     for (int m0 = 0; m0 < Mtot; m0 += mr) {
         p.m0 = m0;
         p.M = (Mtot - m0) < mr ? (Mtot - m0) : mr;
@@ -205,9 +237,9 @@ hipError_t run_head(const Fwd &f, bool last_only, const int32_t *ntok, float *lo
     gp.inv_temp = inv_temp; gp.seed = seed; gp.samp_pos = samp_pos; gp.samp_ntok = samp_ntok;
     gp.samp_nconst = samp_nconst;
     gp.part_val = at<float>(f.ws, f.c.pval); gp.part_idx = at<int32_t>(f.ws, f.c.pidx);
-    const int grid = gemv_grid(gp.n_units);
     if (!token_out && !logits) return hipSuccess;
-    if ((e = gemv_chunked(m, gp, Mh, f.s)) != hipSuccess) return e;
+    int grid = 0;
+    if ((e = gemv_chunked(m, gp, Mh, f.s, &grid)) != hipSuccess) return e;
     if (token_out) return launch_sample_reduce(gp.part_val, gp.part_idx, grid, Mh, token_out, token_stride, f.s);
     return hipSuccess;
 }

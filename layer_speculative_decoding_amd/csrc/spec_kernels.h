@@ -61,9 +61,17 @@ struct GemvParams {
 };
 
 // dtype: 0 float32, 1 bfloat16 (weights, activations X and act share it).
+// VALU GEMV: units are row pairs, M <= gemv_max_rows() per launch.
 hipError_t launch_gemv(int dtype, const GemvParams &p, int grid, hipStream_t s);
 int gemv_max_rows();
 int gemv_grid(int n_units);
+// MFMA skinny GEMM (bf16): units are pairs of 16-row blocks (n_units = rows /
+// 32), M <= 32 per launch, K a multiple of 64, pair_block a multiple of 32.
+hipError_t launch_gemm_mfma(const GemvParams &p, int grid, int ks, hipStream_t s);
+bool gemm_mfma_supported(const GemvParams &p);
+int gemm_mfma_max_rows();
+int gemm_mfma_grid(int n_units);
+int gemm_mfma_splits(int n_units, int K);
 
 // h[m] (+)= add[m]; normalise (src0 ? src0[m] + add[m] : h[m]) with each of
 // n_gains gains and write xn[g][m][:] (rounded to the activation dtype).
