@@ -5,8 +5,8 @@
 // split).  Its query vectors are the rows of the block times the q heads that
 // share the kv head (GQA), so every K/V tile staged in LDS is used by all of
 // them.  Softmax is online (running max / sum per query vector); with several
-// key splits the partial (max, sum, unnormalised output) are merged by
-// k_attn_combine in a fixed order.
+// key splits the partial (max, sum, unnormalised output) are merged in split
+// order by the last split block to finish (completion counter, reset after).
 #include "spec_device.h"
 #include "spec_kernels.h"
 
@@ -65,8 +65,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
         q_s[qv][d] = p.q[(int64_t)gi * p.q_sel_stride + ((int64_t)row * p.hq + kvh * G + g) * HD + d];
     }
     // keys 0 .. kmax serve this block (rows hold consecutive positions)
-    int last = min(i0 + nrows, ntok) - 1;
-    int kmax = last >= 0 ? pos0 + last : -1;
+    const int last_row = min(i0 + nrows, ntok) - 1;
+    int kmax = last_row >= 0 ? pos0 + last_row : -1;
     if (kmax >= p.capacity) kmax = p.capacity - 1;
     const int total = kmax + 1;
     int per = (total + p.splits - 1) / p.splits;
@@ -143,6 +143,25 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
         __syncthreads();
     }
 
+    T *obase = reinterpret_cast<T *>(p.o) + (int64_t)gi * p.o_sel_stride;
+    if (p.splits == 1) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const int idx = tid + 256 * r;
+            if (idx < QV * HD) {
+                const int qv = idx / HD, d = idx - (idx / HD) * HD;
+                const int rr = qv / G, g = qv - rr * G;
+                const int row = b * mseq + i0 + rr;
+                const float l = l_s[qv];
+                const float val = (pos_s[qv] >= 0 && l > 0.f) ? acc[r] / l : 0.f;
+                obase[(int64_t)row * p.hq * HD + (kvh * G + g) * HD + d] = S::from_f32(val);
+            }
+        }
+        return;
+    }
+    // several key splits: publish (m, l, unnormalised acc); the last split
+    // block of this (layer, kv head, sequence) merges them in split order
+    const int64_t stride_sp = (int64_t)p.n_group * p.Mtot * p.hq;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
         const int idx = tid + 256 * r;
@@ -150,51 +169,47 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
             const int qv = idx / HD, d = idx - (idx / HD) * HD;
             const int rr = qv / G, g = qv - rr * G;
             const int row = b * mseq + i0 + rr;
-            const int h = kvh * G + g;
-            if (p.splits == 1) {
-                const float l = l_s[qv];
-                const float val = (pos_s[qv] >= 0 && l > 0.f) ? acc[r] / l : 0.f;
-                T *o = reinterpret_cast<T *>(p.o) + (int64_t)gi * p.o_sel_stride + (int64_t)row * p.hq * HD;
-                o[h * HD + d] = S::from_f32(val);
-            } else {
-                const int64_t pr = (((int64_t)sp * p.n_group + gi) * p.Mtot + row) * p.hq + h;
-                p.part_acc[pr * HD + d] = acc[r];
-                if (d == 0) {
-                    p.part_ml[pr * 2 + 0] = m_s[qv];
-                    p.part_ml[pr * 2 + 1] = l_s[qv];
+            const int64_t pr = (int64_t)sp * stride_sp + ((int64_t)gi * p.Mtot + row) * p.hq + kvh * G + g;
+            p.part_acc[pr * HD + d] = acc[r];
+            if (d == 0) {
+                p.part_ml[pr * 2 + 0] = m_s[qv];
+                p.part_ml[pr * 2 + 1] = l_s[qv];
+            }
+        }
+    }
+    __shared__ bool is_last;
+    unsigned *ctr = p.counters + ((int64_t)gi * p.hkv + kvh) * p.batch + b;
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) is_last = atomicAdd(ctr, 1u) == (unsigned)(p.splits - 1);
+    __syncthreads();
+    if (!is_last) return;
+    __threadfence();
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const int idx = tid + 256 * r;
+        if (idx < QV * HD) {
+            const int qv = idx / HD, d = idx - (idx / HD) * HD;
+            const int rr = qv / G, g = qv - rr * G;
+            const int row = b * mseq + i0 + rr;
+            const int64_t pr0 = ((int64_t)gi * p.Mtot + row) * p.hq + kvh * G + g;
+            float mx = -INFINITY;
+            for (int s2 = 0; s2 < p.splits; ++s2) mx = fmaxf(mx, p.part_ml[(pr0 + s2 * stride_sp) * 2]);
+            float num = 0.f, den = 0.f;
+            if (mx != -INFINITY) {
+                for (int s2 = 0; s2 < p.splits; ++s2) {
+                    const int64_t pr = pr0 + s2 * stride_sp;
+                    const float mm = p.part_ml[pr * 2];
+                    if (mm == -INFINITY) continue;
+                    const float w = expf(mm - mx);
+                    num = fmaf(w, p.part_acc[pr * HD + d], num);
+                    den = fmaf(w, p.part_ml[pr * 2 + 1], den);
                 }
             }
+            obase[(int64_t)row * p.hq * HD + (kvh * G + g) * HD + d] = S::from_f32(den > 0.f ? num / den : 0.f);
         }
     }
-}
-
-// Merge the key splits of one (layer, row, q head): out = sum_s w_s acc_s /
-// sum_s w_s l_s with w_s = exp(m_s - max_s m_s), splits taken in order.
-template <typename T>
-__global__ __launch_bounds__(128) void k_attn_combine(AttnParams p) {
-    const int row = blockIdx.x / p.hq;
-    const int h = blockIdx.x - row * p.hq;
-    const int gi = blockIdx.y;
-    const int HD = p.hd;
-    const int64_t stride_sp = (int64_t)p.n_group * p.Mtot * p.hq;
-    const int64_t pr0 = ((int64_t)gi * p.Mtot + row) * p.hq + h;
-    float mx = -INFINITY;
-    for (int s = 0; s < p.splits; ++s) mx = fmaxf(mx, p.part_ml[(pr0 + s * stride_sp) * 2]);
-    T *o = reinterpret_cast<T *>(p.o) + (int64_t)gi * p.o_sel_stride + (int64_t)row * p.hq * HD + h * HD;
-    for (int d = threadIdx.x; d < HD; d += blockDim.x) {
-        float num = 0.f, den = 0.f;
-        if (mx != -INFINITY) {
-            for (int s = 0; s < p.splits; ++s) {
-                const int64_t pr = pr0 + s * stride_sp;
-                const float m = p.part_ml[pr * 2];
-                if (m == -INFINITY) continue;
-                const float w = expf(m - mx);
-                num = fmaf(w, p.part_acc[pr * HD + d], num);
-                den = fmaf(w, p.part_ml[pr * 2 + 1], den);
-            }
-        }
-        o[d] = Store<T>::from_f32(den > 0.f ? num / den : 0.f);
-    }
+    if (tid == 0) *ctr = 0u;
 }
 
 template <typename T, int HD>
@@ -203,9 +218,6 @@ hipError_t launch_hd(const AttnParams &p, hipStream_t s) {
     const int QB = (kQV / G) > 0 ? kQV / G : 1;
     dim3 grid((p.rows.mseq + QB - 1) / QB, p.n_group * p.hkv, p.batch * p.splits);
     hipLaunchKernelGGL((k_attn<T, HD>), grid, dim3(256), 0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.splits == 1) return e;
-    hipLaunchKernelGGL(k_attn_combine<T>, dim3(p.Mtot * p.hq, p.n_group), dim3(128), 0, s, p);
     return hipGetLastError();
 }
 

@@ -25,7 +25,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMaxKS = 8;        // K splits (wave pairs) per workgroup
+constexpr int kMaxKS = 4;        // K splits (wave pairs) per workgroup
 constexpr int kMaxGridM = 256 * 8;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &v) {
@@ -34,9 +34,34 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &v) {
     return r;
 }
 
+__device__ __forceinline__ uint4 pack_bf16x8(const float *f) {
+    uint4 r;
+    r.x = (uint32_t)f32_to_bf16(f[0]) | ((uint32_t)f32_to_bf16(f[1]) << 16);
+    r.y = (uint32_t)f32_to_bf16(f[2]) | ((uint32_t)f32_to_bf16(f[3]) << 16);
+    r.z = (uint32_t)f32_to_bf16(f[4]) | ((uint32_t)f32_to_bf16(f[5]) << 16);
+    r.w = (uint32_t)f32_to_bf16(f[6]) | ((uint32_t)f32_to_bf16(f[7]) << 16);
+    return r;
+}
+
+// A-operand pieces (16 consecutive k of one activation row) for one 64-wide
+// chunk: plain bf16 rows, or RMSNorm-ed residual rows rounded to bf16.
+__device__ __forceinline__ void x_tile(const GemvParams &p, const uint16_t *xrow, int sel, int hrow, float inv,
+                                       int k, uint4 &x0, uint4 &x1) {
+    if (p.xmode == X_PLAIN) {
+        x0 = ld16(xrow + k);
+        x1 = ld16(xrow + k + 8);
+    } else {
+        float f[8];
+        x_norm8(p, sel, hrow, k, inv, f);
+        x0 = pack_bf16x8(f);
+        x_norm8(p, sel, hrow, k + 8, inv, f);
+        x1 = pack_bf16x8(f);
+    }
+}
+
 // MT: number of 16-row activation tiles (1: M <= 16, 2: M <= 32)
-template <int MT>
-__global__ __launch_bounds__(1024) void k_gemm_mfma(GemvParams p, int KS) {
+template <int MT, bool kLogits>
+__global__ __launch_bounds__(512) void k_gemm_mfma(GemvParams p, int KS) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;     // 0 .. 2*KS-1
     const int blk = wave & 1;              // which block of the pair
@@ -53,10 +78,11 @@ __global__ __launch_bounds__(1024) void k_gemm_mfma(GemvParams p, int KS) {
 
     __shared__ f32x4 red[2 * kMaxKS][MT][64];
     __shared__ float tile[2][MT * 16][17];
-    __shared__ float sbv[MT * 16][16];
-    __shared__ int sbi[MT * 16][16];
     float best_v = -INFINITY;
     int best_i = 0x7FFFFFFF;
+    float ss[kMaxSel];
+#pragma unroll
+    for (int s = 0; s < kMaxSel; ++s) ss[s] = 0.f;
 
     for (int u = blockIdx.x; u < p.n_units; u += gridDim.x) {
         const int bb = u / bph;
@@ -72,8 +98,19 @@ __global__ __launch_bounds__(1024) void k_gemm_mfma(GemvParams p, int KS) {
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         bool xok[MT];
+        int hrow[MT];
+        float inv[MT];
 #pragma unroll
-        for (int t = 0; t < MT; ++t) xok[t] = (t * 16 + li) < p.M;
+        for (int t = 0; t < MT; ++t) {
+            xok[t] = (t * 16 + li) < p.M;
+            hrow[t] = 0;
+            inv[t] = 0.f;
+            if (xok[t] && p.xmode == X_NORM) {
+                hrow[t] = x_row(p, p.m0 + t * 16 + li);
+                inv[t] = x_inv(p, sel, hrow[t]);
+            }
+        }
+        const int kl = 16 * lg;   // this lane group's offset inside a chunk
 
         int c = c0;
         for (; c + 3 < c1; c += 4) {
@@ -88,11 +125,8 @@ __global__ __launch_bounds__(1024) void k_gemm_mfma(GemvParams p, int KS) {
 #pragma unroll
                 for (int t = 0; t < MT; ++t) {
                     uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
-                    if (xok[t]) {
-                        const uint16_t *xr = x + (int64_t)(t * 16 + li) * K + (c + q) * 64;
-                        x0 = ld16(xr);
-                        x1 = ld16(xr + 8);
-                    }
+                    if (xok[t])
+                        x_tile(p, x - kl + (int64_t)(t * 16 + li) * K, sel, hrow[t], inv[t], (c + q) * 64 + kl, x0, x1);
                     acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x0), as_bf16x8(wv[q][0]), acc[t], 0, 0, 0);
                     acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x1), as_bf16x8(wv[q][1]), acc[t], 0, 0, 0);
                 }
@@ -103,11 +137,8 @@ __global__ __launch_bounds__(1024) void k_gemm_mfma(GemvParams p, int KS) {
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
                 uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
-                if (xok[t]) {
-                    const uint16_t *xr = x + (int64_t)(t * 16 + li) * K + c * 64;
-                    x0 = ld16(xr);
-                    x1 = ld16(xr + 8);
-                }
+                if (xok[t])
+                    x_tile(p, x - kl + (int64_t)(t * 16 + li) * K, sel, hrow[t], inv[t], c * 64 + kl, x0, x1);
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x0), as_bf16x8(w0), acc[t], 0, 0, 0);
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x1), as_bf16x8(w1), acc[t], 0, 0, 0);
             }
@@ -132,27 +163,42 @@ __global__ __launch_bounds__(1024) void k_gemm_mfma(GemvParams p, int KS) {
         __syncthreads();
         for (int e = threadIdx.x; e < p.M * 16; e += blockDim.x) {
             const int m = e >> 4, j = e & 15;
-            epilogue<uint16_t>(p, r0 + j, r0 + j, r1 + j, sel, m, tile[0][m][j], tile[1][m][j], best_v, best_i);
+            epilogue<uint16_t, kLogits>(p, r0 + j, r0 + j, r1 + j, sel, m, tile[0][m][j], tile[1][m][j], best_v, best_i, ss);
         }
         __syncthreads();
     }
 
-    if (p.epi == EPI_LOGITS) {
-        // thread e (< 16 M) always handled activation row e / 16
-        const int e = threadIdx.x;
-        if (e < MT * 256) {
-            sbv[e >> 4][e & 15] = best_v;
-            sbi[e >> 4][e & 15] = best_i;
-        }
-        __syncthreads();
-        if (e < p.M) {
+    // block partials: thread e < 16 M always handled activation row e / 16
+    // (the launch guarantees blockDim >= 16 M)
+    const bool norm = p.n_norm_sel > 0;
+    const bool logits = p.epi == EPI_LOGITS;
+    if (!norm && !logits) return;
+    __shared__ float sbv[MT * 16][16];
+    __shared__ int sbi[MT * 16][16];
+    __shared__ float sss[kMaxSel][MT * 16][16];
+    const int e = threadIdx.x;
+    if (e < p.M * 16) {
+        sbv[e >> 4][e & 15] = best_v;
+        sbi[e >> 4][e & 15] = best_i;
+#pragma unroll
+        for (int s = 0; s < kMaxSel; ++s) sss[s][e >> 4][e & 15] = ss[s];
+    }
+    __syncthreads();
+    if (e < p.M) {
+        if (logits) {
             float v = sbv[e][0];
             int i = sbi[e][0];
             for (int j = 1; j < 16; ++j) argmax_merge(v, i, sbv[e][j], sbi[e][j]);
             p.part_val[(int64_t)(p.m0 + e) * gridDim.x + blockIdx.x] = v;
             p.part_idx[(int64_t)(p.m0 + e) * gridDim.x + blockIdx.x] = i;
         }
+        for (int s = 0; s < p.n_norm_sel; ++s) {
+            float t = sss[s][e][0];
+            for (int j = 1; j < 16; ++j) t += sss[s][e][j];
+            p.ss[((int64_t)s * p.Mtot + p.m0 + e) * gridDim.x + blockIdx.x] = t;
+        }
     }
+    last_block_reduce(p);
 }
 
 }  // namespace
@@ -174,9 +220,16 @@ bool gemm_mfma_supported(const GemvParams &p) {
 }
 
 hipError_t launch_gemm_mfma(const GemvParams &p, int grid, int ks, hipStream_t s) {
+    while (128 * ks < 16 * p.M) ks *= 2;   // one epilogue element per thread
     dim3 g(grid), b(128 * ks);
-    if (p.M <= 16) hipLaunchKernelGGL((k_gemm_mfma<1>), g, b, 0, s, p, ks);
-    else hipLaunchKernelGGL((k_gemm_mfma<2>), g, b, 0, s, p, ks);
+    const bool lg = p.epi == EPI_LOGITS;
+    if (p.M <= 16) {
+        if (lg) hipLaunchKernelGGL((k_gemm_mfma<1, true>), g, b, 0, s, p, ks);
+        else hipLaunchKernelGGL((k_gemm_mfma<1, false>), g, b, 0, s, p, ks);
+    } else {
+        if (lg) hipLaunchKernelGGL((k_gemm_mfma<2, true>), g, b, 0, s, p, ks);
+        else hipLaunchKernelGGL((k_gemm_mfma<2, false>), g, b, 0, s, p, ks);
+    }
     return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
-// Weight-streaming matrix-vector products for few activation rows, with the
-// epilogues of the decoder fused in (QKV + RoPE + KV append, SiLU-gate,
-// residual add, logits + sampling partials), plus RMSNorm and embedding.
+// Weight-streaming matrix-vector products for few activation rows (the draft
+// step's one row per sequence, and the float32 path), with RMSNorm folded
+// into the operand load and the decoder's consumers fused into the epilogue;
+// plus the embedding kernel that starts every forward call.
 //
 // At decode batch sizes these products read every weight byte once and do a
 // handful of flops per byte, so they are bound by HBM bandwidth: each wave
@@ -21,7 +22,20 @@ constexpr int kMaxRows = 8;        // activation rows per launch
 constexpr int kMaxGrid = 256 * 8;  // workgroups (8 per CU)
 constexpr int kUnroll = 4;
 
-template <typename T, int MR>
+template <typename T, int E>
+__device__ __forceinline__ void load_x(const GemvParams &p, const T *xplain, int sel, int m, int hrow, float inv,
+                                       int k, float *fx) {
+    if (p.xmode == X_PLAIN) {
+        Store<T>::unpack(ld16(xplain + (int64_t)m * p.K + k), fx);
+    } else {
+        if constexpr (E == 8) x_norm8(p, sel, hrow, k, inv, fx);
+        else x_norm4(p, sel, hrow, k, inv, fx);
+#pragma unroll
+        for (int e = 0; e < E; ++e) fx[e] = Store<T>::round(fx[e]);
+    }
+}
+
+template <typename T, int MR, bool kLogits>
 __global__ __launch_bounds__(256) void k_gemv(GemvParams p) {
     using S = Store<T>;
     constexpr int E = S::kPer16;
@@ -32,6 +46,9 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p) {
     const int half = p.pair_block >> 1;
     float best_v = -INFINITY;
     int best_i = 0x7FFFFFFF;
+    float ss[kMaxSel];
+#pragma unroll
+    for (int s = 0; s < kMaxSel; ++s) ss[s] = 0.f;
 
     for (int u = blockIdx.x * kWaves + wave; u < p.n_units; u += gridDim.x * kWaves) {
         const int blk = u / half;
@@ -41,7 +58,18 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p) {
         const int sel = r0 / p.rows_per_sel;
         const T *w0 = reinterpret_cast<const T *>(p.W) + (int64_t)r0 * K;
         const T *w1 = reinterpret_cast<const T *>(p.W) + (int64_t)r1 * K;
-        const T *x = reinterpret_cast<const T *>(p.X) + (int64_t)sel * p.x_sel_stride + (int64_t)p.m0 * K;
+        const T *xp = reinterpret_cast<const T *>(p.X) + (int64_t)sel * p.x_sel_stride + (int64_t)p.m0 * K;
+        int hrow[MR];
+        float inv[MR];
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            hrow[m] = 0;
+            inv[m] = 0.f;
+            if (p.xmode == X_NORM && m < p.M) {
+                hrow[m] = x_row(p, p.m0 + m);
+                inv[m] = x_inv(p, sel, hrow[m]);
+            }
+        }
         float a0[MR], a1[MR];
 #pragma unroll
         for (int m = 0; m < MR; ++m) { a0[m] = 0.f; a1[m] = 0.f; }
@@ -63,7 +91,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p) {
                 for (int m = 0; m < MR; ++m) {
                     if (m < p.M) {
                         float fx[E];
-                        S::unpack(ld16(x + (int64_t)m * K + k + q * step), fx);
+                        load_x<T, E>(p, xp, sel, m, hrow[m], inv[m], k + q * step, fx);
 #pragma unroll
                         for (int e = 0; e < E; ++e) {
                             a0[m] = fmaf(fa[e], fx[e], a0[m]);
@@ -81,7 +109,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p) {
             for (int m = 0; m < MR; ++m) {
                 if (m < p.M) {
                     float fx[E];
-                    S::unpack(ld16(x + (int64_t)m * K + k), fx);
+                    load_x<T, E>(p, xp, sel, m, hrow[m], inv[m], k, fx);
 #pragma unroll
                     for (int e = 0; e < E; ++e) {
                         a0[m] = fmaf(fa[e], fx[e], a0[m]);
@@ -99,86 +127,96 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p) {
                 if (lane == m) { y0 = s0; y1 = s1; }
             }
         }
-        if (lane < p.M) epilogue<T>(p, u, r0, r1, sel, lane, y0, y1, best_v, best_i);
+        if (lane < p.M) epilogue<T, kLogits>(p, u, r0, r1, sel, lane, y0, y1, best_v, best_i, ss);
     }
 
-    if (p.epi == EPI_LOGITS) {
-        // per-workgroup arg-max of each sampling row; lane m holds row m
-        __shared__ float sv[kWaves][kMaxRows];
-        __shared__ int si[kWaves][kMaxRows];
-        if (lane < p.M) { sv[wave][lane] = best_v; si[wave][lane] = best_i; }
-        __syncthreads();
-        if (threadIdx.x < p.M) {
-            float v = sv[0][threadIdx.x];
-            int i = si[0][threadIdx.x];
-            for (int w = 1; w < kWaves; ++w) argmax_merge(v, i, sv[w][threadIdx.x], si[w][threadIdx.x]);
-            p.part_val[(int64_t)(p.m0 + threadIdx.x) * gridDim.x + blockIdx.x] = v;
-            p.part_idx[(int64_t)(p.m0 + threadIdx.x) * gridDim.x + blockIdx.x] = i;
+    const bool norm = p.n_norm_sel > 0;
+    const bool logits = p.epi == EPI_LOGITS;
+    if (!norm && !logits) return;
+    // block partials: lane m of every wave holds row m's contribution
+    __shared__ float sv[kWaves][kMaxRows];
+    __shared__ int si[kWaves][kMaxRows];
+    __shared__ float sss[kWaves][kMaxSel][kMaxRows];
+    if (lane < p.M) {
+        sv[wave][lane] = best_v;
+        si[wave][lane] = best_i;
+#pragma unroll
+        for (int s = 0; s < kMaxSel; ++s) sss[wave][s][lane] = ss[s];
+    }
+    __syncthreads();
+    if (threadIdx.x < p.M) {
+        const int m = threadIdx.x;
+        if (logits) {
+            float v = sv[0][m];
+            int i = si[0][m];
+            for (int w = 1; w < kWaves; ++w) argmax_merge(v, i, sv[w][m], si[w][m]);
+            p.part_val[(int64_t)(p.m0 + m) * gridDim.x + blockIdx.x] = v;
+            p.part_idx[(int64_t)(p.m0 + m) * gridDim.x + blockIdx.x] = i;
+        }
+        for (int s = 0; s < p.n_norm_sel; ++s) {
+            float t = sss[0][s][m];
+            for (int w = 1; w < kWaves; ++w) t += sss[w][s][m];
+            p.ss[((int64_t)s * p.Mtot + p.m0 + m) * gridDim.x + blockIdx.x] = t;
         }
     }
+    last_block_reduce(p);
+}
+
+template <typename T, bool kLogits>
+hipError_t launch_tl(const GemvParams &p, int grid, hipStream_t s) {
+    dim3 g(grid), b(256);
+    if (p.M <= 1) hipLaunchKernelGGL((k_gemv<T, 1, kLogits>), g, b, 0, s, p);
+    else if (p.M <= 2) hipLaunchKernelGGL((k_gemv<T, 2, kLogits>), g, b, 0, s, p);
+    else if (p.M <= 4) hipLaunchKernelGGL((k_gemv<T, 4, kLogits>), g, b, 0, s, p);
+    else hipLaunchKernelGGL((k_gemv<T, 8, kLogits>), g, b, 0, s, p);
+    return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_t(const GemvParams &p, int grid, hipStream_t s) {
-    dim3 g(grid), b(256);
-    if (p.M <= 1) hipLaunchKernelGGL((k_gemv<T, 1>), g, b, 0, s, p);
-    else if (p.M <= 2) hipLaunchKernelGGL((k_gemv<T, 2>), g, b, 0, s, p);
-    else if (p.M <= 4) hipLaunchKernelGGL((k_gemv<T, 4>), g, b, 0, s, p);
-    else hipLaunchKernelGGL((k_gemv<T, 8>), g, b, 0, s, p);
-    return hipGetLastError();
+    return p.epi == EPI_LOGITS ? launch_tl<T, true>(p, grid, s) : launch_tl<T, false>(p, grid, s);
 }
 
-// ------------------------------------------------------------------ norm
+// ------------------------------------------------------------------ embed
 template <typename T>
-__global__ __launch_bounds__(256) void k_norm(NormParams p) {
-    extern __shared__ float src[];
+__global__ __launch_bounds__(256) void k_embed(EmbedParams p) {
     __shared__ float red[kWaves];
     const int m = blockIdx.x;
-    const int d = p.d;
-    int in_row = m;
-    if (p.gather_mseq > 0) {
-        int nt = p.gather_ntok ? p.gather_ntok[m] : p.gather_mseq;
-        nt = nt < 1 ? 1 : (nt > p.gather_mseq ? p.gather_mseq : nt);
-        in_row = m * p.gather_mseq + nt - 1;
-    }
-    float *h = p.h + (int64_t)in_row * d;
-    const float *add = p.add ? p.add + (int64_t)in_row * d : nullptr;
-    const float *s0 = p.src0 ? p.src0 + (int64_t)in_row * d : nullptr;
+    const int mseq = p.rows.mseq;
+    const int b = m / mseq, i = m - b * mseq;
+    if (m == 0)
+        for (int c = threadIdx.x; c < p.n_counters; c += blockDim.x) p.counters[c] = 0u;
+    int tok = p.tokens[(int64_t)b * p.tok_ld + (int64_t)i * p.tok_step];
+    tok = tok < 0 ? 0 : (tok >= p.vocab ? p.vocab - 1 : tok);
+    const T *e = reinterpret_cast<const T *>(p.E) + (int64_t)tok * p.d;
+    float *o = p.h + (int64_t)m * p.d;
     float ss = 0.f;
-    for (int j = threadIdx.x; j < d; j += 256) {
-        const float hv = h[j];
-        float v = hv;
-        if (add) {
-            v = hv + add[j];
-            if (p.gather_mseq == 0) h[j] = v;
-        }
-        if (p.h0copy) p.h0copy[(int64_t)in_row * d + j] = hv;
-        const float sv = s0 ? s0[j] + add[j] : v;
-        src[j] = sv;
-        ss = fmaf(sv, sv, ss);
+    for (int j = threadIdx.x; j < p.d; j += 256) {
+        const float v = Store<T>::to_f32(e[j]);
+        o[j] = v;
+        ss = fmaf(v, v, ss);
     }
     ss = wave_sum(ss);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    const float tot = red[0] + red[1] + red[2] + red[3];
-    const float inv = 1.0f / sqrtf(tot / (float)d + p.eps);
-    for (int g = 0; g < p.n_gains; ++g) {
-        const float *gain = p.gains + (int64_t)g * p.gain_stride;
-        T *o = reinterpret_cast<T *>(p.xn) + (int64_t)g * p.xn_sel_stride + (int64_t)m * d;
-        for (int j = threadIdx.x; j < d; j += 256) o[j] = Store<T>::from_f32(src[j] * inv * gain[j]);
+    // RoPE table of this row's position: angle pos * theta^(-2j/hd) formed and
+    // reduced modulo 2 pi in double precision, then sin / cos in float32
+    int pos = p.rows.start_pos[b] + i;
+    if (pos < 0 || pos >= p.rows.capacity) pos = 0;
+    const int half = p.hd / 2;
+    for (int j = threadIdx.x; j < half; j += 256) {
+        const double inv_freq = pow((double)p.rope_theta, -2.0 * (double)j / (double)p.hd);
+        double ang = (double)pos * inv_freq;
+        const double two_pi = 6.283185307179586476925286766559;
+        ang -= two_pi * rint(ang / two_pi);
+        float sn, cs;
+        sincosf((float)ang, &sn, &cs);
+        p.rope_cs[(int64_t)m * half + j] = make_float2(cs, sn);
     }
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void k_embed(const T *E, int vocab, int d, const int32_t *tokens,
-                                               int64_t tok_ld, int tok_step, int mseq, float *h) {
-    const int m = blockIdx.x;
-    const int b = m / mseq, i = m - b * mseq;
-    int tok = tokens[(int64_t)b * tok_ld + (int64_t)i * tok_step];
-    tok = tok < 0 ? 0 : (tok >= vocab ? vocab - 1 : tok);
-    const T *e = E + (int64_t)tok * d;
-    float *o = h + (int64_t)m * d;
-    for (int j = threadIdx.x; j < d; j += 256) o[j] = Store<T>::to_f32(e[j]);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const float tot = red[0] + red[1] + red[2] + red[3];
+        p.inv[m] = 1.0f / sqrtf(tot / (float)p.d + p.eps);
+    }
 }
 
 }  // namespace
@@ -194,21 +232,9 @@ hipError_t launch_gemv(int dtype, const GemvParams &p, int grid, hipStream_t s) 
     return dtype ? launch_t<uint16_t>(p, grid, s) : launch_t<float>(p, grid, s);
 }
 
-hipError_t launch_norm(int dtype, const NormParams &p, hipStream_t s) {
-    const size_t lds = (size_t)p.d * sizeof(float);
-    if (dtype) hipLaunchKernelGGL(k_norm<uint16_t>, dim3(p.M), dim3(256), lds, s, p);
-    else hipLaunchKernelGGL(k_norm<float>, dim3(p.M), dim3(256), lds, s, p);
-    return hipGetLastError();
-}
-
-hipError_t launch_embed(int dtype, const void *E, int vocab, int d, const int32_t *tokens,
-                        int64_t tok_ld, int tok_step, int B, int mseq, float *h, hipStream_t s) {
-    if (dtype)
-        hipLaunchKernelGGL(k_embed<uint16_t>, dim3(B * mseq), dim3(256), 0, s,
-                           reinterpret_cast<const uint16_t *>(E), vocab, d, tokens, tok_ld, tok_step, mseq, h);
-    else
-        hipLaunchKernelGGL(k_embed<float>, dim3(B * mseq), dim3(256), 0, s,
-                           reinterpret_cast<const float *>(E), vocab, d, tokens, tok_ld, tok_step, mseq, h);
+hipError_t launch_embed(int dtype, const EmbedParams &p, int Mtot, hipStream_t s) {
+    if (dtype) hipLaunchKernelGGL(k_embed<uint16_t>, dim3(Mtot), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL(k_embed<float>, dim3(Mtot), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

@@ -1,5 +1,4 @@
-// Vocabulary-wide reductions: the final arg-max of the lm-head sampling
-// partials, and the fused speculative accept / resample.
+// The fused speculative accept / resample over the vocabulary.
 //
 // Accept / resample follows the speculative sampling rule (Leviathan et al.;
 // Chen et al.; the EasySpec pages cite both and require the base distribution
@@ -30,16 +29,6 @@ __device__ __forceinline__ void block_argmax(float &v, int &i) {
     v = sv[0]; i = si[0];
     for (int w = 1; w < (int)(blockDim.x >> 6); ++w) argmax_merge(v, i, sv[w], si[w]);
     __syncthreads();
-}
-
-__global__ __launch_bounds__(256) void k_sample_reduce(const float *pv, const int32_t *pi, int n, int32_t *out,
-                                                       int stride) {
-    const int m = blockIdx.x;
-    float v = -INFINITY;
-    int i = 0x7FFFFFFF;
-    for (int j = threadIdx.x; j < n; j += blockDim.x) argmax_merge(v, i, pv[(int64_t)m * n + j], pi[(int64_t)m * n + j]);
-    block_argmax(v, i);
-    if (threadIdx.x == 0) out[(int64_t)m * stride] = i;
 }
 
 __device__ __forceinline__ const float *acc_row(const AcceptParams &p, int b, int r) {
@@ -186,12 +175,6 @@ __global__ __launch_bounds__(64) void k_acc_final(AcceptParams p) {
 }  // namespace
 
 int accept_chunks(int vocab) { return (vocab + kChunk - 1) / kChunk; }
-
-hipError_t launch_sample_reduce(const float *pv, const int32_t *pi, int n, int M, int32_t *out, int stride,
-                                hipStream_t s) {
-    hipLaunchKernelGGL(k_sample_reduce, dim3(M), dim3(256), 0, s, pv, pi, n, out, stride);
-    return hipGetLastError();
-}
 
 hipError_t launch_accept(const AcceptParams &p, hipStream_t s) {
     const int rows = p.inv_temp == 0.0f ? p.k + 1 : 2 * p.k + 1;

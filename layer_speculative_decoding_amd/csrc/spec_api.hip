@@ -42,29 +42,36 @@ inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace layout for R activation rows and sets of at most G layers.
 struct Carve {
-    size_t h, h0, abuf, xn, q, o, act, pacc, pml, pval, pidx, total;
+    size_t h, h0, abuf, q, o, act, pacc, pml, pval, pidx, ss, inv, rope, ctr, total;
+    int n_counters;
 };
+
+constexpr int kPartialsMax = 2048;   // largest grid of a partial-sum producer
 
 Carve carve(const spec_model *m, int batch, int max_m, int G) {
     const size_t R = (size_t)batch * max_m;
     const size_t d = m->d.d_model, xs = m->xs;
     const size_t hq = m->d.n_q_heads, hd = m->d.head_dim;
     const size_t prow = R < 64 ? R : 64;
-    const size_t nparts = (size_t)gemv_grid((m->d.vocab + 1) / 2);
+    const size_t nsel = G < kMaxSel ? G : kMaxSel;
     Carve c{};
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
     c.h = take(R * d * 4);
     c.h0 = take(R * d * 4);
     c.abuf = take((size_t)G * R * d * 4);
-    c.xn = take((size_t)G * R * d * xs);
     c.q = take((size_t)G * R * hq * hd * 4);
     c.o = take((size_t)G * R * hq * hd * xs);
     c.act = take(R * (size_t)m->d.d_ffn * xs);
     c.pacc = take((size_t)attention_split_max() * G * prow * hq * hd * 4);
     c.pml = take((size_t)attention_split_max() * G * prow * hq * 2 * 4);
-    c.pval = take((size_t)batch * nparts * 4);
-    c.pidx = take((size_t)batch * nparts * 4);
+    c.pval = take((size_t)batch * kPartialsMax * 4);
+    c.pidx = take((size_t)batch * kPartialsMax * 4);
+    c.ss = take(nsel * R * kPartialsMax * 4);
+    c.inv = take(nsel * R * 4);
+    c.rope = take(R * (hd / 2) * 8);
+    c.n_counters = 1 + G * m->d.n_kv_heads * batch;
+    c.ctr = take((size_t)c.n_counters * 4);
     c.total = off;
     return c;
 }
@@ -96,38 +103,54 @@ int mfma_min_rows() {
     return v;
 }
 
-// Weight-streaming product over Mtot activation rows, chunked by the kernel's
-// row limit.  *grid_out receives the grid of the launches (the number of
-// sampling partials per row for EPI_LOGITS).
-hipError_t gemv_chunked(const spec_model *m, GemvParams p, int Mtot, hipStream_t s, int *grid_out = nullptr) {
+// Weight-streaming product over the call's Mtot activation rows (p.Mtot),
+// chunked by the kernel's row limit.
+hipError_t product(const Fwd &f, GemvParams p) {
+    const spec_model *m = f.m;
+    const int Mtot = p.Mtot;
+    p.counter = at<unsigned>(f.ws, f.c.ctr);
+    p.ss = at<float>(f.ws, f.c.ss);
+    p.part_val = at<float>(f.ws, f.c.pval);
+    p.part_idx = at<int32_t>(f.ws, f.c.pidx);
     GemvParams q = p;
+    q.pair_block = p.pair_block == 2 ? 32 : p.pair_block;   // adjacent rows -> adjacent 16-row blocks
     q.M = Mtot < 32 ? Mtot : 32;
     const bool mfma = m->d.dtype == SPEC_BF16 && Mtot >= mfma_min_rows() && gemm_mfma_supported(q) &&
-                      !(p.epi == EPI_LOGITS && Mtot > 8);
+                      (p.n_units * 2) % 32 == 0;
     if (mfma) {
         q.n_units = p.n_units / 16;           // row pairs -> pairs of 16-row blocks
         const int grid = gemm_mfma_grid(q.n_units);
         const int ks = gemm_mfma_splits(q.n_units, p.K);
-        if (grid_out) *grid_out = grid;
         const int mr = gemm_mfma_max_rows();
         for (int m0 = 0; m0 < Mtot; m0 += mr) {
             q.m0 = m0;
             q.M = (Mtot - m0) < mr ? (Mtot - m0) : mr;
-            hipError_t e = launch_gemm_mfma(q, grid, ks, s);
+            hipError_t e = launch_gemm_mfma(q, grid, ks, f.s);
             if (e != hipSuccess) return e;
         }
         return hipSuccess;
     }
     const int mr = gemv_max_rows();
     const int grid = gemv_grid(p.n_units);
-    if (grid_out) *grid_out = grid;
     for (int m0 = 0; m0 < Mtot; m0 += mr) {
         p.m0 = m0;
         p.M = (Mtot - m0) < mr ? (Mtot - m0) : mr;
-        hipError_t e = launch_gemv(m->d.dtype, p, grid, s);
+        hipError_t e = launch_gemv(m->d.dtype, p, grid, f.s);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+// Embedding, 1/rms of every row, RoPE table, counter reset.
+hipError_t run_embed(const Fwd &f, const int32_t *tokens, int64_t tok_ld, int tok_step) {
+    const spec_model *m = f.m;
+    EmbedParams e{};
+    e.E = m->w.embed; e.vocab = m->d.vocab; e.d = m->d.d_model;
+    e.tokens = tokens; e.tok_ld = tok_ld; e.tok_step = tok_step; e.rows = f.rows;
+    e.h = at<float>(f.ws, f.c.h); e.inv = at<float>(f.ws, f.c.inv); e.eps = m->d.rms_eps;
+    e.rope_cs = at<float2>(f.ws, f.c.rope); e.hd = m->d.head_dim; e.rope_theta = m->d.rope_theta;
+    e.counters = at<unsigned>(f.ws, f.c.ctr); e.n_counters = f.c.n_counters;
+    return launch_embed(m->d.dtype, e, f.batch * f.mseq, f.s);
 }
 
 // One stage: attention of the set [l0, l0 + n) on the stage input h0, then
@@ -141,35 +164,29 @@ hipError_t run_stage(const Fwd &f, int l0, int n, int mlp_mode) {
     float *h = at<float>(f.ws, f.c.h);
     float *h0 = at<float>(f.ws, f.c.h0);
     float *abuf = at<float>(f.ws, f.c.abuf);
-    void *xn = at<char>(f.ws, f.c.xn);
+    float *inv = at<float>(f.ws, f.c.inv);
     float *q = at<float>(f.ws, f.c.q);
     void *o = at<char>(f.ws, f.c.o);
     void *act = at<char>(f.ws, f.c.act);
     hipError_t e;
 
-    // 1. one RMS of h0, N gains -> xn[i]
-    NormParams np{};
-    np.h = h; np.add = nullptr; np.src0 = nullptr; np.h0copy = par ? h0 : nullptr;
-    np.gains = m->w.attn_norm + (size_t)l0 * dm;
-    np.n_gains = n; np.gain_stride = dm;
-    np.xn = xn; np.xn_sel_stride = (int64_t)R * dm;
-    np.M = R; np.d = dm; np.eps = d.rms_eps; np.gather_mseq = 0; np.gather_ntok = nullptr;
-    if ((e = launch_norm(d.dtype, np, f.s)) != hipSuccess) return e;
-
-    // 2. grouped QKV + RoPE + KV append over the N layers' concatenated rows
+    // 1. grouped QKV over the N layers' concatenated rows: operand = one RMS
+    //    of h0 with each layer's gain; epilogue = RoPE + KV append
     GemvParams gp{};
+    gp.Mtot = R; gp.d = dm; gp.eps = d.rms_eps;
     gp.W = layer_ptr(m->w.wqkv, l0, (size_t)D * dm, xs);
     gp.K = dm; gp.n_units = n * D / 2; gp.pair_block = d.head_dim; gp.rows_per_sel = D;
-    gp.X = xn; gp.x_sel_stride = (int64_t)R * dm;
+    gp.xmode = X_NORM; gp.xh = h; gp.xgain = m->w.attn_norm + (size_t)l0 * dm; gp.xgain_stride = dm; gp.xinv = inv;
     gp.bias = m->w.bqkv ? m->w.bqkv + (size_t)l0 * D : nullptr;
     gp.epi = EPI_QKV_ROPE;
     gp.q_out = q; gp.q_sel_stride = (int64_t)R * qd;
     gp.kc = f.kv->k; gp.vc = f.kv->v; gp.layer0 = l0; gp.batch = f.batch;
-    gp.hq = d.n_q_heads; gp.hkv = d.n_kv_heads; gp.hd = d.head_dim; gp.rope_theta = d.rope_theta;
+    gp.hq = d.n_q_heads; gp.hkv = d.n_kv_heads; gp.hd = d.head_dim;
+    gp.rope_cs = at<float2>(f.ws, f.c.rope);
     gp.rows = f.rows;
-    if ((e = gemv_chunked(m, gp, R, f.s)) != hipSuccess) return e;
+    if ((e = product(f, gp)) != hipSuccess) return e;
 
-    // 3. grouped attention
+    // 2. grouped attention
     AttnParams ap{};
     ap.q = q; ap.q_sel_stride = (int64_t)R * qd;
     ap.kc = f.kv->k; ap.vc = f.kv->v; ap.layer0 = l0; ap.n_group = n; ap.batch = f.batch;
@@ -177,71 +194,71 @@ hipError_t run_stage(const Fwd &f, int l0, int n, int mlp_mode) {
     ap.rows = f.rows; ap.max_pos = f.max_pos;
     ap.splits = attention_splits(n, f.batch, d.n_q_heads, d.n_kv_heads, f.mseq, f.max_pos);
     ap.o = o; ap.o_sel_stride = (int64_t)R * qd;
-    ap.part_acc = at<float>(f.ws, f.c.pacc); ap.part_ml = at<float>(f.ws, f.c.pml); ap.Mtot = R;
+    ap.part_acc = at<float>(f.ws, f.c.pacc); ap.part_ml = at<float>(f.ws, f.c.pml);
+    ap.counters = at<unsigned>(f.ws, f.c.ctr) + 1; ap.Mtot = R;
     if ((e = launch_attention(d.dtype, ap, f.s)) != hipSuccess) return e;
 
-    // 4. grouped O projection -> a_i
+    // 3. grouped O projection: a_0 goes into the residual (sequential MLPs),
+    //    the others wait in abuf; partial sums give the MLP inputs' RMS
     gp = GemvParams{};
+    gp.Mtot = R; gp.d = dm; gp.eps = d.rms_eps;
     gp.W = layer_ptr(m->w.wo, l0, (size_t)dm * qd, xs);
     gp.K = qd; gp.n_units = n * dm / 2; gp.pair_block = 2; gp.rows_per_sel = dm;
-    gp.X = o; gp.x_sel_stride = (int64_t)R * qd;
-    gp.epi = EPI_STORE; gp.out = abuf; gp.out_ld = dm; gp.out_sel_stride = (int64_t)R * dm;
-    if ((e = gemv_chunked(m, gp, R, f.s)) != hipSuccess) return e;
+    gp.xmode = X_PLAIN; gp.X = o; gp.x_sel_stride = (int64_t)R * qd;
+    gp.epi = EPI_ATTN_OUT; gp.h = h; gp.h0 = h0; gp.par_mlp = par ? 1 : 0;
+    gp.out = abuf; gp.out_sel_stride = (int64_t)R * dm;
+    gp.n_norm_sel = par ? n : 1; gp.inv_out = inv;
+    if ((e = product(f, gp)) != hipSuccess) return e;
 
-    // 5. MLPs in set order
+    // 4. MLPs in set order
     for (int i = 0; i < n; ++i) {
         const int l = l0 + i;
-        np = NormParams{};
-        np.h = h; np.add = abuf + (size_t)i * R * dm; np.src0 = par ? h0 : nullptr; np.h0copy = nullptr;
-        np.gains = m->w.ffn_norm + (size_t)l * dm; np.n_gains = 1; np.gain_stride = dm;
-        np.xn = xn; np.xn_sel_stride = 0; np.M = R; np.d = dm; np.eps = d.rms_eps;
-        if ((e = launch_norm(d.dtype, np, f.s)) != hipSuccess) return e;
-
         gp = GemvParams{};
+        gp.Mtot = R; gp.d = dm; gp.eps = d.rms_eps;
         gp.W = layer_ptr(m->w.w_gate_up, l, (size_t)2 * d.d_ffn * dm, xs);
         gp.K = dm; gp.n_units = d.d_ffn; gp.pair_block = 2 * d.d_ffn; gp.rows_per_sel = 2 * d.d_ffn;
-        gp.X = xn; gp.x_sel_stride = 0;
+        gp.xmode = X_NORM; gp.xgain = m->w.ffn_norm + (size_t)l * dm;
+        if (par) { gp.xh = h0; gp.xadd = abuf + (size_t)i * R * dm; gp.xinv = inv + (size_t)i * R; }
+        else { gp.xh = h; gp.xinv = inv; }
         gp.epi = EPI_SILU_MUL; gp.act = act; gp.act_ld = d.d_ffn;
-        if ((e = gemv_chunked(m, gp, R, f.s)) != hipSuccess) return e;
+        if ((e = product(f, gp)) != hipSuccess) return e;
 
         gp = GemvParams{};
+        gp.Mtot = R; gp.d = dm; gp.eps = d.rms_eps;
         gp.W = layer_ptr(m->w.w_down, l, (size_t)dm * d.d_ffn, xs);
         gp.K = d.d_ffn; gp.n_units = dm / 2; gp.pair_block = 2; gp.rows_per_sel = dm;
-        gp.X = act; gp.x_sel_stride = 0;
-        gp.epi = EPI_RESID_ADD; gp.out = h; gp.out_ld = dm;
-        if ((e = gemv_chunked(m, gp, R, f.s)) != hipSuccess) return e;
+        gp.xmode = X_PLAIN; gp.X = act;
+        gp.epi = EPI_RESID_ADD; gp.h = h;
+        // sequential: h += m_i + a_{i+1} (the next member's attention output);
+        // parallel: h += a_i + m_i
+        gp.add2 = par ? abuf + (size_t)i * R * dm : (i + 1 < n ? abuf + (size_t)(i + 1) * R * dm : nullptr);
+        gp.n_norm_sel = 1; gp.inv_out = inv;
+        if ((e = product(f, gp)) != hipSuccess) return e;
     }
     return hipSuccess;
 }
 
-// Final norm (optionally of the last valid row of each sequence) + lm head.
+// Final RMSNorm (folded into the operand; optionally of the last valid row of
+// each sequence) + lm head; with token_out, the sampled / arg-max token of each
+// sampling row is reduced by the last block of the lm-head launch.
 hipError_t run_head(const Fwd &f, bool last_only, const int32_t *ntok, float *logits, int64_t logits_ld,
                     float inv_temp, uint64_t seed, const int32_t *samp_pos, const int32_t *samp_ntok,
                     int samp_nconst, int32_t *token_out, int token_stride) {
     const spec_model *m = f.m;
     const int dm = m->d.d_model;
     const int R = f.batch * f.mseq;
-    const int Mh = last_only ? f.batch : R;
-    NormParams np{};
-    np.h = at<float>(f.ws, f.c.h);
-    np.gains = m->w.final_norm; np.n_gains = 1; np.gain_stride = dm;
-    np.xn = at<char>(f.ws, f.c.xn); np.xn_sel_stride = 0; np.M = Mh; np.d = dm; np.eps = m->d.rms_eps;
-    np.gather_mseq = last_only ? f.mseq : 0; np.gather_ntok = ntok;
-    hipError_t e = launch_norm(m->d.dtype, np, f.s);
-    if (e != hipSuccess) return e;
+    if (!token_out && !logits) return hipSuccess;
     GemvParams gp{};
+    gp.Mtot = last_only ? f.batch : R; gp.d = dm; gp.eps = m->d.rms_eps;
     gp.W = m->w.lm_head; gp.K = dm; gp.n_units = m->d.vocab / 2; gp.pair_block = 2; gp.rows_per_sel = m->d.vocab;
-    gp.X = np.xn; gp.x_sel_stride = 0;
+    gp.xmode = X_NORM; gp.xh = at<float>(f.ws, f.c.h); gp.xgain = m->w.final_norm; gp.xgain_stride = 0;
+    gp.xinv = at<float>(f.ws, f.c.inv);
+    gp.xgather_mseq = last_only ? f.mseq : 0; gp.xgather_ntok = ntok;
     gp.epi = token_out ? EPI_LOGITS : EPI_STORE;
     gp.out = logits; gp.out_ld = logits_ld; gp.out_sel_stride = 0;
     gp.inv_temp = inv_temp; gp.seed = seed; gp.samp_pos = samp_pos; gp.samp_ntok = samp_ntok;
-    gp.samp_nconst = samp_nconst;
-    gp.part_val = at<float>(f.ws, f.c.pval); gp.part_idx = at<int32_t>(f.ws, f.c.pidx);
-    if (!token_out && !logits) return hipSuccess;
-    int grid = 0;
-    if ((e = gemv_chunked(m, gp, Mh, f.s, &grid)) != hipSuccess) return e;
-    if (token_out) return launch_sample_reduce(gp.part_val, gp.part_idx, grid, Mh, token_out, token_stride, f.s);
-    return hipSuccess;
+    gp.samp_nconst = samp_nconst; gp.token_out = token_out; gp.token_stride = token_stride;
+    return product(f, gp);
 }
 
 spec_status check_model(const spec_model *m, const spec_kv *kv, int batch) {
@@ -357,6 +374,8 @@ spec_status spec_draft_group_step(const spec_model *draft, const spec_kv *kv, co
         if (n < 1) return fail(SPEC_ERR_PLAN, "stage %d is empty or out of order", s);
         if (n > G) G = n;
     }
+    if (flags == SPEC_MLP_PARALLEL && G > kMaxSel)
+        return fail(SPEC_ERR_UNSUPPORTED, "parallel MLPs support sets of at most %d layers", kMaxSel);
     if (!tokens || !positions || !token_out) return fail(SPEC_ERR_INVALID_ARG, "NULL tokens/positions/token_out");
     if (tokens_stride < 1 || token_out_stride < 1) return fail(SPEC_ERR_INVALID_ARG, "strides must be >= 1");
     if (logits_out && logits_stride < draft->d.vocab) return fail(SPEC_ERR_INVALID_ARG, "logits_stride < vocab");
@@ -367,8 +386,7 @@ spec_status spec_draft_group_step(const spec_model *draft, const spec_kv *kv, co
 
     Fwd f{draft, kv, batch, 1, max_pos, RowMap{positions, nullptr, 1, kv->capacity}, workspace,
           carve(draft, batch, 1, G), (hipStream_t)stream};
-    hipError_t e = launch_embed(draft->d.dtype, draft->w.embed, draft->d.vocab, draft->d.d_model, tokens,
-                                tokens_stride, 0, batch, 1, at<float>(workspace, f.c.h), f.s);
+    hipError_t e = run_embed(f, tokens, tokens_stride, 0);
     if (e != hipSuccess) return hip_fail(e, "embed");
     for (int s = 0; s < n_stages; ++s) {
         e = run_stage(f, plan_offsets[s], plan_offsets[s + 1] - plan_offsets[s], flags);
@@ -386,8 +404,7 @@ static spec_status precise_forward(const spec_model *m, const spec_kv *kv, int b
                                    void *ws, hipStream_t s, Fwd &f) {
     f = Fwd{m, kv, batch, mseq, max_pos, RowMap{start_pos, n_tokens, mseq, kv->capacity}, ws,
             carve(m, batch, mseq, 1), s};
-    hipError_t e = launch_embed(m->d.dtype, m->w.embed, m->d.vocab, m->d.d_model, tokens, mseq, 1, batch, mseq,
-                                at<float>(ws, f.c.h), s);
+    hipError_t e = run_embed(f, tokens, mseq, 1);
     if (e != hipSuccess) return hip_fail(e, "embed");
     for (int l = 0; l < m->d.n_layers; ++l) {
         e = run_stage(f, l, 1, SPEC_MLP_SEQUENTIAL);

@@ -107,6 +107,22 @@ __device__ __forceinline__ void gumbel4(uint64_t seed, uint32_t b, uint32_t pos,
 #pragma unroll
     for (int i = 0; i < 4; ++i) g[i] = -logf(-logf(word_to_uniform(r.w[i])));
 }
+__device__ __forceinline__ float pick_word(const Philox4 &r, uint32_t i) {
+    const uint64_t w = i == 0 ? r.w[0] : (i == 1 ? r.w[1] : (i == 2 ? r.w[2] : r.w[3]));
+    return -logf(-logf(word_to_uniform(w)));
+}
+// Gumbel noise of vocab entries v0 and v1 (one Philox block when they share it).
+__device__ __forceinline__ void gumbel_pair(uint64_t seed, uint32_t b, uint32_t pos, uint32_t purpose,
+                                            uint32_t v0, uint32_t v1, float &g0, float &g1) {
+    const Philox4 r = philox4x64_10(v0 >> 2, pos, 0, purpose, seed, b);
+    g0 = pick_word(r, v0 & 3);
+    if ((v1 >> 2) == (v0 >> 2)) {
+        g1 = pick_word(r, v1 & 3);
+    } else {
+        const Philox4 r1 = philox4x64_10(v1 >> 2, pos, 0, purpose, seed, b);
+        g1 = pick_word(r1, v1 & 3);
+    }
+}
 __device__ __forceinline__ float accept_uniform(uint64_t seed, uint32_t b, uint32_t pos) {
     Philox4 r = philox4x64_10(0, pos, 0, kAccept, seed, b);
     return word_to_uniform(r.w[0]);

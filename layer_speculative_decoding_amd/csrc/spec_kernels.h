@@ -5,6 +5,8 @@
 
 namespace spec {
 
+constexpr int kMaxSel = 8;   // largest layer-parallel set whose MLP inputs get their own RMS
+
 // Activation row m of a call -> (sequence b, position, valid).  Rows are
 // sequence-major: m = b * mseq + i, position = start_pos[b] + i, valid iff
 // i < n_tok[b] (n_tok NULL: all) and 0 <= position < capacity.
@@ -19,35 +21,68 @@ enum GemvEpi : int {
     EPI_STORE = 0,      // out[m * out_ld + sel * out_sel_stride + row_in_sel] = y
     EPI_QKV_ROPE = 1,   // RoPE on q/k pairs; q -> q_out, k/v -> KV cache
     EPI_SILU_MUL = 2,   // act[m * act_ld + unit] = round(silu(gate) * up)
-    EPI_RESID_ADD = 3,  // out[m * out_ld + row] += y
-    EPI_LOGITS = 4,     // EPI_STORE (if out) + Gumbel / greedy arg-max partials
+    EPI_RESID_ADD = 3,  // h[m][row] += y (+ add2[m][row]); row-norm partials of h
+    EPI_LOGITS = 4,     // store (if out) + Gumbel / greedy arg-max, last block reduces
+    EPI_ATTN_OUT = 5,   // sequential MLPs: sel 0 -> h += y (+ partials), sel > 0 -> abuf
+                        // parallel MLPs: every sel -> abuf, partials of h0 + y; sel 0
+                        // also copies h to h0
+};
+
+// How a product reads its activations.
+enum XMode : int {
+    X_PLAIN = 0,   // X[sel * x_sel_stride + m * K + k] (activation dtype)
+    X_NORM = 1,    // round(gain_sel[k] * (xh[hrow][k] + xadd[sel][hrow][k]) * inv[isel][hrow])
 };
 
 struct GemvParams {
-    // weights: rows of length K, row-major; a unit is the row pair
-    // (blk * pair_block + j, blk * pair_block + j + pair_block / 2) with
-    // blk = u / (pair_block / 2), j = u % (pair_block / 2).
+    // weights: rows of length K, row-major.  VALU GEMV: a unit is the row pair
+    // (blk * pair_block + j, ... + pair_block / 2), blk = u / (pair_block / 2),
+    // j = u % (pair_block / 2).  MFMA: the same with 16-row blocks.
     const void *W;
     int K;
     int n_units;
     int pair_block;
     int rows_per_sel;     // activation set index sel = row / rows_per_sel
-    // activations X: set sel, row m, element k at X[sel * x_sel_stride + m * K + k]
-    const void *X;
-    int64_t x_sel_stride;
     int m0, M;            // this launch covers rows m0 .. m0 + M - 1
+    int Mtot;             // rows of the whole call
+    // activations
+    int xmode;
+    const void *X;        // X_PLAIN
+    int64_t x_sel_stride;
+    const float *xh;      // X_NORM: residual rows [Mtot][K]
+    const float *xadd;    // X_NORM, nullable: [sel][Mtot][K]
+    int64_t xadd_sel_stride;
+    const float *xgain;   // X_NORM: gain of set member sel at xgain + sel * xgain_stride
+    int64_t xgain_stride;
+    const float *xinv;    // X_NORM: 1/rms at xinv[isel * Mtot + hrow]
+    int xinv_per_sel;     // isel = xinv_per_sel ? sel : 0
+    int xgather_mseq;     // > 0: activation row m reads residual row
+    const int32_t *xgather_ntok;   //   m * mseq + ntok[m] - 1 (last valid row)
     const float *bias;    // [rows] or NULL
     int epi;
     float *out;
     int64_t out_ld, out_sel_stride;
     void *act;
     int64_t act_ld;
+    // RESID_ADD / ATTN_OUT
+    float *h;             // [Mtot][d]
+    float *h0;            // [Mtot][d] (parallel MLPs)
+    const float *add2;    // RESID_ADD: nullable extra addend [Mtot][d]
+    int par_mlp;          // ATTN_OUT: parallel-MLP reading
+    // row-norm partials of the updated residual: ss[sel][m][block]; the last
+    // block to finish writes inv[sel][m] = 1 / sqrt(sum / d + eps)
+    float *ss;
+    float *inv_out;
+    unsigned *counter;
+    int n_norm_sel;       // 0: no partials; else number of sels with partials
+    int d;
+    float eps;
     // QKV epilogue
     float *q_out;
     int64_t q_sel_stride;  // elements between group layers in q_out
     void *kc, *vc;         // KV arenas [L][B][hkv][cap][hd]
     int layer0, batch, hq, hkv, hd;
-    float rope_theta;
+    const float2 *rope_cs; // [Mtot][hd/2] (cos, sin) of each row's position
     RowMap rows;
     // LOGITS epilogue: sampling row m is sequence m0 + m; the decided
     // position is samp_pos[b] + (samp_ntok ? samp_ntok[b] : samp_nconst).
@@ -56,11 +91,13 @@ struct GemvParams {
     const int32_t *samp_pos;
     const int32_t *samp_ntok;
     int samp_nconst;
-    float *part_val;       // [M][gridDim.x]
+    float *part_val;       // [Mtot][gridDim.x]
     int32_t *part_idx;
+    int32_t *token_out;    // last block writes the arg-max of row m here
+    int token_stride;
 };
 
-// dtype: 0 float32, 1 bfloat16 (weights, activations X and act share it).
+// dtype: 0 float32, 1 bfloat16 (weights and activation buffers share it).
 // VALU GEMV: units are row pairs, M <= gemv_max_rows() per launch.
 hipError_t launch_gemv(int dtype, const GemvParams &p, int grid, hipStream_t s);
 int gemv_max_rows();
@@ -73,34 +110,29 @@ int gemm_mfma_max_rows();
 int gemm_mfma_grid(int n_units);
 int gemm_mfma_splits(int n_units, int K);
 
-// h[m] (+)= add[m]; normalise (src0 ? src0[m] + add[m] : h[m]) with each of
-// n_gains gains and write xn[g][m][:] (rounded to the activation dtype).
-// h0copy (nullable) receives h[m] before the add.  If gather_mseq > 0, output
-// row m reads input row m * gather_mseq + (gather_ntok ? gather_ntok[m] :
-// gather_mseq) - 1 and h is not written.
-struct NormParams {
+// Embedding of every row (h = E[token]), its 1/rms, the RoPE (cos, sin) of
+// its position, and zeroing of the call's completion counters.
+struct EmbedParams {
+    const void *E;
+    int vocab, d;
+    const int32_t *tokens;
+    int64_t tok_ld;
+    int tok_step;
+    RowMap rows;
     float *h;
-    const float *add;
-    const float *src0;
-    float *h0copy;
-    const float *gains;
-    int n_gains;
-    int64_t gain_stride;
-    void *xn;
-    int64_t xn_sel_stride;
-    int M, d;
+    float *inv;            // [Mtot]
     float eps;
-    int gather_mseq;
-    const int32_t *gather_ntok;
+    float2 *rope_cs;       // [Mtot][hd/2]
+    int hd;
+    float rope_theta;
+    unsigned *counters;
+    int n_counters;
 };
-hipError_t launch_norm(int dtype, const NormParams &p, hipStream_t s);
+hipError_t launch_embed(int dtype, const EmbedParams &p, int Mtot, hipStream_t s);
 
-// h[m][:] = E[clamp(tokens[...])] for m = b * mseq + i; token of row m is
-// tokens[b * tok_ld + i * tok_step].
-hipError_t launch_embed(int dtype, const void *E, int vocab, int d, const int32_t *tokens,
-                        int64_t tok_ld, int tok_step, int B, int mseq, float *h, hipStream_t s);
-
-// Grouped causal attention over n_group consecutive layers.
+// Grouped causal attention over n_group consecutive layers.  With several
+// key splits the last split block of each (layer, kv head, sequence) merges
+// the partials.
 struct AttnParams {
     const float *q;        // [g][Mtot][hq][hd]
     int64_t q_sel_stride;
@@ -113,15 +145,12 @@ struct AttnParams {
     int64_t o_sel_stride;
     float *part_acc;       // [splits][g][Mtot][hq][hd]
     float *part_ml;        // [splits][g][Mtot][hq][2]
+    unsigned *counters;    // [g][hkv][batch]
     int Mtot;
 };
 hipError_t launch_attention(int dtype, const AttnParams &p, hipStream_t s);
 int attention_splits(int n_group, int batch, int hq, int hkv, int mseq, int max_pos);
 int attention_split_max();
-
-// Arg-max reduction of lm-head partials -> tokens.
-hipError_t launch_sample_reduce(const float *part_val, const int32_t *part_idx, int n_parts, int M,
-                                int32_t *token_out, int token_stride, hipStream_t s);
 
 // Accept / resample.
 struct AcceptParams {
