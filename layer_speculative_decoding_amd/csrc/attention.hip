@@ -5,8 +5,8 @@
 // split).  Its query vectors are the rows of the block times the q heads that
 // share the kv head (GQA), so every K/V tile staged in LDS is used by all of
 // them.  Softmax is online (running max / sum per query vector); with several
-// key splits the partial (max, sum, unnormalised output) are merged in split
-// order by the last split block to finish (completion counter, reset after).
+// key splits the partial (max, sum, unnormalised output) are merged by
+// k_attn_merge in split order.
 #include "spec_device.h"
 #include "spec_kernels.h"
 
@@ -159,8 +159,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
         }
         return;
     }
-    // several key splits: publish (m, l, unnormalised acc); the last split
-    // block of this (layer, kv head, sequence) merges them in split order
+    // several key splits: publish (max, sum, unnormalised output)
     const int64_t stride_sp = (int64_t)p.n_group * p.Mtot * p.hq;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
@@ -177,39 +176,36 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
             }
         }
     }
-    __shared__ bool is_last;
-    unsigned *ctr = p.counters + ((int64_t)gi * p.hkv + kvh) * p.batch + b;
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) is_last = atomicAdd(ctr, 1u) == (unsigned)(p.splits - 1);
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-        const int idx = tid + 256 * r;
-        if (idx < QV * HD) {
-            const int qv = idx / HD, d = idx - (idx / HD) * HD;
-            const int rr = qv / G, g = qv - rr * G;
-            const int row = b * mseq + i0 + rr;
-            const int64_t pr0 = ((int64_t)gi * p.Mtot + row) * p.hq + kvh * G + g;
-            float mx = -INFINITY;
-            for (int s2 = 0; s2 < p.splits; ++s2) mx = fmaxf(mx, p.part_ml[(pr0 + s2 * stride_sp) * 2]);
-            float num = 0.f, den = 0.f;
-            if (mx != -INFINITY) {
-                for (int s2 = 0; s2 < p.splits; ++s2) {
-                    const int64_t pr = pr0 + s2 * stride_sp;
-                    const float mm = p.part_ml[pr * 2];
-                    if (mm == -INFINITY) continue;
-                    const float w = expf(mm - mx);
-                    num = fmaf(w, p.part_acc[pr * HD + d], num);
-                    den = fmaf(w, p.part_ml[pr * 2 + 1], den);
-                }
+}
+
+// Merge the key splits of one (layer, row, q head) per wave: out = sum_s w_s
+// acc_s / sum_s w_s l_s with w_s = exp(m_s - max_s m_s), in split order.
+template <typename T>
+__global__ __launch_bounds__(256) void k_attn_merge(AttnParams p) {
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t n_items = (int64_t)p.n_group * p.Mtot * p.hq;
+    if (item >= n_items) return;
+    const int HD = p.hd;
+    const int64_t stride_sp = n_items;
+    float mx = -INFINITY;
+    for (int s2 = 0; s2 < p.splits; ++s2) mx = fmaxf(mx, p.part_ml[(item + s2 * stride_sp) * 2]);
+    const int gi = (int)(item / ((int64_t)p.Mtot * p.hq));
+    const int64_t rh = item - (int64_t)gi * p.Mtot * p.hq;       // row * hq + head
+    T *o = reinterpret_cast<T *>(p.o) + (int64_t)gi * p.o_sel_stride + rh * HD;
+    for (int d = lane; d < HD; d += 64) {
+        float num = 0.f, den = 0.f;
+        if (mx != -INFINITY) {
+            for (int s2 = 0; s2 < p.splits; ++s2) {
+                const int64_t pr = item + s2 * stride_sp;
+                const float mm = p.part_ml[pr * 2];
+                const float w = mm == -INFINITY ? 0.f : expf(mm - mx);
+                num = fmaf(w, p.part_acc[pr * HD + d], num);
+                den = fmaf(w, p.part_ml[pr * 2 + 1], den);
             }
-            obase[(int64_t)row * p.hq * HD + (kvh * G + g) * HD + d] = S::from_f32(den > 0.f ? num / den : 0.f);
         }
+        o[d] = Store<T>::from_f32(den > 0.f ? num / den : 0.f);
     }
-    if (tid == 0) *ctr = 0u;
 }
 
 template <typename T, int HD>
@@ -218,6 +214,10 @@ hipError_t launch_hd(const AttnParams &p, hipStream_t s) {
     const int QB = (kQV / G) > 0 ? kQV / G : 1;
     dim3 grid((p.rows.mseq + QB - 1) / QB, p.n_group * p.hkv, p.batch * p.splits);
     hipLaunchKernelGGL((k_attn<T, HD>), grid, dim3(256), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.splits == 1) return e;
+    const int64_t items = (int64_t)p.n_group * p.Mtot * p.hq;
+    hipLaunchKernelGGL(k_attn_merge<T>, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

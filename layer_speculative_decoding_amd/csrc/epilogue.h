@@ -2,15 +2,14 @@
 // GEMV and MFMA skinny GEMM).
 //
 //  * X_NORM operands: RMSNorm is folded into the consumer.  Activation row m
-//    is round(gain[k] * h[k] * inv_rms), with inv_rms produced by whoever last
-//    wrote h (the embedding, or the residual-add epilogue below), so no
-//    separate normalisation launch exists on the path.
+//    is round(gain[k] * h[k] * inv_rms); whoever last wrote h (the embedding,
+//    or a residual-add epilogue below) left per-block partial sums of squares,
+//    and every consuming block sums a row's partials in block order, so no
+//    separate normalisation launch and no cross-block synchronisation exist.
 //  * Epilogues get the two output rows r0, r1 of a unit for activation row m,
 //    add the bias and apply the fused consumer: store, QKV RoPE + KV append,
 //    SiLU gate, residual add, attention-output routing, logits + arg-max.
-//  * Residual writers also emit per-block partial sums of squares of the new
-//    rows; the last block of the launch (completion counter) sums the partials
-//    in a fixed order and writes the next consumer's 1/rms.
+//  * Residual writers emit those per-block partial sums of squares.
 #pragma once
 #include "spec_device.h"
 #include "spec_kernels.h"
@@ -34,8 +33,20 @@ __device__ __forceinline__ int x_row(const GemvParams &p, int gm) {
     return gm * p.xgather_mseq + nt - 1;
 }
 
-__device__ __forceinline__ float x_inv(const GemvParams &p, int sel, int hrow) {
-    return p.xinv[(int64_t)(p.xinv_per_sel ? sel : 0) * p.Mtot + hrow];
+// 1/rms of this launch's activation rows into inv_s[0 .. M-1]: wave w sums the
+// partials of rows w, w + nw, ... (lane-strided, then a fixed tree); every
+// block computes bit-identical values.  Call with the whole block.
+__device__ __forceinline__ void block_inv_rms(const GemvParams &p, float *inv_s) {
+    if (p.xmode != X_NORM) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    for (int m = wave; m < p.M; m += nw) {
+        const float *src = p.xss + (int64_t)x_row(p, p.m0 + m) * p.xnparts;
+        float s = 0.f;
+        for (int i = lane; i < p.xnparts; i += 64) s += src[i];
+        s = wave_sum(s);
+        if (lane == 0) inv_s[m] = 1.0f / sqrtf(s / (float)p.K + p.eps);
+    }
+    __syncthreads();
 }
 
 // 8 normalised activations of residual row hrow at k .. k+7, as float
@@ -188,43 +199,6 @@ __device__ __forceinline__ void epilogue(const GemvParams &p, int u, int r0, int
     default:
         break;
     }
-}
-
-// Called by every thread of the block after the block wrote its partials
-// (row-norm sums ss[sel][m][block] and / or arg-max part_val / part_idx).
-// The last block to arrive reduces them in a fixed order.
-__device__ __forceinline__ void last_block_reduce(const GemvParams &p) {
-    __shared__ bool is_last;
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) is_last = atomicAdd(p.counter, 1u) == gridDim.x - 1;
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    const int G = gridDim.x;
-    if (p.n_norm_sel > 0) {
-        for (int t = wave; t < p.n_norm_sel * p.M; t += nw) {
-            const int sel = t / p.M, gm = p.m0 + t % p.M;
-            const float *src = p.ss + ((int64_t)sel * p.Mtot + gm) * G;
-            float s = 0.f;
-            for (int b = lane; b < G; b += 64) s += src[b];
-            s = wave_sum(s);
-            if (lane == 0) p.inv_out[(int64_t)sel * p.Mtot + gm] = 1.0f / sqrtf(s / (float)p.d + p.eps);
-        }
-    }
-    if (p.epi == EPI_LOGITS && p.token_out) {
-        for (int m = wave; m < p.M; m += nw) {
-            const int gm = p.m0 + m;
-            float v = -INFINITY;
-            int i = 0x7FFFFFFF;
-            for (int b = lane; b < G; b += 64)
-                argmax_merge(v, i, p.part_val[(int64_t)gm * G + b], p.part_idx[(int64_t)gm * G + b]);
-            wave_argmax(v, i);
-            if (lane == 0) p.token_out[(int64_t)gm * p.token_stride] = i;
-        }
-    }
-    if (threadIdx.x == 0) *p.counter = 0u;   // ready for the next launch
 }
 
 }  // namespace spec

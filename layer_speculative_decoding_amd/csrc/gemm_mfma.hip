@@ -83,6 +83,8 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemvParams p, int KS) {
     float ss[kMaxSel];
 #pragma unroll
     for (int s = 0; s < kMaxSel; ++s) ss[s] = 0.f;
+    __shared__ float inv_s[MT * 16];
+    block_inv_rms(p, inv_s);
 
     for (int u = blockIdx.x; u < p.n_units; u += gridDim.x) {
         const int bb = u / bph;
@@ -107,7 +109,7 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemvParams p, int KS) {
             inv[t] = 0.f;
             if (xok[t] && p.xmode == X_NORM) {
                 hrow[t] = x_row(p, p.m0 + t * 16 + li);
-                inv[t] = x_inv(p, sel, hrow[t]);
+                inv[t] = inv_s[t * 16 + li];
             }
         }
         const int kl = 16 * lg;   // this lane group's offset inside a chunk
@@ -195,10 +197,9 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemvParams p, int KS) {
         for (int s = 0; s < p.n_norm_sel; ++s) {
             float t = sss[s][e][0];
             for (int j = 1; j < 16; ++j) t += sss[s][e][j];
-            p.ss[((int64_t)s * p.Mtot + p.m0 + e) * gridDim.x + blockIdx.x] = t;
+            p.ss[(int64_t)s * p.ss_sel_stride + (int64_t)(p.m0 + e) * gridDim.x + blockIdx.x] = t;
         }
     }
-    last_block_reduce(p);
 }
 
 }  // namespace

@@ -49,6 +49,8 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p) {
     float ss[kMaxSel];
 #pragma unroll
     for (int s = 0; s < kMaxSel; ++s) ss[s] = 0.f;
+    __shared__ float inv_s[kMaxRows];
+    block_inv_rms(p, inv_s);
 
     for (int u = blockIdx.x * kWaves + wave; u < p.n_units; u += gridDim.x * kWaves) {
         const int blk = u / half;
@@ -67,7 +69,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p) {
             inv[m] = 0.f;
             if (p.xmode == X_NORM && m < p.M) {
                 hrow[m] = x_row(p, p.m0 + m);
-                inv[m] = x_inv(p, sel, hrow[m]);
+                inv[m] = inv_s[m];
             }
         }
         float a0[MR], a1[MR];
@@ -156,10 +158,9 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p) {
         for (int s = 0; s < p.n_norm_sel; ++s) {
             float t = sss[0][s][m];
             for (int w = 1; w < kWaves; ++w) t += sss[w][s][m];
-            p.ss[((int64_t)s * p.Mtot + p.m0 + m) * gridDim.x + blockIdx.x] = t;
+            p.ss[(int64_t)s * p.ss_sel_stride + (int64_t)(p.m0 + m) * gridDim.x + blockIdx.x] = t;
         }
     }
-    last_block_reduce(p);
 }
 
 template <typename T, bool kLogits>
@@ -177,6 +178,24 @@ hipError_t launch_t(const GemvParams &p, int grid, hipStream_t s) {
     return p.epi == EPI_LOGITS ? launch_tl<T, true>(p, grid, s) : launch_tl<T, false>(p, grid, s);
 }
 
+// ------------------------------------------------------------------ sampling
+__global__ __launch_bounds__(256) void k_sample_reduce(const float *pv, const int32_t *pi, int n, int32_t *out,
+                                                       int stride) {
+    __shared__ float sv[kWaves];
+    __shared__ int si[kWaves];
+    const int m = blockIdx.x;
+    float v = -INFINITY;
+    int i = 0x7FFFFFFF;
+    for (int j = threadIdx.x; j < n; j += blockDim.x) argmax_merge(v, i, pv[(int64_t)m * n + j], pi[(int64_t)m * n + j]);
+    wave_argmax(v, i);
+    if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = v; si[threadIdx.x >> 6] = i; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < kWaves; ++w) argmax_merge(sv[0], si[0], sv[w], si[w]);
+        out[(int64_t)m * stride] = si[0];
+    }
+}
+
 // ------------------------------------------------------------------ embed
 template <typename T>
 __global__ __launch_bounds__(256) void k_embed(EmbedParams p) {
@@ -184,8 +203,6 @@ __global__ __launch_bounds__(256) void k_embed(EmbedParams p) {
     const int m = blockIdx.x;
     const int mseq = p.rows.mseq;
     const int b = m / mseq, i = m - b * mseq;
-    if (m == 0)
-        for (int c = threadIdx.x; c < p.n_counters; c += blockDim.x) p.counters[c] = 0u;
     int tok = p.tokens[(int64_t)b * p.tok_ld + (int64_t)i * p.tok_step];
     tok = tok < 0 ? 0 : (tok >= p.vocab ? p.vocab - 1 : tok);
     const T *e = reinterpret_cast<const T *>(p.E) + (int64_t)tok * p.d;
@@ -213,10 +230,7 @@ __global__ __launch_bounds__(256) void k_embed(EmbedParams p) {
         p.rope_cs[(int64_t)m * half + j] = make_float2(cs, sn);
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        const float tot = red[0] + red[1] + red[2] + red[3];
-        p.inv[m] = 1.0f / sqrtf(tot / (float)p.d + p.eps);
-    }
+    if (threadIdx.x == 0) p.ss[m] = red[0] + red[1] + red[2] + red[3];
 }
 
 }  // namespace
@@ -230,6 +244,12 @@ int gemv_grid(int n_units) {
 
 hipError_t launch_gemv(int dtype, const GemvParams &p, int grid, hipStream_t s) {
     return dtype ? launch_t<uint16_t>(p, grid, s) : launch_t<float>(p, grid, s);
+}
+
+hipError_t launch_sample_reduce(const float *pv, const int32_t *pi, int n, int M, int32_t *out, int stride,
+                                hipStream_t s) {
+    hipLaunchKernelGGL(k_sample_reduce, dim3(M), dim3(256), 0, s, pv, pi, n, out, stride);
+    return hipGetLastError();
 }
 
 hipError_t launch_embed(int dtype, const EmbedParams &p, int Mtot, hipStream_t s) {

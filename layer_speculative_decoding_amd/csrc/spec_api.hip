@@ -42,8 +42,8 @@ inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace layout for R activation rows and sets of at most G layers.
 struct Carve {
-    size_t h, h0, abuf, q, o, act, pacc, pml, pval, pidx, ss, inv, rope, ctr, total;
-    int n_counters;
+    size_t h, h0, abuf, q, o, act, pacc, pml, pval, pidx, ss, rope, total;
+    int64_t ss_sel_stride;   // floats per set member in ss
 };
 
 constexpr int kPartialsMax = 2048;   // largest grid of a partial-sum producer
@@ -67,11 +67,9 @@ Carve carve(const spec_model *m, int batch, int max_m, int G) {
     c.pml = take((size_t)attention_split_max() * G * prow * hq * 2 * 4);
     c.pval = take((size_t)batch * kPartialsMax * 4);
     c.pidx = take((size_t)batch * kPartialsMax * 4);
+    c.ss_sel_stride = (int64_t)R * kPartialsMax;
     c.ss = take(nsel * R * kPartialsMax * 4);
-    c.inv = take(nsel * R * 4);
     c.rope = take(R * (hd / 2) * 8);
-    c.n_counters = 1 + G * m->d.n_kv_heads * batch;
-    c.ctr = take((size_t)c.n_counters * 4);
     c.total = off;
     return c;
 }
@@ -82,7 +80,8 @@ const void *layer_ptr(const void *base, size_t layer, size_t elems_per_layer, in
     return reinterpret_cast<const char *>(base) + layer * elems_per_layer * xs;
 }
 
-// Everything a forward over R = batch * mseq rows needs.
+// Everything a forward over R = batch * mseq rows needs, plus the number of
+// sum-of-squares partials each set member's residual row currently has.
 struct Fwd {
     const spec_model *m;
     const spec_kv *kv;
@@ -91,6 +90,7 @@ struct Fwd {
     void *ws;
     Carve c;
     hipStream_t s;
+    int nparts[kMaxSel];
 };
 
 // Activation-row count from which bf16 products use the matrix-core kernel
@@ -103,13 +103,14 @@ int mfma_min_rows() {
     return v;
 }
 
-// Weight-streaming product over the call's Mtot activation rows (p.Mtot),
-// chunked by the kernel's row limit.
-hipError_t product(const Fwd &f, GemvParams p) {
+// Weight-streaming product over the call's p.Mtot activation rows, chunked by
+// the kernel's row limit.  *grid_out: the grid of the launches (= partials
+// per row of its sum-of-squares or sampling output).
+hipError_t product(const Fwd &f, GemvParams p, int *grid_out = nullptr) {
     const spec_model *m = f.m;
     const int Mtot = p.Mtot;
-    p.counter = at<unsigned>(f.ws, f.c.ctr);
     p.ss = at<float>(f.ws, f.c.ss);
+    p.ss_sel_stride = f.c.ss_sel_stride;
     p.part_val = at<float>(f.ws, f.c.pval);
     p.part_idx = at<int32_t>(f.ws, f.c.pidx);
     GemvParams q = p;
@@ -121,6 +122,7 @@ hipError_t product(const Fwd &f, GemvParams p) {
         q.n_units = p.n_units / 16;           // row pairs -> pairs of 16-row blocks
         const int grid = gemm_mfma_grid(q.n_units);
         const int ks = gemm_mfma_splits(q.n_units, p.K);
+        if (grid_out) *grid_out = grid;
         const int mr = gemm_mfma_max_rows();
         for (int m0 = 0; m0 < Mtot; m0 += mr) {
             q.m0 = m0;
@@ -132,6 +134,7 @@ hipError_t product(const Fwd &f, GemvParams p) {
     }
     const int mr = gemv_max_rows();
     const int grid = gemv_grid(p.n_units);
+    if (grid_out) *grid_out = grid;
     for (int m0 = 0; m0 < Mtot; m0 += mr) {
         p.m0 = m0;
         p.M = (Mtot - m0) < mr ? (Mtot - m0) : mr;
@@ -141,21 +144,21 @@ hipError_t product(const Fwd &f, GemvParams p) {
     return hipSuccess;
 }
 
-// Embedding, 1/rms of every row, RoPE table, counter reset.
-hipError_t run_embed(const Fwd &f, const int32_t *tokens, int64_t tok_ld, int tok_step) {
+// Embedding, the sum of squares of every row (one partial), RoPE table.
+hipError_t run_embed(Fwd &f, const int32_t *tokens, int64_t tok_ld, int tok_step) {
     const spec_model *m = f.m;
     EmbedParams e{};
     e.E = m->w.embed; e.vocab = m->d.vocab; e.d = m->d.d_model;
     e.tokens = tokens; e.tok_ld = tok_ld; e.tok_step = tok_step; e.rows = f.rows;
-    e.h = at<float>(f.ws, f.c.h); e.inv = at<float>(f.ws, f.c.inv); e.eps = m->d.rms_eps;
+    e.h = at<float>(f.ws, f.c.h); e.ss = at<float>(f.ws, f.c.ss);
     e.rope_cs = at<float2>(f.ws, f.c.rope); e.hd = m->d.head_dim; e.rope_theta = m->d.rope_theta;
-    e.counters = at<unsigned>(f.ws, f.c.ctr); e.n_counters = f.c.n_counters;
+    f.nparts[0] = 1;
     return launch_embed(m->d.dtype, e, f.batch * f.mseq, f.s);
 }
 
 // One stage: attention of the set [l0, l0 + n) on the stage input h0, then
 // the set's MLPs.  A stage of one layer is the ordinary decoder layer.
-hipError_t run_stage(const Fwd &f, int l0, int n, int mlp_mode) {
+hipError_t run_stage(Fwd &f, int l0, int n, int mlp_mode) {
     const spec_model *m = f.m;
     const spec_model_desc &d = m->d;
     const int R = f.batch * f.mseq;
@@ -164,11 +167,12 @@ hipError_t run_stage(const Fwd &f, int l0, int n, int mlp_mode) {
     float *h = at<float>(f.ws, f.c.h);
     float *h0 = at<float>(f.ws, f.c.h0);
     float *abuf = at<float>(f.ws, f.c.abuf);
-    float *inv = at<float>(f.ws, f.c.inv);
+    float *ss = at<float>(f.ws, f.c.ss);
     float *q = at<float>(f.ws, f.c.q);
     void *o = at<char>(f.ws, f.c.o);
     void *act = at<char>(f.ws, f.c.act);
     hipError_t e;
+    int grid = 0;
 
     // 1. grouped QKV over the N layers' concatenated rows: operand = one RMS
     //    of h0 with each layer's gain; epilogue = RoPE + KV append
@@ -176,7 +180,8 @@ hipError_t run_stage(const Fwd &f, int l0, int n, int mlp_mode) {
     gp.Mtot = R; gp.d = dm; gp.eps = d.rms_eps;
     gp.W = layer_ptr(m->w.wqkv, l0, (size_t)D * dm, xs);
     gp.K = dm; gp.n_units = n * D / 2; gp.pair_block = d.head_dim; gp.rows_per_sel = D;
-    gp.xmode = X_NORM; gp.xh = h; gp.xgain = m->w.attn_norm + (size_t)l0 * dm; gp.xgain_stride = dm; gp.xinv = inv;
+    gp.xmode = X_NORM; gp.xh = h; gp.xgain = m->w.attn_norm + (size_t)l0 * dm; gp.xgain_stride = dm;
+    gp.xss = ss; gp.xnparts = f.nparts[0];
     gp.bias = m->w.bqkv ? m->w.bqkv + (size_t)l0 * D : nullptr;
     gp.epi = EPI_QKV_ROPE;
     gp.q_out = q; gp.q_sel_stride = (int64_t)R * qd;
@@ -194,8 +199,7 @@ hipError_t run_stage(const Fwd &f, int l0, int n, int mlp_mode) {
     ap.rows = f.rows; ap.max_pos = f.max_pos;
     ap.splits = attention_splits(n, f.batch, d.n_q_heads, d.n_kv_heads, f.mseq, f.max_pos);
     ap.o = o; ap.o_sel_stride = (int64_t)R * qd;
-    ap.part_acc = at<float>(f.ws, f.c.pacc); ap.part_ml = at<float>(f.ws, f.c.pml);
-    ap.counters = at<unsigned>(f.ws, f.c.ctr) + 1; ap.Mtot = R;
+    ap.part_acc = at<float>(f.ws, f.c.pacc); ap.part_ml = at<float>(f.ws, f.c.pml); ap.Mtot = R;
     if ((e = launch_attention(d.dtype, ap, f.s)) != hipSuccess) return e;
 
     // 3. grouped O projection: a_0 goes into the residual (sequential MLPs),
@@ -207,19 +211,22 @@ hipError_t run_stage(const Fwd &f, int l0, int n, int mlp_mode) {
     gp.xmode = X_PLAIN; gp.X = o; gp.x_sel_stride = (int64_t)R * qd;
     gp.epi = EPI_ATTN_OUT; gp.h = h; gp.h0 = h0; gp.par_mlp = par ? 1 : 0;
     gp.out = abuf; gp.out_sel_stride = (int64_t)R * dm;
-    gp.n_norm_sel = par ? n : 1; gp.inv_out = inv;
-    if ((e = product(f, gp)) != hipSuccess) return e;
+    gp.n_norm_sel = par ? n : 1;
+    if ((e = product(f, gp, &grid)) != hipSuccess) return e;
+    for (int i = 0; i < gp.n_norm_sel; ++i) f.nparts[i] = grid;
 
     // 4. MLPs in set order
     for (int i = 0; i < n; ++i) {
         const int l = l0 + i;
+        const int si = par ? i : 0;
         gp = GemvParams{};
         gp.Mtot = R; gp.d = dm; gp.eps = d.rms_eps;
         gp.W = layer_ptr(m->w.w_gate_up, l, (size_t)2 * d.d_ffn * dm, xs);
         gp.K = dm; gp.n_units = d.d_ffn; gp.pair_block = 2 * d.d_ffn; gp.rows_per_sel = 2 * d.d_ffn;
         gp.xmode = X_NORM; gp.xgain = m->w.ffn_norm + (size_t)l * dm;
-        if (par) { gp.xh = h0; gp.xadd = abuf + (size_t)i * R * dm; gp.xinv = inv + (size_t)i * R; }
-        else { gp.xh = h; gp.xinv = inv; }
+        gp.xss = ss + (size_t)si * f.c.ss_sel_stride; gp.xnparts = f.nparts[si];
+        if (par) { gp.xh = h0; gp.xadd = abuf + (size_t)i * R * dm; }
+        else gp.xh = h;
         gp.epi = EPI_SILU_MUL; gp.act = act; gp.act_ld = d.d_ffn;
         if ((e = product(f, gp)) != hipSuccess) return e;
 
@@ -232,16 +239,17 @@ hipError_t run_stage(const Fwd &f, int l0, int n, int mlp_mode) {
         // sequential: h += m_i + a_{i+1} (the next member's attention output);
         // parallel: h += a_i + m_i
         gp.add2 = par ? abuf + (size_t)i * R * dm : (i + 1 < n ? abuf + (size_t)(i + 1) * R * dm : nullptr);
-        gp.n_norm_sel = 1; gp.inv_out = inv;
-        if ((e = product(f, gp)) != hipSuccess) return e;
+        gp.n_norm_sel = 1;
+        if ((e = product(f, gp, &grid)) != hipSuccess) return e;
+        f.nparts[0] = grid;
     }
     return hipSuccess;
 }
 
 // Final RMSNorm (folded into the operand; optionally of the last valid row of
-// each sequence) + lm head; with token_out, the sampled / arg-max token of each
-// sampling row is reduced by the last block of the lm-head launch.
-hipError_t run_head(const Fwd &f, bool last_only, const int32_t *ntok, float *logits, int64_t logits_ld,
+// each sequence) + lm head; with token_out, per-block arg-max partials of the
+// sampling scores are reduced by a small kernel.
+hipError_t run_head(Fwd &f, bool last_only, const int32_t *ntok, float *logits, int64_t logits_ld,
                     float inv_temp, uint64_t seed, const int32_t *samp_pos, const int32_t *samp_ntok,
                     int samp_nconst, int32_t *token_out, int token_stride) {
     const spec_model *m = f.m;
@@ -252,13 +260,17 @@ hipError_t run_head(const Fwd &f, bool last_only, const int32_t *ntok, float *lo
     gp.Mtot = last_only ? f.batch : R; gp.d = dm; gp.eps = m->d.rms_eps;
     gp.W = m->w.lm_head; gp.K = dm; gp.n_units = m->d.vocab / 2; gp.pair_block = 2; gp.rows_per_sel = m->d.vocab;
     gp.xmode = X_NORM; gp.xh = at<float>(f.ws, f.c.h); gp.xgain = m->w.final_norm; gp.xgain_stride = 0;
-    gp.xinv = at<float>(f.ws, f.c.inv);
+    gp.xss = at<float>(f.ws, f.c.ss); gp.xnparts = f.nparts[0];
     gp.xgather_mseq = last_only ? f.mseq : 0; gp.xgather_ntok = ntok;
     gp.epi = token_out ? EPI_LOGITS : EPI_STORE;
     gp.out = logits; gp.out_ld = logits_ld; gp.out_sel_stride = 0;
     gp.inv_temp = inv_temp; gp.seed = seed; gp.samp_pos = samp_pos; gp.samp_ntok = samp_ntok;
-    gp.samp_nconst = samp_nconst; gp.token_out = token_out; gp.token_stride = token_stride;
-    return product(f, gp);
+    gp.samp_nconst = samp_nconst;
+    int grid = 0;
+    hipError_t e = product(f, gp, &grid);
+    if (e != hipSuccess || !token_out) return e;
+    return launch_sample_reduce(at<float>(f.ws, f.c.pval), at<int32_t>(f.ws, f.c.pidx), grid, gp.Mtot, token_out,
+                                token_stride, f.s);
 }
 
 spec_status check_model(const spec_model *m, const spec_kv *kv, int batch) {
@@ -385,7 +397,7 @@ spec_status spec_draft_group_step(const spec_model *draft, const spec_kv *kv, co
     if ((st = check_ws(draft, batch, 1, G, workspace, ws_bytes))) return st;
 
     Fwd f{draft, kv, batch, 1, max_pos, RowMap{positions, nullptr, 1, kv->capacity}, workspace,
-          carve(draft, batch, 1, G), (hipStream_t)stream};
+          carve(draft, batch, 1, G), (hipStream_t)stream, {0}};
     hipError_t e = run_embed(f, tokens, tokens_stride, 0);
     if (e != hipSuccess) return hip_fail(e, "embed");
     for (int s = 0; s < n_stages; ++s) {
@@ -403,7 +415,7 @@ static spec_status precise_forward(const spec_model *m, const spec_kv *kv, int b
                                    const int32_t *start_pos, const int32_t *n_tokens, int mseq, int max_pos,
                                    void *ws, hipStream_t s, Fwd &f) {
     f = Fwd{m, kv, batch, mseq, max_pos, RowMap{start_pos, n_tokens, mseq, kv->capacity}, ws,
-            carve(m, batch, mseq, 1), s};
+            carve(m, batch, mseq, 1), s, {0}};
     hipError_t e = run_embed(f, tokens, mseq, 1);
     if (e != hipSuccess) return hip_fail(e, "embed");
     for (int l = 0; l < m->d.n_layers; ++l) {

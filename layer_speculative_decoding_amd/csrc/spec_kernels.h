@@ -22,7 +22,7 @@ enum GemvEpi : int {
     EPI_QKV_ROPE = 1,   // RoPE on q/k pairs; q -> q_out, k/v -> KV cache
     EPI_SILU_MUL = 2,   // act[m * act_ld + unit] = round(silu(gate) * up)
     EPI_RESID_ADD = 3,  // h[m][row] += y (+ add2[m][row]); row-norm partials of h
-    EPI_LOGITS = 4,     // store (if out) + Gumbel / greedy arg-max, last block reduces
+    EPI_LOGITS = 4,     // store (if out) + per-block Gumbel / greedy arg-max partials
     EPI_ATTN_OUT = 5,   // sequential MLPs: sel 0 -> h += y (+ partials), sel > 0 -> abuf
                         // parallel MLPs: every sel -> abuf, partials of h0 + y; sel 0
                         // also copies h to h0
@@ -31,7 +31,7 @@ enum GemvEpi : int {
 // How a product reads its activations.
 enum XMode : int {
     X_PLAIN = 0,   // X[sel * x_sel_stride + m * K + k] (activation dtype)
-    X_NORM = 1,    // round(gain_sel[k] * (xh[hrow][k] + xadd[sel][hrow][k]) * inv[isel][hrow])
+    X_NORM = 1,    // round(gain_sel[k] * (xh[hrow][k] + xadd[sel][hrow][k]) / rms(hrow))
 };
 
 struct GemvParams {
@@ -54,8 +54,8 @@ struct GemvParams {
     int64_t xadd_sel_stride;
     const float *xgain;   // X_NORM: gain of set member sel at xgain + sel * xgain_stride
     int64_t xgain_stride;
-    const float *xinv;    // X_NORM: 1/rms at xinv[isel * Mtot + hrow]
-    int xinv_per_sel;     // isel = xinv_per_sel ? sel : 0
+    const float *xss;     // X_NORM: sum-of-squares partials of residual row hrow at
+    int xnparts;          //   xss[hrow * xnparts + 0 .. xnparts-1] (summed in order)
     int xgather_mseq;     // > 0: activation row m reads residual row
     const int32_t *xgather_ntok;   //   m * mseq + ntok[m] - 1 (last valid row)
     const float *bias;    // [rows] or NULL
@@ -69,11 +69,10 @@ struct GemvParams {
     float *h0;            // [Mtot][d] (parallel MLPs)
     const float *add2;    // RESID_ADD: nullable extra addend [Mtot][d]
     int par_mlp;          // ATTN_OUT: parallel-MLP reading
-    // row-norm partials of the updated residual: ss[sel][m][block]; the last
-    // block to finish writes inv[sel][m] = 1 / sqrt(sum / d + eps)
+    // row-norm partials of the updated residual: ss[sel * ss_sel_stride +
+    // m * gridDim.x + block]; consumers sum a row's partials in block order
     float *ss;
-    float *inv_out;
-    unsigned *counter;
+    int64_t ss_sel_stride;
     int n_norm_sel;       // 0: no partials; else number of sels with partials
     int d;
     float eps;
@@ -93,8 +92,6 @@ struct GemvParams {
     int samp_nconst;
     float *part_val;       // [Mtot][gridDim.x]
     int32_t *part_idx;
-    int32_t *token_out;    // last block writes the arg-max of row m here
-    int token_stride;
 };
 
 // dtype: 0 float32, 1 bfloat16 (weights and activation buffers share it).
@@ -110,8 +107,8 @@ int gemm_mfma_max_rows();
 int gemm_mfma_grid(int n_units);
 int gemm_mfma_splits(int n_units, int K);
 
-// Embedding of every row (h = E[token]), its 1/rms, the RoPE (cos, sin) of
-// its position, and zeroing of the call's completion counters.
+// Embedding of every row (h = E[token]), its sum of squares (one partial),
+// and the RoPE (cos, sin) of its position.
 struct EmbedParams {
     const void *E;
     int vocab, d;
@@ -120,19 +117,15 @@ struct EmbedParams {
     int tok_step;
     RowMap rows;
     float *h;
-    float *inv;            // [Mtot]
-    float eps;
+    float *ss;             // [Mtot]
     float2 *rope_cs;       // [Mtot][hd/2]
     int hd;
     float rope_theta;
-    unsigned *counters;
-    int n_counters;
 };
 hipError_t launch_embed(int dtype, const EmbedParams &p, int Mtot, hipStream_t s);
 
 // Grouped causal attention over n_group consecutive layers.  With several
-// key splits the last split block of each (layer, kv head, sequence) merges
-// the partials.
+// key splits a second small kernel merges the split partials.
 struct AttnParams {
     const float *q;        // [g][Mtot][hq][hd]
     int64_t q_sel_stride;
@@ -145,12 +138,15 @@ struct AttnParams {
     int64_t o_sel_stride;
     float *part_acc;       // [splits][g][Mtot][hq][hd]
     float *part_ml;        // [splits][g][Mtot][hq][2]
-    unsigned *counters;    // [g][hkv][batch]
     int Mtot;
 };
 hipError_t launch_attention(int dtype, const AttnParams &p, hipStream_t s);
 int attention_splits(int n_group, int batch, int hq, int hkv, int mseq, int max_pos);
 int attention_split_max();
+
+// Arg-max reduction of the lm-head sampling partials -> tokens.
+hipError_t launch_sample_reduce(const float *part_val, const int32_t *part_idx, int n_parts, int M,
+                                int32_t *token_out, int token_stride, hipStream_t s);
 
 // Accept / resample.
 struct AcceptParams {
