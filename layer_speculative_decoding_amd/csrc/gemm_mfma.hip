@@ -60,15 +60,19 @@ __device__ __forceinline__ void x_tile(const GemvParams &p, const uint16_t *xrow
 }
 
 // MT: number of 16-row activation tiles (1: M <= 16, 2: M <= 32)
-template <int MT, bool kLogits>
+// kSingle: a unit is one 16-row block (rows r0 .. r0+15, epilogue pairs
+// (r0 + j, r0 + 8 + j)) and all 2 KS waves split K; otherwise a unit is a
+// pair of 16-row blocks and KS wave pairs split K.
+template <int MT, bool kLogits, bool kSingle>
 __global__ __launch_bounds__(512) void k_gemm_mfma(GemvParams p, int KS) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;     // 0 .. 2*KS-1
-    const int blk = wave & 1;              // which block of the pair
-    const int part = wave >> 1;            // K split index
+    const int blk = kSingle ? 0 : (wave & 1);      // which block of the pair
+    const int part = kSingle ? wave : (wave >> 1); // K split index
+    const int nparts_k = kSingle ? 2 * KS : KS;
     const int K = p.K;
     const int nchunk = K >> 6;             // 64-element chunks
-    const int per = (nchunk + KS - 1) / KS;
+    const int per = (nchunk + nparts_k - 1) / nparts_k;
     const int c0 = part * per;
     const int c1 = min(nchunk, c0 + per);
     const int half = p.pair_block >> 1;
@@ -87,10 +91,16 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemvParams p, int KS) {
     block_inv_rms(p, inv_s);
 
     for (int u = blockIdx.x; u < p.n_units; u += gridDim.x) {
-        const int bb = u / bph;
-        const int jb = u - bb * bph;
-        const int r0 = bb * p.pair_block + jb * 16;
-        const int r1 = r0 + half;
+        int r0, r1;
+        if (kSingle) {
+            r0 = u * 16;
+            r1 = r0 + 8;
+        } else {
+            const int bb = u / bph;
+            const int jb = u - bb * bph;
+            r0 = bb * p.pair_block + jb * 16;
+            r1 = r0 + half;
+        }
         const int rb = blk ? r1 : r0;
         const int sel = r0 / p.rows_per_sel;
         const uint16_t *w = reinterpret_cast<const uint16_t *>(p.W) + (int64_t)(rb + li) * K + 16 * lg;
@@ -154,8 +164,8 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemvParams p, int KS) {
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
                 f32x4 s = red[blk][t][lane];
-                for (int q = 1; q < KS; ++q) {
-                    const f32x4 o = red[2 * q + blk][t][lane];
+                for (int q = 1; q < nparts_k; ++q) {
+                    const f32x4 o = red[kSingle ? q : 2 * q + blk][t][lane];
                     s[0] += o[0]; s[1] += o[1]; s[2] += o[2]; s[3] += o[3];
                 }
 #pragma unroll
@@ -163,15 +173,19 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemvParams p, int KS) {
             }
         }
         __syncthreads();
-        for (int e = threadIdx.x; e < p.M * 16; e += blockDim.x) {
-            const int m = e >> 4, j = e & 15;
-            epilogue<uint16_t, kLogits>(p, r0 + j, r0 + j, r1 + j, sel, m, tile[0][m][j], tile[1][m][j], best_v, best_i, ss);
+        constexpr int EPR = kSingle ? 8 : 16;   // epilogue elements per activation row
+        for (int e = threadIdx.x; e < p.M * EPR; e += blockDim.x) {
+            const int m = e / EPR, j = e % EPR;
+            const float y0 = tile[0][m][j];
+            const float y1 = kSingle ? tile[0][m][j + 8] : tile[1][m][j];
+            epilogue<uint16_t, kLogits>(p, r0 + j, r0 + j, r1 + j, sel, m, y0, y1, best_v, best_i, ss);
         }
         __syncthreads();
     }
 
-    // block partials: thread e < 16 M always handled activation row e / 16
+    // block partials: thread e < EPR M always handled activation row e / EPR
     // (the launch guarantees blockDim >= 16 M)
+    constexpr int EPR = kSingle ? 8 : 16;
     const bool norm = p.n_norm_sel > 0;
     const bool logits = p.epi == EPI_LOGITS;
     if (!norm && !logits) return;
@@ -179,24 +193,24 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemvParams p, int KS) {
     __shared__ int sbi[MT * 16][16];
     __shared__ float sss[kMaxSel][MT * 16][16];
     const int e = threadIdx.x;
-    if (e < p.M * 16) {
-        sbv[e >> 4][e & 15] = best_v;
-        sbi[e >> 4][e & 15] = best_i;
+    if (e < p.M * EPR) {
+        sbv[e / EPR][e % EPR] = best_v;
+        sbi[e / EPR][e % EPR] = best_i;
 #pragma unroll
-        for (int s = 0; s < kMaxSel; ++s) sss[s][e >> 4][e & 15] = ss[s];
+        for (int s = 0; s < kMaxSel; ++s) sss[s][e / EPR][e % EPR] = ss[s];
     }
     __syncthreads();
     if (e < p.M) {
         if (logits) {
             float v = sbv[e][0];
             int i = sbi[e][0];
-            for (int j = 1; j < 16; ++j) argmax_merge(v, i, sbv[e][j], sbi[e][j]);
+            for (int j = 1; j < EPR; ++j) argmax_merge(v, i, sbv[e][j], sbi[e][j]);
             p.part_val[(int64_t)(p.m0 + e) * gridDim.x + blockIdx.x] = v;
             p.part_idx[(int64_t)(p.m0 + e) * gridDim.x + blockIdx.x] = i;
         }
         for (int s = 0; s < p.n_norm_sel; ++s) {
             float t = sss[s][e][0];
-            for (int j = 1; j < 16; ++j) t += sss[s][e][j];
+            for (int j = 1; j < EPR; ++j) t += sss[s][e][j];
             p.ss[(int64_t)s * p.ss_sel_stride + (int64_t)(p.m0 + e) * gridDim.x + blockIdx.x] = t;
         }
     }
@@ -210,26 +224,33 @@ int gemm_mfma_grid(int n_units) { return n_units < kMaxGridM ? (n_units < 1 ? 1 
 
 // K splits so that a launch has about 8K waves in flight, at least two
 // 64-element chunks per wave.
-int gemm_mfma_splits(int n_units, int K) {
+int gemm_mfma_splits(int n_units, int K, bool single) {
+    const int per_ks = single ? 2 : 1;     // K parts per unit and KS step
     int ks = 1;
-    while (ks < kMaxKS && (int64_t)n_units * 2 * ks < 8192 && (K >> 6) >= 4 * ks) ks *= 2;
+    while (ks < kMaxKS && (int64_t)n_units * 2 * ks < 8192 && (K >> 6) >= 4 * ks * per_ks) ks *= 2;
     return ks;
 }
 
 bool gemm_mfma_supported(const GemvParams &p) {
-    return (p.K % 64) == 0 && (p.pair_block % 32) == 0 && p.M >= 1 && p.M <= 32;
+    return (p.K % 64) == 0 && (p.pair_block == 2 || (p.pair_block % 32) == 0) && p.M >= 1 && p.M <= 32;
 }
 
-hipError_t launch_gemm_mfma(const GemvParams &p, int grid, int ks, hipStream_t s) {
+template <int MT, bool kSingle>
+void launch_mt(const GemvParams &p, dim3 g, dim3 b, int ks, hipStream_t s) {
+    if (p.epi == EPI_LOGITS) hipLaunchKernelGGL((k_gemm_mfma<MT, true, kSingle>), g, b, 0, s, p, ks);
+    else hipLaunchKernelGGL((k_gemm_mfma<MT, false, kSingle>), g, b, 0, s, p, ks);
+}
+
+// single: units are single 16-row blocks (adjacent-row products)
+hipError_t launch_gemm_mfma(const GemvParams &p, int grid, int ks, bool single, hipStream_t s) {
     while (128 * ks < 16 * p.M) ks *= 2;   // one epilogue element per thread
     dim3 g(grid), b(128 * ks);
-    const bool lg = p.epi == EPI_LOGITS;
     if (p.M <= 16) {
-        if (lg) hipLaunchKernelGGL((k_gemm_mfma<1, true>), g, b, 0, s, p, ks);
-        else hipLaunchKernelGGL((k_gemm_mfma<1, false>), g, b, 0, s, p, ks);
+        if (single) launch_mt<1, true>(p, g, b, ks, s);
+        else launch_mt<1, false>(p, g, b, ks, s);
     } else {
-        if (lg) hipLaunchKernelGGL((k_gemm_mfma<2, true>), g, b, 0, s, p, ks);
-        else hipLaunchKernelGGL((k_gemm_mfma<2, false>), g, b, 0, s, p, ks);
+        if (single) launch_mt<2, true>(p, g, b, ks, s);
+        else launch_mt<2, false>(p, g, b, ks, s);
     }
     return hipGetLastError();
 }

@@ -178,6 +178,30 @@ hipError_t launch_t(const GemvParams &p, int grid, hipStream_t s) {
     return p.epi == EPI_LOGITS ? launch_tl<T, true>(p, grid, s) : launch_tl<T, false>(p, grid, s);
 }
 
+// ------------------------------------------------------------------ norm
+// Normalised activations for the matrix-core products:
+// xn[sel][m][k] = round(gain_sel[k] * (xh[hrow][k] + xadd[sel][hrow][k]) / rms(hrow)),
+// rms from the row's sum-of-squares partials (summed in block order by every
+// wave, so all blocks agree bit for bit).  Grid (K / 2048, M, n_sel).
+template <typename T>
+__global__ __launch_bounds__(256) void k_norm_rows(GemvParams p, void *xn) {
+    const int m = blockIdx.y, sel = blockIdx.z;
+    const int lane = threadIdx.x & 63;
+    const int hrow = x_row(p, p.m0 + m);
+    const float *src = p.xss + (int64_t)hrow * p.xnparts;
+    float s = 0.f;
+    for (int i = lane; i < p.xnparts; i += 64) s += src[i];
+    s = wave_sum(s);
+    const float inv = 1.0f / sqrtf(s / (float)p.K + p.eps);
+    const int k = (blockIdx.x * 256 + threadIdx.x) * 8;
+    if (k >= p.K) return;
+    float f[8];
+    x_norm8(p, sel, hrow, k, inv, f);
+    T *o = reinterpret_cast<T *>(xn) + ((int64_t)sel * p.Mtot + p.m0 + m) * p.K + k;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = Store<T>::from_f32(f[e]);
+}
+
 // ------------------------------------------------------------------ sampling
 __global__ __launch_bounds__(256) void k_sample_reduce(const float *pv, const int32_t *pi, int n, int32_t *out,
                                                        int stride) {
@@ -244,6 +268,13 @@ int gemv_grid(int n_units) {
 
 hipError_t launch_gemv(int dtype, const GemvParams &p, int grid, hipStream_t s) {
     return dtype ? launch_t<uint16_t>(p, grid, s) : launch_t<float>(p, grid, s);
+}
+
+hipError_t launch_norm_rows(int dtype, const GemvParams &p, int n_sel, void *xn, hipStream_t s) {
+    dim3 grid((p.K + 2047) / 2048, p.M, n_sel);
+    if (dtype) hipLaunchKernelGGL(k_norm_rows<uint16_t>, grid, dim3(256), 0, s, p, xn);
+    else hipLaunchKernelGGL(k_norm_rows<float>, grid, dim3(256), 0, s, p, xn);
+    return hipGetLastError();
 }
 
 hipError_t launch_sample_reduce(const float *pv, const int32_t *pi, int n, int M, int32_t *out, int stride,

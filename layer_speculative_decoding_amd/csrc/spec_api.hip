@@ -42,7 +42,7 @@ inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace layout for R activation rows and sets of at most G layers.
 struct Carve {
-    size_t h, h0, abuf, q, o, act, pacc, pml, pval, pidx, ss, rope, total;
+    size_t h, h0, abuf, xn, q, o, act, pacc, pml, pval, pidx, ss, rope, total;
     int64_t ss_sel_stride;   // floats per set member in ss
 };
 
@@ -60,6 +60,7 @@ Carve carve(const spec_model *m, int batch, int max_m, int G) {
     c.h = take(R * d * 4);
     c.h0 = take(R * d * 4);
     c.abuf = take((size_t)G * R * d * 4);
+    c.xn = take((size_t)G * R * d * xs);
     c.q = take((size_t)G * R * hq * hd * 4);
     c.o = take((size_t)G * R * hq * hd * xs);
     c.act = take(R * (size_t)m->d.d_ffn * xs);
@@ -119,15 +120,30 @@ hipError_t product(const Fwd &f, GemvParams p, int *grid_out = nullptr) {
     const bool mfma = m->d.dtype == SPEC_BF16 && Mtot >= mfma_min_rows() && gemm_mfma_supported(q) &&
                       (p.n_units * 2) % 32 == 0;
     if (mfma) {
-        q.n_units = p.n_units / 16;           // row pairs -> pairs of 16-row blocks
+        const bool single = p.pair_block == 2;
+        q.n_units = single ? p.n_units / 8 : p.n_units / 16;   // row pairs -> 16-row units
         const int grid = gemm_mfma_grid(q.n_units);
-        const int ks = gemm_mfma_splits(q.n_units, p.K);
+        const int ks = gemm_mfma_splits(q.n_units, p.K, single);
         if (grid_out) *grid_out = grid;
         const int mr = gemm_mfma_max_rows();
         for (int m0 = 0; m0 < Mtot; m0 += mr) {
             q.m0 = m0;
             q.M = (Mtot - m0) < mr ? (Mtot - m0) : mr;
-            hipError_t e = launch_gemm_mfma(q, grid, ks, f.s);
+            if (p.xmode == X_NORM) {
+                // normalise once into xn, then stream the weights against it
+                const int n_sel = (p.n_units * 2) / p.rows_per_sel;
+                void *xn = at<char>(f.ws, f.c.xn);
+                hipError_t e = launch_norm_rows(m->d.dtype, q, n_sel, xn, f.s);
+                if (e != hipSuccess) return e;
+                GemvParams r = q;
+                r.xmode = X_PLAIN;
+                r.X = xn;   // rows (sel * Mtot + m0 + m); the kernel adds m0 * K
+                r.x_sel_stride = (int64_t)Mtot * p.K;
+                e = launch_gemm_mfma(r, grid, ks, single, f.s);
+                if (e != hipSuccess) return e;
+                continue;
+            }
+            hipError_t e = launch_gemm_mfma(q, grid, ks, single, f.s);
             if (e != hipSuccess) return e;
         }
         return hipSuccess;

@@ -101,11 +101,16 @@ int gemv_max_rows();
 int gemv_grid(int n_units);
 // MFMA skinny GEMM (bf16): units are pairs of 16-row blocks (n_units = rows /
 // 32), M <= 32 per launch, K a multiple of 64, pair_block a multiple of 32.
-hipError_t launch_gemm_mfma(const GemvParams &p, int grid, int ks, hipStream_t s);
+// single: units are single 16-row blocks whose epilogue pairs rows (r, r + 8)
+// (products whose rows need no partner); otherwise pairs of 16-row blocks.
+hipError_t launch_gemm_mfma(const GemvParams &p, int grid, int ks, bool single, hipStream_t s);
+// X_NORM operands written once as activation-dtype rows xn[sel][m][K] for
+// rows m0 .. m0 + M - 1 (the matrix-core products then read them plainly).
+hipError_t launch_norm_rows(int dtype, const GemvParams &p, int n_sel, void *xn, hipStream_t s);
 bool gemm_mfma_supported(const GemvParams &p);
 int gemm_mfma_max_rows();
 int gemm_mfma_grid(int n_units);
-int gemm_mfma_splits(int n_units, int K);
+int gemm_mfma_splits(int n_units, int K, bool single);
 
 // Embedding of every row (h = E[token]), its sum of squares (one partial),
 // and the RoPE (cos, sin) of its position.
