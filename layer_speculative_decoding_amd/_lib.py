@@ -23,7 +23,8 @@ STATUS = {0: "SPEC_OK", -1: "SPEC_ERR_INVALID_ARG", -2: "SPEC_ERR_SHAPE", -3: "S
 EXPORTS = ("spec_model_create", "spec_model_destroy", "spec_check_pair", "spec_default_group_plan",
            "spec_workspace_bytes", "spec_draft_group_step", "spec_calibrate_kv", "spec_verify_forward",
            "spec_accept_workspace_bytes", "spec_accept_resample", "spec_status_string", "spec_last_error",
-           "spec_version")
+           "spec_version", "spec_profile_enable", "spec_profile_reset", "spec_profile_collect",
+           "spec_profile_entry")
 
 
 class SpecError(RuntimeError):
@@ -75,6 +76,11 @@ def load() -> C.CDLL:
         "spec_status_string": (C.c_char_p, [i32]),
         "spec_last_error": (C.c_char_p, []),
         "spec_version": (C.c_char_p, []),
+        "spec_profile_enable": (i32, [i32]),
+        "spec_profile_reset": (None, []),
+        "spec_profile_collect": (i32, []),
+        "spec_profile_entry": (i32, [i32, C.c_char_p, i32, C.POINTER(C.c_int64), C.POINTER(C.c_double),
+                                     C.POINTER(C.c_double)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -134,3 +134,25 @@ def spec_accept_resample(batch: int, k: int, vocab: int, p_logits: torch.Tensor,
         batch, k, vocab, _ptr(p_logits), _ptr(q_logits), dptr, draft_stride, _ptr(round_pos),
         C.c_float(inv_temperature), C.c_uint64(seed), _ptr(n_accepted_out), _ptr(next_token_out),
         next_token_stride, _ptr(commit_out), _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def spec_profile_enable(on: bool):
+    check(load().spec_profile_enable(1 if on else 0))
+
+
+def spec_profile_reset():
+    load().spec_profile_reset()
+
+
+def spec_profile_collect() -> dict:
+    """{kernel instance: (launches, total_ms, total_bytes)} of the launches
+    recorded while profiling was enabled (synchronises their events)."""
+    lib = load()
+    n = lib.spec_profile_collect()
+    out = {}
+    buf = C.create_string_buffer(256)
+    for i in range(n):
+        la, ms, by = C.c_int64(), C.c_double(), C.c_double()
+        check(lib.spec_profile_entry(i, buf, 256, C.byref(la), C.byref(ms), C.byref(by)))
+        out[buf.value.decode()] = (la.value, ms.value, by.value)
+    return out

@@ -7,6 +7,8 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
+#include <string>
 #include <vector>
 
 #include "../../include/spec.h"
@@ -39,6 +41,69 @@ spec_status hip_fail(hipError_t e, const char *where) {
 }
 
 inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ------------------------------------------------------------ measurement
+// While enabled, each weight-streaming product launch is bracketed by two
+// HIP events on its stream and attributed to its kernel instance with the
+// bytes the launch must read (weights + activation rows).
+struct ProfPending {
+    std::string name;
+    double bytes;
+    hipEvent_t a, b;
+};
+struct ProfAgg {
+    std::string name;
+    int64_t launches;
+    double ms, bytes;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfPending> g_prof_pending;
+std::vector<ProfAgg> g_prof_agg;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+    if (!g_prof_pool.empty()) {
+        hipEvent_t e = g_prof_pool.back();
+        g_prof_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    (void)hipEventCreate(&e);
+    return e;
+}
+
+struct ProfScope {
+    bool on;
+    hipEvent_t a = nullptr;
+    hipStream_t s;
+    ProfScope(hipStream_t s_) : s(s_) {
+        std::lock_guard<std::mutex> g(g_prof_mu);
+        on = g_prof_on;
+        if (on) {
+            a = prof_event();
+            (void)hipEventRecord(a, s);
+        }
+    }
+    void done(const std::string &name, double bytes) {
+        if (!on) return;
+        std::lock_guard<std::mutex> g(g_prof_mu);
+        hipEvent_t b = prof_event();
+        (void)hipEventRecord(b, s);
+        g_prof_pending.push_back({name, bytes, a, b});
+    }
+};
+
+std::string gemv_name(int dtype, int M, bool logits) {
+    const int mr = M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : 8));
+    return std::string("k_gemv<") + (dtype ? "unsigned short" : "float") + ", " + std::to_string(mr) + ", " +
+           (logits ? "true" : "false") + ">";
+}
+
+std::string mfma_name(int M, bool logits, bool single) {
+    return std::string("k_gemm_mfma<") + (M <= 16 ? "1" : "2") + ", " + (logits ? "true" : "false") + ", " +
+           (single ? "true" : "false") + ">";
+}
 
 // Workspace layout for R activation rows and sets of at most G layers.
 struct Carve {
@@ -119,6 +184,7 @@ hipError_t product(const Fwd &f, GemvParams p, int *grid_out = nullptr) {
     q.M = Mtot < 32 ? Mtot : 32;
     const bool mfma = m->d.dtype == SPEC_BF16 && Mtot >= mfma_min_rows() && gemm_mfma_supported(q) &&
                       (p.n_units * 2) % 32 == 0;
+    const double wbytes = (double)p.n_units * 2 * p.K * m->xs;   // every weight row once
     if (mfma) {
         const bool single = p.pair_block == 2;
         q.n_units = single ? p.n_units / 8 : p.n_units / 16;   // row pairs -> 16-row units
@@ -139,11 +205,15 @@ hipError_t product(const Fwd &f, GemvParams p, int *grid_out = nullptr) {
                 r.xmode = X_PLAIN;
                 r.X = xn;   // rows (sel * Mtot + m0 + m); the kernel adds m0 * K
                 r.x_sel_stride = (int64_t)Mtot * p.K;
+                ProfScope ps(f.s);
                 e = launch_gemm_mfma(r, grid, ks, single, f.s);
+                ps.done(mfma_name(q.M, p.epi == EPI_LOGITS, single), wbytes + (double)q.M * p.K * m->xs * n_sel);
                 if (e != hipSuccess) return e;
                 continue;
             }
+            ProfScope ps(f.s);
             hipError_t e = launch_gemm_mfma(q, grid, ks, single, f.s);
+            ps.done(mfma_name(q.M, p.epi == EPI_LOGITS, single), wbytes + (double)q.M * p.K * m->xs);
             if (e != hipSuccess) return e;
         }
         return hipSuccess;
@@ -154,7 +224,10 @@ hipError_t product(const Fwd &f, GemvParams p, int *grid_out = nullptr) {
     for (int m0 = 0; m0 < Mtot; m0 += mr) {
         p.m0 = m0;
         p.M = (Mtot - m0) < mr ? (Mtot - m0) : mr;
+        ProfScope ps(f.s);
         hipError_t e = launch_gemv(m->d.dtype, p, grid, f.s);
+        ps.done(gemv_name(m->d.dtype, p.M, p.epi == EPI_LOGITS),
+                wbytes + (double)p.M * p.K * (p.xmode == X_NORM ? 4 : m->xs));
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -309,6 +382,57 @@ spec_status check_ws(const spec_model *m, int batch, int max_m, int G, void *ws,
 extern "C" {
 
 const char *spec_version(void) { return "0.1.0 gfx950"; }
+
+spec_status spec_profile_enable(int on) {
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    g_prof_on = on != 0;
+    return SPEC_OK;
+}
+
+void spec_profile_reset(void) {
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    for (auto &p : g_prof_pending) {
+        g_prof_pool.push_back(p.a);
+        g_prof_pool.push_back(p.b);
+    }
+    g_prof_pending.clear();
+    g_prof_agg.clear();
+}
+
+int spec_profile_collect(void) {
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    for (auto &p : g_prof_pending) {
+        float ms = 0.f;
+        if (hipEventSynchronize(p.b) == hipSuccess) (void)hipEventElapsedTime(&ms, p.a, p.b);
+        ProfAgg *agg = nullptr;
+        for (auto &x : g_prof_agg)
+            if (x.name == p.name) agg = &x;
+        if (!agg) {
+            g_prof_agg.push_back({p.name, 0, 0.0, 0.0});
+            agg = &g_prof_agg.back();
+        }
+        agg->launches += 1;
+        agg->ms += ms;
+        agg->bytes += p.bytes;
+        g_prof_pool.push_back(p.a);
+        g_prof_pool.push_back(p.b);
+    }
+    g_prof_pending.clear();
+    return (int)g_prof_agg.size();
+}
+
+spec_status spec_profile_entry(int i, char *name, int name_cap, int64_t *launches, double *total_ms,
+                               double *total_bytes) {
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    if (i < 0 || i >= (int)g_prof_agg.size() || !name || name_cap < 1)
+        return fail(SPEC_ERR_INVALID_ARG, "profile entry %d out of range", i);
+    const ProfAgg &a = g_prof_agg[i];
+    snprintf(name, (size_t)name_cap, "%s", a.name.c_str());
+    if (launches) *launches = a.launches;
+    if (total_ms) *total_ms = a.ms;
+    if (total_bytes) *total_bytes = a.bytes;
+    return SPEC_OK;
+}
 const char *spec_last_error(void) { return g_err; }
 
 const char *spec_status_string(spec_status s) {
