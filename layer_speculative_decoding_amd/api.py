@@ -52,7 +52,10 @@ class SpecModel:
     def __del__(self):
         h = getattr(self, "handle", None)
         if h:
-            load().spec_model_destroy(h)
+            try:
+                load().spec_model_destroy(h)
+            except Exception:   # interpreter shutdown
+                pass
             self.handle = None
 
 
