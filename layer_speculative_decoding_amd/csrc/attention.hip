@@ -3,17 +3,23 @@
 //
 // A workgroup owns (query block, layer of the group, kv head, sequence, key
 // split).  Its query vectors are the rows of the block times the q heads that
-// share the kv head (GQA), so every K/V tile staged in LDS serves all of them.
-// Per 64-key tile:
-//   QK   lane = key, the four waves split the query vectors; the key's row is
-//        read from LDS in 16-byte pieces and every query element is a
-//        wave-uniform (broadcast) LDS read, so one K read feeds many FMAs;
-//   softmax  wave = query vector, lane = key: running max / sum with wave
-//        reductions (online softmax, float32);
-//   PV   lane = head dimension, four keys per step.
-// The next tile's K/V is prefetched into registers while the current one is
-// processed.  With several key splits the partial (max, sum, unnormalised
-// output) are merged by k_attn_merge in split order.
+// share the kv head (GQA): 16 or 32 of them, zero-padded, held in registers as
+// the B operand of float32 matrix-core products (v_mfma_f32_16x16x4_f32).
+// The four waves take interleaved 16-key blocks of the split's key range and
+// run independently, reading K and V straight from HBM (no LDS staging):
+//   QK   S[key][qv] = sum_d K[key][d] q[qv][d]; lane (c, g) = (l % 16, l / 16)
+//        supplies K[key c][dims of group g] and q[qv c][the same dims], so
+//        each lane's K slice is contiguous in memory;
+//   softmax  online (running max and sum per query vector) in float32; the
+//        scores of query vector c sit in lane group column c;
+//   PV   O[qv][dim] += P[qv][key] V[key][dim]: the probabilities are used in
+//        place as the A operand, lane (c, g) supplies V[key 4g + r][dims
+//        (HD / 16) c ...], so each lane reads HD / 16 contiguous elements.
+// Every product input is exact in float32 (K, V widened from the cache type),
+// so the result equals the float32 dot products up to summation order.  The
+// waves' (max, sum, output) are merged in wave order through LDS; with several
+// key splits the workgroup publishes them and k_attn_merge combines the splits
+// in split order.
 #include "spec_device.h"
 #include "spec_kernels.h"
 
@@ -21,29 +27,75 @@ namespace spec {
 
 namespace {
 
-constexpr int kQV = 64;        // query vectors per workgroup
-constexpr int kTK = 64;        // keys per tile
+constexpr int kKB = 16;        // keys per block (one MFMA row block)
+constexpr int kWaves = 4;
+constexpr int kSpan = kKB * kWaves;   // keys per round of the four waves
 constexpr int kSplitMax = 64;
+constexpr int kMaxQV = 32;     // query vectors per workgroup at most
 
-template <typename T, int HD>
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// N consecutive elements of the cache type, widened to float.
+template <int N>
+__device__ __forceinline__ void load_span(const uint16_t *p, float *o) {
+    if constexpr (N % 8 == 0) {
+#pragma unroll
+        for (int i = 0; i < N / 8; ++i) Store<uint16_t>::unpack(ld16(p + 8 * i), o + 8 * i);
+    } else if constexpr (N == 4) {
+        const uint2 v = *reinterpret_cast<const uint2 *>(p);
+        o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+    } else if constexpr (N == 2) {
+        const uint32_t v = *reinterpret_cast<const uint32_t *>(p);
+        o[0] = bf16_lo(v); o[1] = bf16_hi(v);
+    } else {
+        static_assert(N == 1, "span");
+        o[0] = bf16_to_f32(p[0]);
+    }
+}
+template <int N>
+__device__ __forceinline__ void load_span(const float *p, float *o) {
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N / 4; ++i) Store<float>::unpack(ld16(p + 4 * i), o + 4 * i);
+    } else if constexpr (N == 2) {
+        const float2 v = *reinterpret_cast<const float2 *>(p);
+        o[0] = v.x; o[1] = v.y;
+    } else {
+        static_assert(N == 1, "span");
+        o[0] = p[0];
+    }
+}
+
+template <typename T, int N>
+__device__ __forceinline__ void store_span(T *p, const float *v) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) p[i] = Store<T>::from_f32(v[i]);
+}
+
+// The workgroup's query vector qv -> (row of the call, q head); -1 if padding.
+struct QvMap {
+    int G, QV, row0, head0;
+    __device__ __forceinline__ bool valid(int qv) const { return qv < QV; }
+    __device__ __forceinline__ int row(int qv) const { return row0 + qv / G; }
+    __device__ __forceinline__ int head(int qv) const { return head0 + qv % G; }
+};
+
+template <typename T, int HD, int NQB>
 __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
-    using S = Store<T>;
-    constexpr int E = S::kPer16;                 // elements per 16-byte piece
-    constexpr int KROW = HD + 16 / sizeof(T);    // LDS row stride (elements), padded by 16 bytes
-    constexpr int NPF = (kTK * HD / E + 255) / 256;   // 16-byte pieces of one tile per thread
-    constexpr int QVW = kQV / 4;                 // query vectors per wave in QK
-    constexpr int DPT = 256 / HD;                // threads per head dimension in PV
-    constexpr int NQP = kQV / DPT;               // query vectors per thread in PV (max)
-    __shared__ __align__(16) float q_s[kQV][HD];
-    __shared__ __align__(16) T k_s[kTK][KROW];
-    __shared__ __align__(16) T v_s[kTK][KROW];
-    __shared__ __align__(16) float p_s[kQV][kTK];
-    __shared__ float m_s[kQV], l_s[kQV], c_s[kQV];
-    __shared__ int pos_s[kQV];
+    constexpr int DK = HD / 4 < 8 ? HD / 4 : 8;   // dims per lane per QK piece
+    constexpr int NP = HD / (4 * DK);             // QK pieces per key
+    constexpr int NT = HD / 4;                    // QK products per block (NP * DK)
+    constexpr int DV = HD / 16;                   // dims per lane per key in PV
+    constexpr int QVB = 16 * NQB;
+    constexpr int NREG = NQB * DV * 4;            // output values per lane
+    __shared__ float m_s[kWaves][QVB], l_s[kWaves][QVB];
+    __shared__ __align__(16) float o_s[kWaves - 1][NREG][64];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane & 15, g = lane >> 4;
     const int G = p.hq / p.hkv;
-    const int QB = (kQV / G) > 0 ? kQV / G : 1;
+    const int QB = QVB / G;                       // rows per workgroup
     const int gi = blockIdx.y / p.hkv;
     const int kvh = blockIdx.y - gi * p.hkv;
     const int b = blockIdx.z / p.splits;
@@ -51,10 +103,10 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
     const int mseq = p.rows.mseq;
     const int i0 = blockIdx.x * QB;
     const int nrows = min(QB, mseq - i0);
-    const int QV = nrows * G;
     const int ntok = p.rows.n_tok ? p.rows.n_tok[b] : mseq;
     const int pos0 = p.rows.start_pos[b];
     const float scale = 1.0f / sqrtf((float)HD);
+    const QvMap qm{G, nrows * G, b * mseq + i0, kvh * G};
 
     // keys 0 .. kmax serve this block (rows hold consecutive positions)
     const int last_row = min(i0 + nrows, ntok) - 1;
@@ -62,7 +114,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
     if (kmax >= p.capacity) kmax = p.capacity - 1;
     const int total = kmax + 1;
     int per = (total + p.splits - 1) / p.splits;
-    per = ((per + kTK - 1) / kTK) * kTK;
+    per = ((per + kSpan - 1) / kSpan) * kSpan;
     const int ks = sp * per;
     const int ke = min(total, ks + per);
 
@@ -70,162 +122,166 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
     const T *Kc = reinterpret_cast<const T *>(p.kc) + cache_off;
     const T *Vc = reinterpret_cast<const T *>(p.vc) + cache_off;
 
-    // prefetch of one tile: piece f (16 bytes) of thread tid covers key
-    // (tid + 256 f) / (HD / E), elements ((tid + 256 f) % (HD / E)) * E
-    uint4 kpf[NPF], vpf[NPF];
-    auto fetch = [&](int t0) {
+    // B operand of QK: q[qv = 16 nb + c][dim (4 DK) i + DK g + e] at t = DK i + e
+    float qreg[NQB][NT];
+    int qpos[NQB];
 #pragma unroll
-        for (int f = 0; f < NPF; ++f) {
-            const int idx = tid + 256 * f;
-            const int key = idx / (HD / E), e0 = (idx % (HD / E)) * E;
-            kpf[f] = make_uint4(0, 0, 0, 0);
-            vpf[f] = make_uint4(0, 0, 0, 0);
-            if (key < kTK && t0 + key < ke) {
-                kpf[f] = ld16(Kc + (int64_t)(t0 + key) * HD + e0);
-                vpf[f] = ld16(Vc + (int64_t)(t0 + key) * HD + e0);
-            }
-        }
-    };
-    auto stash = [&]() {
-#pragma unroll
-        for (int f = 0; f < NPF; ++f) {
-            const int idx = tid + 256 * f;
-            const int key = idx / (HD / E), e0 = (idx % (HD / E)) * E;
-            if (key < kTK) {
-                *reinterpret_cast<uint4 *>(&k_s[key][e0]) = kpf[f];
-                *reinterpret_cast<uint4 *>(&v_s[key][e0]) = vpf[f];
-            }
-        }
-    };
-    if (ks < ke) fetch(ks);
-
-    for (int qv = tid; qv < kQV; qv += 256) {
+    for (int nb = 0; nb < NQB; ++nb) {
+        const int qv = 16 * nb + c;
         int pos = -1;
-        if (qv < QV) {
-            const int i = i0 + qv / G;
-            if (i < ntok) {
-                pos = pos0 + i;
+        if (qm.valid(qv)) {
+            const float *qp = p.q + (int64_t)gi * p.q_sel_stride + ((int64_t)qm.row(qv) * p.hq + qm.head(qv)) * HD;
+#pragma unroll
+            for (int i = 0; i < NP; ++i) load_span<DK>(qp + 4 * DK * i + DK * g, &qreg[nb][DK * i]);
+            const int irow = i0 + qv / G;
+            if (irow < ntok) {
+                pos = pos0 + irow;
                 if (pos < 0 || pos >= p.capacity) pos = -1;
             }
+        } else {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) qreg[nb][t] = 0.f;
         }
-        pos_s[qv] = pos;
-        m_s[qv] = -INFINITY;
-        l_s[qv] = 0.f;
-    }
-    for (int idx = tid; idx < QV * (HD / 4); idx += 256) {
-        const int qv = idx / (HD / 4), d4 = (idx % (HD / 4)) * 4;
-        const int rr = qv / G, g = qv - rr * G;
-        const int row = b * mseq + i0 + rr;
-        *reinterpret_cast<float4 *>(&q_s[qv][d4]) = *reinterpret_cast<const float4 *>(
-            p.q + (int64_t)gi * p.q_sel_stride + ((int64_t)row * p.hq + kvh * G + g) * HD + d4);
+        qpos[nb] = pos;
     }
 
-    // PV ownership: thread -> head dimension pd, query vectors qg + DPT * j
-    const int pd = tid % HD;
-    const int qg = tid / HD;
-    float acc[NQP];
+    float m_run[NQB], l_run[NQB];
+    f32x4 acc[NQB][DV];
 #pragma unroll
-    for (int j = 0; j < NQP; ++j) acc[j] = 0.f;
+    for (int nb = 0; nb < NQB; ++nb) {
+        m_run[nb] = -INFINITY;
+        l_run[nb] = 0.f;
+#pragma unroll
+        for (int j = 0; j < DV; ++j) acc[nb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
-    for (int t0 = ks; t0 < ke; t0 += kTK) {
-        __syncthreads();   // previous tile consumed; q_s, pos_s, m_s ready
-        stash();
-        if (t0 + kTK < ke) fetch(t0 + kTK);
-        __syncthreads();
-        // ---- QK: lane = key, wave handles query vectors wave, wave+4, ...
-        float sc[QVW];
+    for (int kb = ks + kKB * wave; kb < ke; kb += kSpan) {
+        // A operand of QK: K[key kb + c][dims of lane group g]
+        float kf[NT];
+        if (kb + c < ke) {
+            const T *kp = Kc + (int64_t)(kb + c) * HD + DK * g;
 #pragma unroll
-        for (int j = 0; j < QVW; ++j) sc[j] = 0.f;
-        for (int e0 = 0; e0 < HD; e0 += E) {
-            float kf[E];
-            S::unpack(*reinterpret_cast<const uint4 *>(&k_s[lane][e0]), kf);
+            for (int i = 0; i < NP; ++i) load_span<DK>(kp + 4 * DK * i, &kf[DK * i]);
+        } else {
 #pragma unroll
-            for (int j = 0; j < QVW; ++j) {
-                const int qv = wave + 4 * j;
-                if (qv < QV) {
+            for (int t = 0; t < NT; ++t) kf[t] = 0.f;
+        }
+        // B operand of PV: V[key kb + 4 g + r][dims DV c ...]
+        float vf[4][DV];
 #pragma unroll
-                    for (int e = 0; e < E; e += 4) {
-                        const float4 qq = *reinterpret_cast<const float4 *>(&q_s[qv][e0 + e]);
-                        sc[j] = fmaf(qq.x, kf[e], sc[j]);
-                        sc[j] = fmaf(qq.y, kf[e + 1], sc[j]);
-                        sc[j] = fmaf(qq.z, kf[e + 2], sc[j]);
-                        sc[j] = fmaf(qq.w, kf[e + 3], sc[j]);
-                    }
-                }
+        for (int r = 0; r < 4; ++r) {
+            const int key = kb + 4 * g + r;
+            if (key < ke) {
+                load_span<DV>(Vc + (int64_t)key * HD + DV * c, vf[r]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < DV; ++j) vf[r][j] = 0.f;
             }
         }
-        const int key = t0 + lane;
 #pragma unroll
-        for (int j = 0; j < QVW; ++j) {
-            const int qv = wave + 4 * j;
-            if (qv < QV) {
-                // ---- online softmax of this query vector over the tile
-                const float s = (key < ke && key <= pos_s[qv]) ? sc[j] * scale : -INFINITY;
-                const float mx = wave_max(s);
-                const float m_old = m_s[qv];
-                const float m_new = fmaxf(m_old, mx);
-                float pv = 0.f, c = 1.f;
-                if (m_new != -INFINITY) {
-                    pv = expf(s - m_new);
-                    c = expf(m_old - m_new);
-                }
-                const float sum = wave_sum(pv);
-                p_s[qv][lane] = pv;
-                if (lane == 0) {
-                    l_s[qv] = l_s[qv] * c + sum;
-                    m_s[qv] = m_new;
-                    c_s[qv] = c;
-                }
+        for (int nb = 0; nb < NQB; ++nb) {
+            f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < NT; ++t) sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t], qreg[nb][t], sc, 0, 0, 0);
+            // lane holds S[key kb + 4 g + r][qv 16 nb + c]
+            float pr[4];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = kb + 4 * g + r;
+                pr[r] = (key < ke && key <= qpos[nb]) ? sc[r] * scale : -INFINITY;
+                mx = fmaxf(mx, pr[r]);
             }
-        }
-        __syncthreads();
-        // ---- PV: lane = head dimension, four keys per step
+            mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+            const float m_new = fmaxf(m_run[nb], mx);
+            const bool none = m_new == -INFINITY;
+            float sum = 0.f;
 #pragma unroll
-        for (int j = 0; j < NQP; ++j) {
-            const int qv = qg + DPT * j;
-            if (qv < QV) acc[j] *= c_s[qv];
-        }
-        const int nk = min(kTK, ke - t0);
-        for (int kk = 0; kk < nk; kk += 4) {
-            float vv[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) vv[u] = S::to_f32(v_s[kk + u][pd]);
-#pragma unroll
-            for (int j = 0; j < NQP; ++j) {
-                const int qv = qg + DPT * j;
-                if (qv < QV) {
-                    const float4 pp = *reinterpret_cast<const float4 *>(&p_s[qv][kk]);
-                    float a = acc[j];
-                    a = fmaf(pp.x, vv[0], a);
-                    a = fmaf(pp.y, vv[1], a);
-                    a = fmaf(pp.z, vv[2], a);
-                    a = fmaf(pp.w, vv[3], a);
-                    acc[j] = a;
-                }
+            for (int r = 0; r < 4; ++r) {
+                pr[r] = none ? 0.f : expf(pr[r] - m_new);
+                sum += pr[r];
             }
+            sum += __shfl_xor(sum, 16, kWave);
+            sum += __shfl_xor(sum, 32, kWave);
+            const float corr = none ? 1.f : expf(m_run[nb] - m_new);
+            l_run[nb] = l_run[nb] * corr + sum;
+            m_run[nb] = m_new;
+            // rescale of the outputs of query vectors 16 nb + 4 g + r (held by lane 4 g + r)
+            f32x4 cr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * g + r, kWave);
+#pragma unroll
+            for (int j = 0; j < DV; ++j) acc[nb][j] *= cr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int j = 0; j < DV; ++j)
+                    acc[nb][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(pr[r], vf[r][j], acc[nb][j], 0, 0, 0);
         }
+    }
+
+    // merge the four waves in wave order
+    if (g == 0) {
+#pragma unroll
+        for (int nb = 0; nb < NQB; ++nb) {
+            m_s[wave][16 * nb + c] = m_run[nb];
+            l_s[wave][16 * nb + c] = l_run[nb];
+        }
+    }
+    if (wave > 0) {
+#pragma unroll
+        for (int nb = 0; nb < NQB; ++nb)
+#pragma unroll
+            for (int j = 0; j < DV; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o_s[wave - 1][(nb * DV + j) * 4 + r][lane] = acc[nb][j][r];
     }
     __syncthreads();
+    if (wave != 0) return;
 
     T *obase = reinterpret_cast<T *>(p.o) + (int64_t)gi * p.o_sel_stride;
     const int64_t stride_sp = (int64_t)p.n_group * p.Mtot * p.hq;
 #pragma unroll
-    for (int j = 0; j < NQP; ++j) {
-        const int qv = qg + DPT * j;
-        if (qv >= QV) continue;
-        const int rr = qv / G, g = qv - rr * G;
-        const int row = b * mseq + i0 + rr;
-        if (p.splits == 1) {
-            const float l = l_s[qv];
-            const float val = (pos_s[qv] >= 0 && l > 0.f) ? acc[j] / l : 0.f;
-            obase[(int64_t)row * p.hq * HD + (kvh * G + g) * HD + pd] = S::from_f32(val);
-        } else {
-            // several key splits: publish (max, sum, unnormalised output)
-            const int64_t pr = (int64_t)sp * stride_sp + ((int64_t)gi * p.Mtot + row) * p.hq + kvh * G + g;
-            p.part_acc[pr * HD + pd] = acc[j];
-            if (pd == 0) {
-                p.part_ml[pr * 2 + 0] = m_s[qv];
-                p.part_ml[pr * 2 + 1] = l_s[qv];
+    for (int nb = 0; nb < NQB; ++nb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int qv = 16 * nb + 4 * g + r;    // this lane's output rows
+            float mw[kWaves], M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                mw[w] = m_s[w][qv];
+                M = fmaxf(M, mw[w]);
+            }
+            float wt[kWaves], L = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                wt[w] = mw[w] == -INFINITY ? 0.f : expf(mw[w] - M);
+                L = fmaf(wt[w], l_s[w][qv], L);
+            }
+            float ov[DV];
+#pragma unroll
+            for (int j = 0; j < DV; ++j) {
+                float o = wt[0] * acc[nb][j][r];
+#pragma unroll
+                for (int w = 1; w < kWaves; ++w) o = fmaf(wt[w], o_s[w - 1][(nb * DV + j) * 4 + r][lane], o);
+                ov[j] = o;
+            }
+            if (!qm.valid(qv)) continue;
+            const int row = qm.row(qv), head = qm.head(qv);
+            if (p.splits == 1) {
+                const bool ok = L > 0.f;   // rows without a valid position have no keys
+#pragma unroll
+                for (int j = 0; j < DV; ++j) ov[j] = ok ? ov[j] / L : 0.f;
+                store_span<T, DV>(obase + ((int64_t)row * p.hq + head) * HD + DV * c, ov);
+            } else {
+                // several key splits: publish (max, sum, unnormalised output)
+                const int64_t pr = (int64_t)sp * stride_sp + ((int64_t)gi * p.Mtot + row) * p.hq + head;
+                store_span<float, DV>(p.part_acc + pr * HD + DV * c, ov);
+                if (c == 0) {
+                    p.part_ml[pr * 2 + 0] = M;
+                    p.part_ml[pr * 2 + 1] = L;
+                }
             }
         }
     }
@@ -272,12 +328,14 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnParams p) {
     }
 }
 
-template <typename T, int HD>
+int qv_blocks(int G, int mseq) { return (long)mseq * G <= 16 ? 1 : 2; }
+
+template <typename T, int HD, int NQB>
 hipError_t launch_hd(const AttnParams &p, hipStream_t s) {
     const int G = p.hq / p.hkv;
-    const int QB = (kQV / G) > 0 ? kQV / G : 1;
+    const int QB = 16 * NQB / G;
     dim3 grid((p.rows.mseq + QB - 1) / QB, p.n_group * p.hkv, p.batch * p.splits);
-    hipLaunchKernelGGL((k_attn<T, HD>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_attn<T, HD, NQB>), grid, dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
     const int64_t items = (int64_t)p.n_group * p.Mtot * p.hq;
@@ -285,13 +343,21 @@ hipError_t launch_hd(const AttnParams &p, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <typename T, int HD>
+hipError_t launch_nqb(const AttnParams &p, hipStream_t s) {
+    if (qv_blocks(p.hq / p.hkv, p.rows.mseq) == 1) return launch_hd<T, HD, 1>(p, s);
+    return launch_hd<T, HD, 2>(p, s);
+}
+
 template <typename T>
 hipError_t launch_t(const AttnParams &p, hipStream_t s) {
+    if (p.hkv < 1 || p.hq % p.hkv || p.hq / p.hkv > kMaxQV || p.splits < 1 || p.splits > kSplitMax)
+        return hipErrorInvalidValue;
     switch (p.hd) {
-    case 16: return launch_hd<T, 16>(p, s);
-    case 32: return launch_hd<T, 32>(p, s);
-    case 64: return launch_hd<T, 64>(p, s);
-    case 128: return launch_hd<T, 128>(p, s);
+    case 16: return launch_nqb<T, 16>(p, s);
+    case 32: return launch_nqb<T, 32>(p, s);
+    case 64: return launch_nqb<T, 64>(p, s);
+    case 128: return launch_nqb<T, 128>(p, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -300,20 +366,22 @@ hipError_t launch_t(const AttnParams &p, hipStream_t s) {
 
 int attention_split_max() { return kSplitMax; }
 
-// Key splits so that decode-shaped calls (one query block per sequence) fill
-// the GPU; prompt-length calls already have many query blocks.
+// Key splits so that the workgroups of a call fill the GPU: about
+// kTargetWG workgroups, each split at least one round of the four waves.
 int attention_splits(int n_group, int batch, int hq, int hkv, int mseq, int max_pos) {
+    constexpr int kTargetWG = 512;
     const int G = hq / hkv;
-    const int QB = (kQV / G) > 0 ? kQV / G : 1;
+    const int QB = 16 * qv_blocks(G, mseq) / G;
     const int nqb = (mseq + QB - 1) / QB;
-    if (nqb > 1 || batch * mseq > 64) return 1;
-    const int base = n_group * hkv * batch;
-    const int tiles = (max_pos + 1 + kTK - 1) / kTK;
-    int sp = (512 + base - 1) / base;
-    if (sp > tiles) sp = tiles;
+    const long base = (long)nqb * n_group * hkv * batch;
+    const int rounds = (max_pos + 1 + kSpan - 1) / kSpan;
+    long sp = (kTargetWG + base - 1) / base;
+    if (sp > rounds) sp = rounds;
     if (sp > kSplitMax) sp = kSplitMax;
-    return sp < 1 ? 1 : sp;
+    return sp < 1 ? 1 : (int)sp;
 }
+
+int attention_max_group() { return kMaxQV; }
 
 hipError_t launch_attention(int dtype, const AttnParams &p, hipStream_t s) {
     return dtype ? launch_t<uint16_t>(p, s) : launch_t<float>(p, s);

@@ -459,6 +459,9 @@ spec_status spec_model_create(const spec_model_desc *desc, const spec_weights *w
     if (d.head_dim != 16 && d.head_dim != 32 && d.head_dim != 64 && d.head_dim != 128)
         return fail(SPEC_ERR_UNSUPPORTED, "head_dim %d not in {16, 32, 64, 128}", d.head_dim);
     if (d.n_q_heads % d.n_kv_heads) return fail(SPEC_ERR_SHAPE, "n_q_heads %% n_kv_heads != 0");
+    if (d.n_q_heads / d.n_kv_heads > attention_max_group())
+        return fail(SPEC_ERR_UNSUPPORTED, "n_q_heads / n_kv_heads %d > %d", d.n_q_heads / d.n_kv_heads,
+                    attention_max_group());
     if (d.d_model % 8 || d.d_ffn % 8 || (d.n_q_heads * d.head_dim) % 8)
         return fail(SPEC_ERR_SHAPE, "d_model, d_ffn and n_q_heads*head_dim must be multiples of 8");
     if (d.d_model > 16384) return fail(SPEC_ERR_UNSUPPORTED, "d_model %d > 16384", d.d_model);

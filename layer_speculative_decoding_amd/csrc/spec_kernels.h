@@ -148,6 +148,7 @@ struct AttnParams {
 hipError_t launch_attention(int dtype, const AttnParams &p, hipStream_t s);
 int attention_splits(int n_group, int batch, int hq, int hkv, int mseq, int max_pos);
 int attention_split_max();
+int attention_max_group();   // largest n_q_heads / n_kv_heads
 
 // Arg-max reduction of the lm-head sampling partials -> tokens.
 hipError_t launch_sample_reduce(const float *part_val, const int32_t *part_idx, int n_parts, int M,
