@@ -6,9 +6,9 @@
 //    or a residual-add epilogue below) left per-block partial sums of squares,
 //    and every consuming block sums a row's partials in block order, so no
 //    separate normalisation launch and no cross-block synchronisation exist.
-//  * Epilogues get the two output rows r0, r1 of a unit for activation row m,
-//    add the bias and apply the fused consumer: store, QKV RoPE + KV append,
-//    SiLU gate, residual add, attention-output routing, logits + arg-max.
+//  * Epilogues add the bias and apply the fused consumer: QKV RoPE + KV
+//    append and the SiLU gate take a pair of output rows; store, residual
+//    add, attention-output routing and logits + arg-max take one row.
 //  * Residual writers emit those per-block partial sums of squares.
 #pragma once
 #include "spec_device.h"
@@ -33,20 +33,25 @@ __device__ __forceinline__ int x_row(const GemvParams &p, int gm) {
     return gm * p.xgather_mseq + nt - 1;
 }
 
-// 1/rms of this launch's activation rows into inv_s[0 .. M-1]: wave w sums the
-// partials of rows w, w + nw, ... (lane-strided, then a fixed tree); every
-// block computes bit-identical values.  Call with the whole block.
-__device__ __forceinline__ void block_inv_rms(const GemvParams &p, float *inv_s) {
-    if (p.xmode != X_NORM) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    for (int m = wave; m < p.M; m += nw) {
-        const float *src = p.xss + (int64_t)x_row(p, p.m0 + m) * p.xnparts;
-        float s = 0.f;
-        for (int i = lane; i < p.xnparts; i += 64) s += src[i];
-        s = wave_sum(s);
-        if (lane == 0) inv_s[m] = 1.0f / sqrtf(s / (float)p.K + p.eps);
+// 1/rms of residual row hrow from its p.xnparts sum-of-squares partials.
+// Lane i adds partials i, i + 64, ... in that order (eight loads in flight),
+// then a fixed xor tree: every caller forms the same bits.  Whole wave.
+__device__ __forceinline__ float row_inv_rms(const GemvParams &p, int hrow) {
+    const int lane = threadIdx.x & 63;
+    const float *src = p.xss + (int64_t)hrow * p.xnparts;
+    const int n = p.xnparts;
+    float s = 0.f;
+    int i = lane;
+    for (; i + 7 * 64 < n; i += 8 * 64) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = src[i + 64 * j];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s += v[j];
     }
-    __syncthreads();
+    for (; i < n; i += 64) s += src[i];
+    s = wave_sum(s);
+    return 1.0f / sqrtf(s / (float)p.K + p.eps);
 }
 
 // 8 normalised activations of residual row hrow at k .. k+7, as float
@@ -84,23 +89,17 @@ __device__ __forceinline__ void add_sel(float (&acc)[kMaxSel], int sel, float v)
     for (int s = 0; s < kMaxSel; ++s) acc[s] += (s == sel) ? v : 0.f;
 }
 
-// kLogits: instance that carries the logits / sampling case (the Philox and
-// Gumbel code is kept out of the register budget of the other instances)
-template <typename T, bool kLogits>
-__device__ __forceinline__ void epilogue(const GemvParams &p, int u, int r0, int r1, int sel, int m,
-                                         float y0, float y1, float &best_v, int &best_i,
-                                         float (&ss)[kMaxSel]) {
+// Epilogues whose output rows come in pairs: EPI_QKV_ROPE (the rotate-half
+// partners j, j + hd/2 of a q or k head; v rows pass through) and
+// EPI_SILU_MUL (gate row r0, up row r1).  u: the unit (pair) index, which is
+// the activation column of the SiLU product.
+template <typename T, int EPI>
+__device__ __forceinline__ void epi_pair(const GemvParams &p, int u, int r0, int r1, int sel, int m, float y0,
+                                         float y1) {
     using S = Store<T>;
     const int gm = p.m0 + m;
     if (p.bias) { y0 += p.bias[r0]; y1 += p.bias[r1]; }
-    switch (p.epi) {
-    case EPI_STORE: {
-        const int64_t base = (int64_t)gm * p.out_ld + (int64_t)sel * p.out_sel_stride - (int64_t)sel * p.rows_per_sel;
-        p.out[base + r0] = y0;
-        p.out[base + r1] = y1;
-        break;
-    }
-    case EPI_QKV_ROPE: {
+    if constexpr (EPI == EPI_QKV_ROPE) {
         const int rl = r0 - sel * p.rows_per_sel;
         const int hd = p.hd;
         const int head = rl / hd;
@@ -127,78 +126,89 @@ __device__ __forceinline__ void epilogue(const GemvParams &p, int u, int r0, int
             c[j] = S::from_f32(y0);
             c[j + hd / 2] = S::from_f32(y1);
         }
-        break;
-    }
-    case EPI_SILU_MUL: {
+    } else if constexpr (EPI == EPI_SILU_MUL) {
         T *a = reinterpret_cast<T *>(p.act) + (int64_t)gm * p.act_ld + u;
         *a = S::from_f32(silu(y0) * y1);
-        break;
     }
-    case EPI_RESID_ADD: {
+}
+
+// Gumbel noise of vocab row v of the draft stream (kept out of line: the
+// matrix-core epilogue calls it for several rows per lane).
+__device__ __noinline__ float gumbel_one(uint64_t seed, uint32_t b, uint32_t pos, uint32_t v) {
+    const Philox4 w = philox4x64_10(v >> 2, pos, 0, kDraft, seed, b);
+    return pick_word(w, v & 3);
+}
+
+// Epilogues of single output rows.  ssv: this row's contribution to the
+// sum of squares of the residual row the epilogue wrote (set member `sel`
+// for parallel-MLP attention outputs, else member 0); best_v / best_i: the
+// running arg-max of the sampling scores.
+template <typename T, int EPI>
+__device__ __forceinline__ void epi_row(const GemvParams &p, int r, int sel, int m, float y, float &ssv,
+                                        float &best_v, int &best_i) {
+    const int gm = p.m0 + m;
+    if (p.bias) y += p.bias[r];
+    const int rl = r - sel * p.rows_per_sel;
+    if constexpr (EPI == EPI_STORE) {
+        p.out[(int64_t)gm * p.out_ld + (int64_t)sel * p.out_sel_stride + rl] = y;
+    } else if constexpr (EPI == EPI_RESID_ADD) {
         float *h = p.h + (int64_t)gm * p.d;
-        float v0 = h[r0] + y0, v1 = h[r1] + y1;
-        if (p.add2) {
-            const float *a = p.add2 + (int64_t)gm * p.d;
-            v0 += a[r0];
-            v1 += a[r1];
-        }
-        h[r0] = v0;
-        h[r1] = v1;
-        add_sel(ss, 0, v0 * v0 + v1 * v1);
-        break;
-    }
-    case EPI_ATTN_OUT: {
-        const int rl0 = r0 - sel * p.rows_per_sel, rl1 = r1 - sel * p.rows_per_sel;
+        float v = h[rl] + y;
+        if (p.add2) v += p.add2[(int64_t)gm * p.d + rl];
+        h[rl] = v;
+        ssv = fmaf(v, v, ssv);
+    } else if constexpr (EPI == EPI_ATTN_OUT) {
         const int64_t row = (int64_t)gm * p.d;
         if (!p.par_mlp) {
             if (sel == 0) {
                 float *h = p.h + row;
-                const float v0 = h[rl0] + y0, v1 = h[rl1] + y1;
-                h[rl0] = v0;
-                h[rl1] = v1;
-                add_sel(ss, 0, v0 * v0 + v1 * v1);
+                const float v = h[rl] + y;
+                h[rl] = v;
+                ssv = fmaf(v, v, ssv);
             } else {
-                float *a = p.out + (int64_t)sel * p.out_sel_stride + row;
-                a[rl0] = y0;
-                a[rl1] = y1;
+                p.out[(int64_t)sel * p.out_sel_stride + row + rl] = y;
             }
         } else {
-            const float *h = p.h + row;
-            const float h0 = h[rl0], h1 = h[rl1];
-            if (sel == 0) {
-                p.h0[row + rl0] = h0;
-                p.h0[row + rl1] = h1;
-            }
-            float *a = p.out + (int64_t)sel * p.out_sel_stride + row;
-            a[rl0] = y0;
-            a[rl1] = y1;
-            const float s0 = h0 + y0, s1 = h1 + y1;
-            add_sel(ss, sel, s0 * s0 + s1 * s1);
+            const float hv = p.h[row + rl];
+            if (sel == 0) p.h0[row + rl] = hv;
+            p.out[(int64_t)sel * p.out_sel_stride + row + rl] = y;
+            const float s0 = hv + y;
+            ssv = fmaf(s0, s0, ssv);
         }
-        break;
-    }
-    case EPI_LOGITS: {
-        if constexpr (!kLogits) break;
-        if (p.out) {
-            float *o = p.out + (int64_t)gm * p.out_ld;
-            o[r0] = y0;
-            o[r1] = y1;
-        }
-        float s0 = y0, s1 = y1;
+    } else if constexpr (EPI == EPI_LOGITS) {
+        if (p.out) p.out[(int64_t)gm * p.out_ld + rl] = y;
+        float sc = y;
         if (p.inv_temp != 0.0f) {
             const int pos = p.samp_pos[gm] + (p.samp_ntok ? p.samp_ntok[gm] : p.samp_nconst);
-            float g0, g1;
-            gumbel_pair(p.seed, (uint32_t)gm, (uint32_t)pos, kDraft, (uint32_t)r0, (uint32_t)r1, g0, g1);
-            s0 = y0 * p.inv_temp + g0;
-            s1 = y1 * p.inv_temp + g1;
+            sc = y * p.inv_temp + gumbel_one(p.seed, (uint32_t)gm, (uint32_t)pos, (uint32_t)rl);
         }
-        argmax_merge(best_v, best_i, s0, r0);
-        argmax_merge(best_v, best_i, s1, r1);
-        break;
-    }
-    default:
-        break;
+        argmax_merge(best_v, best_i, sc, rl);
     }
 }
+
+// EPI_LOGITS for two adjacent rows r0, r0 + 1 (one Philox block serves both)
+template <typename T>
+__device__ __forceinline__ void epi_logits2(const GemvParams &p, int r0, int r1, int m, float y0, float y1,
+                                            float &best_v, int &best_i) {
+    const int gm = p.m0 + m;
+    if (p.bias) { y0 += p.bias[r0]; y1 += p.bias[r1]; }
+    if (p.out) {
+        p.out[(int64_t)gm * p.out_ld + r0] = y0;
+        p.out[(int64_t)gm * p.out_ld + r1] = y1;
+    }
+    float s0 = y0, s1 = y1;
+    if (p.inv_temp != 0.0f) {
+        const int pos = p.samp_pos[gm] + (p.samp_ntok ? p.samp_ntok[gm] : p.samp_nconst);
+        float g0, g1;
+        gumbel_pair(p.seed, (uint32_t)gm, (uint32_t)pos, kDraft, (uint32_t)r0, (uint32_t)r1, g0, g1);
+        s0 = y0 * p.inv_temp + g0;
+        s1 = y1 * p.inv_temp + g1;
+    }
+    argmax_merge(best_v, best_i, s0, r0);
+    argmax_merge(best_v, best_i, s1, r1);
+}
+
+constexpr bool epi_is_pair(int epi) { return epi == EPI_QKV_ROPE || epi == EPI_SILU_MUL; }
+constexpr bool epi_has_ss(int epi) { return epi == EPI_RESID_ADD || epi == EPI_ATTN_OUT; }
 
 }  // namespace spec

@@ -1,19 +1,25 @@
 // Skinny bf16 GEMM on the matrix cores for 2..32 activation rows (the k+1
-// verification rows, the calibration rows), with the same fused epilogues as
-// the VALU GEMV.
+// verification rows, the calibration rows, several sequences' draft rows),
+// with the same fused epilogues as the VALU GEMV.
 //
 // Y[m][n] = sum_k X[m][k] W[n][k] with v_mfma_f32_16x16x32_bf16: the
 // activations are the A operand (16 rows, zero padded), a 16-row block of W
-// is the B operand, so every lane loads 16 contiguous bytes of a weight row
-// per MFMA and each weight byte is read from HBM exactly once.  At these row
-// counts the product is bandwidth bound (a few flops per weight byte); the
-// matrix cores remove the VALU bottleneck that a per-row FMA loop hits once
-// there are more than a handful of activation rows.
+// is the B operand.  At these row counts the product is bound by HBM
+// bandwidth (a few flops per weight byte), so the kernel is organised around
+// the weight stream:
 //
-// A workgroup owns a unit = a pair of 16-row blocks (r0 .. r0+15 and the
-// partner block r1 = r0 + pair_block/2, so RoPE pairs and (gate, up) pairs
-// meet in one workgroup) and splits K over KS wave pairs; the KS partial
-// tiles are summed in a fixed order through LDS.
+//  * A workgroup owns one unit: a 16-row block of W, or for paired epilogues
+//    (RoPE partners, gate/up) the two blocks r0 and r0 + pair_block/2, so the
+//    pair meets in the same lane's registers.  Its KS waves split K into
+//    contiguous ranges of 256-element tiles.
+//  * Weights are read with whole-row coalescing: each 16-byte-per-lane load
+//    instruction covers two rows x 512 contiguous bytes.  The MFMA operand
+//    layout needs 16 rows x 64 bytes per instruction instead, which halves the
+//    bytes per memory request, so each wave stages its tile through a private
+//    LDS buffer (padded rows keep the operand reads conflict-free) and loads
+//    the next tile while the matrix cores consume the current one.
+//  * The KS partial tiles are summed in wave order through LDS; the first
+//    wave runs the epilogue straight from its accumulators.
 #include "epilogue.h"
 #include "spec_device.h"
 #include "spec_kernels.h"
@@ -25,8 +31,10 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMaxKS = 4;        // K splits (wave pairs) per workgroup
-constexpr int kMaxGridM = 256 * 8;
+constexpr int kTK = 256;          // K elements per staged tile
+constexpr int kLD = kTK + 8;      // LDS row stride in elements (16 bytes of padding)
+constexpr int kMaxKS = 16;        // waves per workgroup
+constexpr int kLogitGrid = 2048;  // workgroups of a sampling product (= arg-max partials per row)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &v) {
     bf16x8 r;
@@ -34,225 +42,237 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &v) {
     return r;
 }
 
-__device__ __forceinline__ uint4 pack_bf16x8(const float *f) {
-    uint4 r;
-    r.x = (uint32_t)f32_to_bf16(f[0]) | ((uint32_t)f32_to_bf16(f[1]) << 16);
-    r.y = (uint32_t)f32_to_bf16(f[2]) | ((uint32_t)f32_to_bf16(f[3]) << 16);
-    r.z = (uint32_t)f32_to_bf16(f[4]) | ((uint32_t)f32_to_bf16(f[5]) << 16);
-    r.w = (uint32_t)f32_to_bf16(f[6]) | ((uint32_t)f32_to_bf16(f[7]) << 16);
-    return r;
+// sum over the 16 lanes of a lane group (fixed xor tree)
+__device__ __forceinline__ float group16_sum(float v) {
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, kWave);
+    return v;
 }
-
-// A-operand pieces (16 consecutive k of one activation row) for one 64-wide
-// chunk: plain bf16 rows, or RMSNorm-ed residual rows rounded to bf16.
-__device__ __forceinline__ void x_tile(const GemvParams &p, const uint16_t *xrow, int sel, int hrow, float inv,
-                                       int k, uint4 &x0, uint4 &x1) {
-    if (p.xmode == X_PLAIN) {
-        x0 = ld16(xrow + k);
-        x1 = ld16(xrow + k + 8);
-    } else {
-        float f[8];
-        x_norm8(p, sel, hrow, k, inv, f);
-        x0 = pack_bf16x8(f);
-        x_norm8(p, sel, hrow, k + 8, inv, f);
-        x1 = pack_bf16x8(f);
+__device__ __forceinline__ void group16_argmax(float &v, int &i) {
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+        const float v2 = __shfl_xor(v, o, kWave);
+        const int i2 = __shfl_xor(i, o, kWave);
+        argmax_merge(v, i, v2, i2);
     }
 }
 
-// MT: number of 16-row activation tiles (1: M <= 16, 2: M <= 32)
-// kSingle: a unit is one 16-row block (rows r0 .. r0+15, epilogue pairs
-// (r0 + j, r0 + 8 + j)) and all 2 KS waves split K; otherwise a unit is a
-// pair of 16-row blocks and KS wave pairs split K.
-template <int MT, bool kLogits, bool kSingle>
-__global__ __launch_bounds__(512) void k_gemm_mfma(GemvParams p, int KS) {
+// MT: 16-row activation tiles (1: M <= 16, 2: M <= 32).  Paired epilogues
+// take two 16-row blocks per unit, the others one.  KS waves per workgroup.
+template <int MT, int EPI, int KS>
+__global__ __launch_bounds__(64 * KS) void k_gemm_mfma(GemvParams p, int ups) {
+    constexpr bool kPair = epi_is_pair(EPI);
+    constexpr int B = kPair ? 2 : 1;        // 16-row blocks per unit
+    constexpr int NL = 8 * B;               // 16-byte loads per lane per tile
+    __shared__ __align__(16) uint16_t smem[KS * 16 * B * kLD];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;     // 0 .. 2*KS-1
-    const int blk = kSingle ? 0 : (wave & 1);      // which block of the pair
-    const int part = kSingle ? wave : (wave >> 1); // K split index
-    const int nparts_k = kSingle ? 2 * KS : KS;
+    const int part = threadIdx.x >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    uint16_t *tile = smem + (size_t)part * (16 * B) * kLD;
     const int K = p.K;
-    const int nchunk = K >> 6;             // 64-element chunks
-    const int per = (nchunk + nparts_k - 1) / nparts_k;
-    const int c0 = part * per;
-    const int c1 = min(nchunk, c0 + per);
+    const int ntile = (K + kTK - 1) / kTK;
+    const int per = (ntile + KS - 1) / KS;
+    const int t0 = part * per, t1 = min(ntile, t0 + per);
     const int half = p.pair_block >> 1;
-    const int bph = half >> 4;             // 16-row blocks per half
-    const int li = lane & 15;              // row within the block / activation row
-    const int lg = lane >> 4;              // lane group: k offset 16 * lg within a chunk
+    const int bph = half >> 4;              // 16-row blocks per half (paired)
+    const int lrow = lane >> 5, lcol = 8 * (lane & 31);   // load lane -> (row of a pair, element)
 
-    __shared__ f32x4 red[2 * kMaxKS][MT][64];
-    __shared__ float tile[2][MT * 16][17];
-    float best_v = -INFINITY;
-    int best_i = 0x7FFFFFFF;
-    float ss[kMaxSel];
+    float best_v[MT][4];
+    int best_i[MT][4];
 #pragma unroll
-    for (int s = 0; s < kMaxSel; ++s) ss[s] = 0.f;
-    __shared__ float inv_s[MT * 16];
-    block_inv_rms(p, inv_s);
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) { best_v[t][r] = -INFINITY; best_i[t][r] = 0x7FFFFFFF; }
 
     for (int u = blockIdx.x; u < p.n_units; u += gridDim.x) {
-        int r0, r1;
-        if (kSingle) {
-            r0 = u * 16;
-            r1 = r0 + 8;
+        int r0b, r1b;
+        if (kPair) {
+            const int bb = u / bph, jb = u - bb * bph;
+            r0b = bb * p.pair_block + jb * 16;
+            r1b = r0b + half;
         } else {
-            const int bb = u / bph;
-            const int jb = u - bb * bph;
-            r0 = bb * p.pair_block + jb * 16;
-            r1 = r0 + half;
+            r0b = u * 16;
+            r1b = r0b;
         }
-        const int rb = blk ? r1 : r0;
-        const int sel = r0 / p.rows_per_sel;
-        const uint16_t *w = reinterpret_cast<const uint16_t *>(p.W) + (int64_t)(rb + li) * K + 16 * lg;
-        const uint16_t *x = reinterpret_cast<const uint16_t *>(p.X) + (int64_t)sel * p.x_sel_stride +
-                            (int64_t)p.m0 * K + 16 * lg;
-        f32x4 acc[MT];
-#pragma unroll
-        for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int sel = r0b / p.rows_per_sel;
+        const uint16_t *W = reinterpret_cast<const uint16_t *>(p.W);
+        const uint16_t *xb = reinterpret_cast<const uint16_t *>(p.X) + (int64_t)sel * p.x_sel_stride;
         bool xok[MT];
-        int hrow[MT];
-        float inv[MT];
+        const uint16_t *xr[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-            xok[t] = (t * 16 + li) < p.M;
-            hrow[t] = 0;
-            inv[t] = 0.f;
-            if (xok[t] && p.xmode == X_NORM) {
-                hrow[t] = x_row(p, p.m0 + t * 16 + li);
-                inv[t] = inv_s[t * 16 + li];
-            }
+            xok[t] = t * 16 + li < p.M;
+            xr[t] = xb + (int64_t)(p.m0 + t * 16 + li) * K + 8 * lg;
         }
-        const int kl = 16 * lg;   // this lane group's offset inside a chunk
+        f32x4 acc[MT][B];
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int j = 0; j < B; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        int c = c0;
-        for (; c + 3 < c1; c += 4) {
-            uint4 wv[4][2];
+        uint4 wv[NL];
+        auto load = [&](int tt) {
+            const int k = tt * kTK + lcol;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                wv[q][0] = ld16_stream(w + (c + q) * 64);
-                wv[q][1] = ld16_stream(w + (c + q) * 64 + 8);
+            for (int i = 0; i < NL; ++i) {
+                const int tr = 2 * i + lrow;                      // tile row
+                const int grow = (tr < 16 ? r0b : r1b) + (tr & 15);
+                wv[i] = k < K ? ld16_stream(W + (int64_t)grow * K + k) : make_uint4(0, 0, 0, 0);
             }
+        };
+        if (t0 < t1) load(t0);
+        for (int tt = t0; tt < t1; ++tt) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int i = 0; i < NL; ++i) *reinterpret_cast<uint4 *>(&tile[(2 * i + lrow) * kLD + lcol]) = wv[i];
+            // the tile's activation operands are requested before the next
+            // tile's weights, so the matrix cores wait only for them
+            const int nsteps = min(kTK, K - tt * kTK) >> 5;     // 32-element MFMA steps in this tile
+            uint4 xv[kTK / 32][MT];
 #pragma unroll
-                for (int t = 0; t < MT; ++t) {
-                    uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
-                    if (xok[t])
-                        x_tile(p, x - kl + (int64_t)(t * 16 + li) * K, sel, hrow[t], inv[t], (c + q) * 64 + kl, x0, x1);
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x0), as_bf16x8(wv[q][0]), acc[t], 0, 0, 0);
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x1), as_bf16x8(wv[q][1]), acc[t], 0, 0, 0);
+            for (int s2 = 0; s2 < kTK / 32; ++s2)
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+                    xv[s2][t] = (xok[t] && s2 < nsteps) ? ld16(xr[t] + tt * kTK + 32 * s2) : make_uint4(0, 0, 0, 0);
+            if (tt + 1 < t1) load(tt + 1);
+#pragma unroll
+            for (int s2 = 0; s2 < kTK / 32; ++s2) {
+                if (s2 < nsteps) {
+#pragma unroll
+                    for (int j = 0; j < B; ++j) {
+                        const uint4 wt =
+                            *reinterpret_cast<const uint4 *>(&tile[(16 * j + li) * kLD + 32 * s2 + 8 * lg]);
+#pragma unroll
+                        for (int t = 0; t < MT; ++t)
+                            acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xv[s2][t]), as_bf16x8(wt),
+                                                                                 acc[t][j], 0, 0, 0);
+                    }
                 }
             }
         }
-        for (; c < c1; ++c) {
-            const uint4 w0 = ld16_stream(w + c * 64), w1 = ld16_stream(w + c * 64 + 8);
+        // fixed-order sum of the K parts; C layout: lane l, register r holds
+        // C[4 * (l / 16) + r][l % 16] = (activation row, weight row of the block)
+        if (KS > 1) {
+            __syncthreads();   // every wave is done with its tile
+            f32x4 *red = reinterpret_cast<f32x4 *>(tile);
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
-                if (xok[t])
-                    x_tile(p, x - kl + (int64_t)(t * 16 + li) * K, sel, hrow[t], inv[t], c * 64 + kl, x0, x1);
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x0), as_bf16x8(w0), acc[t], 0, 0, 0);
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x1), as_bf16x8(w1), acc[t], 0, 0, 0);
-            }
-        }
-        // fixed-order sum of the K splits; C layout: lane l, register r holds
-        // C[4 * (l / 16) + r][l % 16]
+            for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int t = 0; t < MT; ++t) red[wave][t][lane] = acc[t];
-        __syncthreads();
-        if (part == 0) {
+                for (int j = 0; j < B; ++j) red[(t * B + j) * 64 + lane] = acc[t][j];
+            __syncthreads();
+            if (part == 0) {
+                for (int q = 1; q < KS; ++q) {
+                    const f32x4 *o = reinterpret_cast<const f32x4 *>(smem + (size_t)q * (16 * B) * kLD);
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                f32x4 s = red[blk][t][lane];
-                for (int q = 1; q < nparts_k; ++q) {
-                    const f32x4 o = red[kSingle ? q : 2 * q + blk][t][lane];
-                    s[0] += o[0]; s[1] += o[1]; s[2] += o[2]; s[3] += o[3];
+                    for (int t = 0; t < MT; ++t)
+#pragma unroll
+                        for (int j = 0; j < B; ++j) acc[t][j] += o[(t * B + j) * 64 + lane];
                 }
+            }
+            __syncthreads();
+        }
+        if (part != 0) continue;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) tile[blk][t * 16 + 4 * lg + r][li] = s[r];
+        for (int t = 0; t < MT; ++t) {
+            float ssv[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = t * 16 + 4 * lg + r;
+                if (m >= p.M) continue;
+                if constexpr (kPair) {
+                    epi_pair<uint16_t, EPI>(p, r0b + li, r0b + li, r1b + li, sel, m, acc[t][0][r], acc[t][1][r]);
+                } else {
+                    epi_row<uint16_t, EPI>(p, r0b + li, sel, m, acc[t][0][r], ssv[r], best_v[t][r], best_i[t][r]);
+                }
+            }
+            if constexpr (epi_has_ss(EPI)) {
+                // one unit per workgroup: partial index = unit within its set member
+                if (p.n_norm_sel > 0 && (EPI == EPI_RESID_ADD || p.par_mlp || sel == 0)) {
+                    const int si = (EPI == EPI_ATTN_OUT && p.par_mlp) ? sel : 0;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float s = group16_sum(ssv[r]);
+                        const int m = t * 16 + 4 * lg + r;
+                        if (li == 0 && m < p.M)
+                            p.ss[(int64_t)si * p.ss_sel_stride + (int64_t)(p.m0 + m) * ups + (u - sel * ups)] = s;
+                    }
+                }
             }
         }
-        __syncthreads();
-        constexpr int EPR = kSingle ? 8 : 16;   // epilogue elements per activation row
-        for (int e = threadIdx.x; e < p.M * EPR; e += blockDim.x) {
-            const int m = e / EPR, j = e % EPR;
-            const float y0 = tile[0][m][j];
-            const float y1 = kSingle ? tile[0][m][j + 8] : tile[1][m][j];
-            epilogue<uint16_t, kLogits>(p, r0 + j, r0 + j, r1 + j, sel, m, y0, y1, best_v, best_i, ss);
-        }
-        __syncthreads();
     }
-
-    // block partials: thread e < EPR M always handled activation row e / EPR
-    // (the launch guarantees blockDim >= 16 M)
-    constexpr int EPR = kSingle ? 8 : 16;
-    const bool norm = p.n_norm_sel > 0;
-    const bool logits = p.epi == EPI_LOGITS;
-    if (!norm && !logits) return;
-    __shared__ float sbv[MT * 16][16];
-    __shared__ int sbi[MT * 16][16];
-    __shared__ float sss[kMaxSel][MT * 16][16];
-    const int e = threadIdx.x;
-    if (e < p.M * EPR) {
-        sbv[e / EPR][e % EPR] = best_v;
-        sbi[e / EPR][e % EPR] = best_i;
+    if constexpr (EPI == EPI_LOGITS) {
+        if (part != 0) return;
 #pragma unroll
-        for (int s = 0; s < kMaxSel; ++s) sss[s][e / EPR][e % EPR] = ss[s];
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v = best_v[t][r];
+                int i = best_i[t][r];
+                group16_argmax(v, i);
+                const int m = t * 16 + 4 * lg + r;
+                if (li == 0 && m < p.M) {
+                    p.part_val[(int64_t)(p.m0 + m) * gridDim.x + blockIdx.x] = v;
+                    p.part_idx[(int64_t)(p.m0 + m) * gridDim.x + blockIdx.x] = i;
+                }
+            }
     }
-    __syncthreads();
-    if (e < p.M) {
-        if (logits) {
-            float v = sbv[e][0];
-            int i = sbi[e][0];
-            for (int j = 1; j < EPR; ++j) argmax_merge(v, i, sbv[e][j], sbi[e][j]);
-            p.part_val[(int64_t)(p.m0 + e) * gridDim.x + blockIdx.x] = v;
-            p.part_idx[(int64_t)(p.m0 + e) * gridDim.x + blockIdx.x] = i;
-        }
-        for (int s = 0; s < p.n_norm_sel; ++s) {
-            float t = sss[s][e][0];
-            for (int j = 1; j < EPR; ++j) t += sss[s][e][j];
-            p.ss[(int64_t)s * p.ss_sel_stride + (int64_t)(p.m0 + e) * gridDim.x + blockIdx.x] = t;
-        }
+}
+
+template <int MT, int EPI>
+void launch_epi(const GemvParams &p, dim3 g, int ks, int ups, hipStream_t s) {
+    if (ks == 4) hipLaunchKernelGGL((k_gemm_mfma<MT, EPI, 4>), g, dim3(256), 0, s, p, ups);
+    else if (ks == 8) hipLaunchKernelGGL((k_gemm_mfma<MT, EPI, 8>), g, dim3(512), 0, s, p, ups);
+    else if constexpr (!epi_is_pair(EPI)) hipLaunchKernelGGL((k_gemm_mfma<MT, EPI, 16>), g, dim3(1024), 0, s, p, ups);
+}
+
+template <int MT>
+hipError_t launch_mt(const GemvParams &p, dim3 g, int ks, int ups, hipStream_t s) {
+    switch (p.epi) {
+    case EPI_STORE: launch_epi<MT, EPI_STORE>(p, g, ks, ups, s); break;
+    case EPI_QKV_ROPE: launch_epi<MT, EPI_QKV_ROPE>(p, g, ks, ups, s); break;
+    case EPI_SILU_MUL: launch_epi<MT, EPI_SILU_MUL>(p, g, ks, ups, s); break;
+    case EPI_RESID_ADD: launch_epi<MT, EPI_RESID_ADD>(p, g, ks, ups, s); break;
+    case EPI_LOGITS: launch_epi<MT, EPI_LOGITS>(p, g, ks, ups, s); break;
+    case EPI_ATTN_OUT: launch_epi<MT, EPI_ATTN_OUT>(p, g, ks, ups, s); break;
+    default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
 }
 
 }  // namespace
 
 int gemm_mfma_max_rows() { return 32; }
 
-int gemm_mfma_grid(int n_units) { return n_units < kMaxGridM ? (n_units < 1 ? 1 : n_units) : kMaxGridM; }
+// One unit per workgroup, except sampling products, which keep a fixed grid
+// (their arg-max partials are per workgroup).
+int gemm_mfma_grid(const GemvParams &p) {
+    const int n = p.n_units < 1 ? 1 : p.n_units;
+    return p.epi == EPI_LOGITS && n > kLogitGrid ? kLogitGrid : n;
+}
 
-// K splits so that a launch has about 8K waves in flight, at least two
-// 64-element chunks per wave.
-int gemm_mfma_splits(int n_units, int K, bool single) {
-    const int per_ks = single ? 2 : 1;     // K parts per unit and KS step
-    int ks = 1;
-    while (ks < kMaxKS && (int64_t)n_units * 2 * ks < 8192 && (K >> 6) >= 4 * ks * per_ks) ks *= 2;
+// Waves per workgroup (4, 8 or 16; 8 at most for paired units, whose LDS
+// tiles are twice as tall): enough for about 3K waves per launch while every
+// wave keeps at least one tile.
+int gemm_mfma_splits(const GemvParams &p) {
+    const int B = epi_is_pair(p.epi) ? 2 : 1;
+    const int ntile = (p.K + kTK - 1) / kTK;
+    int ks = 4;
+    while (ks < kMaxKS / B && (int64_t)p.n_units * ks < 3072 && ks * 2 <= ntile) ks *= 2;
     return ks;
 }
 
 bool gemm_mfma_supported(const GemvParams &p) {
-    return (p.K % 64) == 0 && (p.pair_block == 2 || (p.pair_block % 32) == 0) && p.M >= 1 && p.M <= 32;
+    if (p.K % 32 != 0 || p.M < 1 || p.M > 32 || p.rows_per_sel % 16 != 0) return false;
+    if (epi_is_pair(p.epi)) return p.pair_block % 32 == 0;
+    return true;
 }
 
-template <int MT, bool kSingle>
-void launch_mt(const GemvParams &p, dim3 g, dim3 b, int ks, hipStream_t s) {
-    if (p.epi == EPI_LOGITS) hipLaunchKernelGGL((k_gemm_mfma<MT, true, kSingle>), g, b, 0, s, p, ks);
-    else hipLaunchKernelGGL((k_gemm_mfma<MT, false, kSingle>), g, b, 0, s, p, ks);
-}
-
-// single: units are single 16-row blocks (adjacent-row products)
-hipError_t launch_gemm_mfma(const GemvParams &p, int grid, int ks, bool single, hipStream_t s) {
-    while (128 * ks < 16 * p.M) ks *= 2;   // one epilogue element per thread
-    dim3 g(grid), b(128 * ks);
-    if (p.M <= 16) {
-        if (single) launch_mt<1, true>(p, g, b, ks, s);
-        else launch_mt<1, false>(p, g, b, ks, s);
-    } else {
-        if (single) launch_mt<2, true>(p, g, b, ks, s);
-        else launch_mt<2, false>(p, g, b, ks, s);
-    }
-    return hipGetLastError();
+hipError_t launch_gemm_mfma(const GemvParams &p, int grid, int ks, hipStream_t s) {
+    if ((ks != 4 && ks != 8 && ks != 16) || (epi_is_pair(p.epi) && ks > kMaxKS / 2)) return hipErrorInvalidValue;
+    // partial index of a residual writer: the unit within its set member
+    const int ups = p.rows_per_sel / 16;
+    if (epi_has_ss(p.epi) && p.n_norm_sel > 0 && grid != p.n_units) return hipErrorInvalidValue;
+    if (p.M <= 16) return launch_mt<1>(p, dim3(grid), ks, ups, s);
+    return launch_mt<2>(p, dim3(grid), ks, ups, s);
 }
 
 }  // namespace spec

@@ -22,160 +22,288 @@ constexpr int kMaxRows = 8;        // activation rows per launch
 constexpr int kMaxGrid = 256 * 8;  // workgroups (8 per CU)
 constexpr int kUnroll = 4;
 
-template <typename T, int E>
-__device__ __forceinline__ void load_x(const GemvParams &p, const T *xplain, int sel, int m, int hrow, float inv,
-                                       int k, float *fx) {
-    if (p.xmode == X_PLAIN) {
-        Store<T>::unpack(ld16(xplain + (int64_t)m * p.K + k), fx);
-    } else {
-        if constexpr (E == 8) x_norm8(p, sel, hrow, k, inv, fx);
-        else x_norm4(p, sel, hrow, k, inv, fx);
-#pragma unroll
-        for (int e = 0; e < E; ++e) fx[e] = Store<T>::round(fx[e]);
-    }
-}
+// A workgroup's four waves take 4 / KS units at a time; the KS waves of a
+// unit (a row pair) each stream a contiguous, step-aligned part of K, and
+// their partial dot products meet in LDS and are summed in part order by the
+// unit's first wave, which runs the epilogue.  Per chunk of kUnroll 16-byte
+// steps the weights are requested first, then the activation operands, and
+// every load of a chunk is in flight before the arithmetic starts.
+//
+// Normalised operands: every wave forms the rows' 1/rms from the residual
+// writers' partials (summed in partial order, so all waves agree bit for
+// bit).  When the normalised rows of all set members fit in kStageBytes of
+// LDS, the workgroup writes them there once (rounded to the activation type)
+// and the units read them from LDS; the first chunk of weights is requested
+// before, so the staging overlaps the weight stream.  Otherwise each step
+// normalises its own operands.
+constexpr int kStageBytes = 32768;
 
-template <typename T, int MR, bool kLogits>
-__global__ __launch_bounds__(256) void k_gemv(GemvParams p) {
+enum : int { XM_PLAIN = 0, XM_STAGED = 1, XM_DIRECT = 2 };
+
+template <typename T, int MR, int EPI, int XM>
+__global__ __launch_bounds__(256) void k_gemv(GemvParams p, int KS) {
     using S = Store<T>;
+    constexpr bool kNorm = XM != XM_PLAIN;
+    constexpr bool staged = XM == XM_STAGED;
     constexpr int E = S::kPer16;
+    constexpr bool kPair = epi_is_pair(EPI);
+    __shared__ __align__(16) T xs[staged ? kStageBytes / sizeof(T) : 8];
+    __shared__ float red[kWaves][kMaxRows][2];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    const int upb = kWaves / KS;                 // units per workgroup and round
+    const int slot = wave / KS, part = wave - slot * KS;
     const int K = p.K;
     const int step = kWave * E;
+    const int chunk = kUnroll * step;
+    const int nsteps = (K + step - 1) / step;
+    const int sper = (nsteps + KS - 1) / KS;
+    const int kb = min(K, part * sper * step), ke = min(K, (part + 1) * sper * step);
     const int half = p.pair_block >> 1;
+    const int n_sel = (p.n_units * 2) / p.rows_per_sel;
     float best_v = -INFINITY;
     int best_i = 0x7FFFFFFF;
     float ss[kMaxSel];
 #pragma unroll
     for (int s = 0; s < kMaxSel; ++s) ss[s] = 0.f;
-    __shared__ float inv_s[kMaxRows];
-    block_inv_rms(p, inv_s);
-
-    for (int u = blockIdx.x * kWaves + wave; u < p.n_units; u += gridDim.x * kWaves) {
-        const int blk = u / half;
-        const int j = u - blk * half;
-        const int r0 = blk * p.pair_block + j;
-        const int r1 = r0 + half;
-        const int sel = r0 / p.rows_per_sel;
-        const T *w0 = reinterpret_cast<const T *>(p.W) + (int64_t)r0 * K;
-        const T *w1 = reinterpret_cast<const T *>(p.W) + (int64_t)r1 * K;
-        const T *xp = reinterpret_cast<const T *>(p.X) + (int64_t)sel * p.x_sel_stride + (int64_t)p.m0 * K;
-        int hrow[MR];
-        float inv[MR];
+    float inv[MR];
+    int hrow[MR];
 #pragma unroll
-        for (int m = 0; m < MR; ++m) {
-            hrow[m] = 0;
-            inv[m] = 0.f;
-            if (p.xmode == X_NORM && m < p.M) {
-                hrow[m] = x_row(p, p.m0 + m);
-                inv[m] = inv_s[m];
+    for (int m = 0; m < MR; ++m) { inv[m] = 0.f; hrow[m] = 0; }
+
+    auto unit_rows = [&](int u, int &r0, int &r1, int &sel) {
+        const int blk = u / half, j = u - blk * half;
+        r0 = blk * p.pair_block + j;
+        r1 = r0 + half;
+        sel = r0 / p.rows_per_sel;
+    };
+    auto load_w = [&](const T *w0, const T *w1, int k0, uint4 (&wa)[kUnroll], uint4 (&wb)[kUnroll]) {
+#pragma unroll
+        for (int q = 0; q < kUnroll; ++q) {
+            const int k = k0 + q * step + lane * E;
+            wa[q] = make_uint4(0, 0, 0, 0);
+            wb[q] = make_uint4(0, 0, 0, 0);
+            if (k < ke) {
+                wa[q] = ld16_stream(w0 + k);
+                wb[q] = ld16_stream(w1 + k);
             }
         }
-        float a0[MR], a1[MR];
-#pragma unroll
-        for (int m = 0; m < MR; ++m) { a0[m] = 0.f; a1[m] = 0.f; }
+    };
 
-        int k = lane * E;
-        for (; k + (kUnroll - 1) * step < K; k += kUnroll * step) {
-            uint4 wa[kUnroll], wb[kUnroll];
+    // first chunk of the wave's first unit, requested before the norm work
+    // (the chunk loop finds it in wa / wb)
+    uint4 wa[kUnroll], wb[kUnroll];
+    bool have_pf = false;
+    if (kNorm && blockIdx.x * upb + slot < p.n_units && kb < ke) {
+        int r0, r1, sel;
+        unit_rows(blockIdx.x * upb + slot, r0, r1, sel);
+        load_w(reinterpret_cast<const T *>(p.W) + (int64_t)r0 * K, reinterpret_cast<const T *>(p.W) + (int64_t)r1 * K,
+               kb, wa, wb);
+        have_pf = true;
+    }
+    if constexpr (kNorm) {
 #pragma unroll
-            for (int q = 0; q < kUnroll; ++q) {
-                wa[q] = ld16_stream(w0 + k + q * step);
-                wb[q] = ld16_stream(w1 + k + q * step);
+        for (int m = 0; m < MR; ++m) {
+            if (m < p.M) {
+                hrow[m] = x_row(p, p.m0 + m);
+                inv[m] = row_inv_rms(p, hrow[m]);
             }
-#pragma unroll
-            for (int q = 0; q < kUnroll; ++q) {
-                float fa[E], fb[E];
-                S::unpack(wa[q], fa);
-                S::unpack(wb[q], fb);
+        }
+        if constexpr (staged) {
+            for (int sel = 0; sel < n_sel; ++sel)
 #pragma unroll
                 for (int m = 0; m < MR; ++m) {
-                    if (m < p.M) {
-                        float fx[E];
-                        load_x<T, E>(p, xp, sel, m, hrow[m], inv[m], k + q * step, fx);
+                    if (m >= p.M) continue;
+                    for (int k = threadIdx.x * E; k < K; k += 256 * E) {
+                        float f[E];
+                        if constexpr (E == 8) x_norm8(p, sel, hrow[m], k, inv[m], f);
+                        else x_norm4(p, sel, hrow[m], k, inv[m], f);
 #pragma unroll
-                        for (int e = 0; e < E; ++e) {
-                            a0[m] = fmaf(fa[e], fx[e], a0[m]);
-                            a1[m] = fmaf(fb[e], fx[e], a1[m]);
+                        for (int e = 0; e < E; ++e) xs[(sel * MR + m) * K + k + e] = S::from_f32(f[e]);
+                    }
+                }
+            __syncthreads();
+        }
+    }
+
+    for (int ub = blockIdx.x * upb; ub < p.n_units; ub += gridDim.x * upb) {
+        const int u = ub + slot;
+        const bool active = u < p.n_units;
+        float y0 = 0.f, y1 = 0.f;
+        int r0 = 0, r1 = 0, sel = 0;
+        if (active) {
+            unit_rows(u, r0, r1, sel);
+            const T *w0 = reinterpret_cast<const T *>(p.W) + (int64_t)r0 * K;
+            const T *w1 = reinterpret_cast<const T *>(p.W) + (int64_t)r1 * K;
+            const T *xp = reinterpret_cast<const T *>(p.X) + (int64_t)sel * p.x_sel_stride + (int64_t)p.m0 * K;
+            const T *xl = xs + (int64_t)sel * MR * K;
+            float a0[MR], a1[MR];
+#pragma unroll
+            for (int m = 0; m < MR; ++m) { a0[m] = 0.f; a1[m] = 0.f; }
+            for (int k0 = kb; k0 < ke; k0 += chunk) {
+                if (!have_pf) load_w(w0, w1, k0, wa, wb);
+                have_pf = false;
+                // activation operands of the chunk (zero past the part's end)
+                float xo[kUnroll][MR][E];
+#pragma unroll
+                for (int q = 0; q < kUnroll; ++q) {
+                    const int k = k0 + q * step + lane * E;
+#pragma unroll
+                    for (int m = 0; m < MR; ++m) {
+#pragma unroll
+                        for (int e = 0; e < E; ++e) xo[q][m][e] = 0.f;
+                        if (m >= p.M || k >= ke) continue;
+                        if constexpr (!kNorm) {
+                            S::unpack(ld16(xp + (int64_t)m * K + k), xo[q][m]);
+                        } else if constexpr (staged) {
+                            S::unpack(*reinterpret_cast<const uint4 *>(xl + m * K + k), xo[q][m]);
+                        } else {
+                            if constexpr (E == 8) x_norm8(p, sel, hrow[m], k, inv[m], xo[q][m]);
+                            else x_norm4(p, sel, hrow[m], k, inv[m], xo[q][m]);
+#pragma unroll
+                            for (int e = 0; e < E; ++e) xo[q][m][e] = S::round(xo[q][m][e]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < kUnroll; ++q) {
+                    float fa[E], fb[E];
+                    S::unpack(wa[q], fa);
+                    S::unpack(wb[q], fb);
+#pragma unroll
+                    for (int m = 0; m < MR; ++m) {
+                        if (m < p.M) {
+#pragma unroll
+                            for (int e = 0; e < E; ++e) {
+                                a0[m] = fmaf(fa[e], xo[q][m][e], a0[m]);
+                                a1[m] = fmaf(fb[e], xo[q][m][e], a1[m]);
+                            }
                         }
                     }
                 }
             }
-        }
-        for (; k < K; k += step) {
-            float fa[E], fb[E];
-            S::unpack(ld16_stream(w0 + k), fa);
-            S::unpack(ld16_stream(w1 + k), fb);
 #pragma unroll
             for (int m = 0; m < MR; ++m) {
                 if (m < p.M) {
-                    float fx[E];
-                    load_x<T, E>(p, xp, sel, m, hrow[m], inv[m], k, fx);
-#pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        a0[m] = fmaf(fa[e], fx[e], a0[m]);
-                        a1[m] = fmaf(fb[e], fx[e], a1[m]);
-                    }
+                    const float s0 = wave_sum(a0[m]);
+                    const float s1 = wave_sum(a1[m]);
+                    if (lane == m) { y0 = s0; y1 = s1; }
                 }
             }
         }
-        float y0 = 0.f, y1 = 0.f;
-#pragma unroll
-        for (int m = 0; m < MR; ++m) {
-            if (m < p.M) {
-                const float s0 = wave_sum(a0[m]);
-                const float s1 = wave_sum(a1[m]);
-                if (lane == m) { y0 = s0; y1 = s1; }
+        if (KS > 1) {
+            if (lane < p.M) {
+                red[wave][lane][0] = y0;
+                red[wave][lane][1] = y1;
+            }
+            __syncthreads();
+            if (part == 0 && lane < p.M) {
+                for (int q = 1; q < KS; ++q) {
+                    y0 += red[wave + q][lane][0];
+                    y1 += red[wave + q][lane][1];
+                }
+            }
+            __syncthreads();
+        }
+        if (active && part == 0 && lane < p.M) {
+            if constexpr (kPair) {
+                epi_pair<T, EPI>(p, u, r0, r1, sel, lane, y0, y1);
+            } else if constexpr (EPI == EPI_LOGITS) {
+                epi_logits2<T>(p, r0, r1, lane, y0, y1, best_v, best_i);
+            } else {
+                float t = 0.f;
+                epi_row<T, EPI>(p, r0, sel, lane, y0, t, best_v, best_i);
+                epi_row<T, EPI>(p, r1, sel, lane, y1, t, best_v, best_i);
+                if constexpr (epi_has_ss(EPI)) add_sel(ss, (EPI == EPI_ATTN_OUT && p.par_mlp) ? sel : 0, t);
             }
         }
-        if (lane < p.M) epilogue<T, kLogits>(p, u, r0, r1, sel, lane, y0, y1, best_v, best_i, ss);
     }
 
-    const bool norm = p.n_norm_sel > 0;
-    const bool logits = p.epi == EPI_LOGITS;
-    if (!norm && !logits) return;
-    // block partials: lane m of every wave holds row m's contribution
-    __shared__ float sv[kWaves][kMaxRows];
-    __shared__ int si[kWaves][kMaxRows];
-    __shared__ float sss[kWaves][kMaxSel][kMaxRows];
-    if (lane < p.M) {
-        sv[wave][lane] = best_v;
-        si[wave][lane] = best_i;
+    if constexpr (epi_has_ss(EPI) || EPI == EPI_LOGITS) {
+        // block partials: lane m of every wave holds row m's contribution
+        // (waves with part > 0 hold neutral values)
+        __shared__ float sv[kWaves][kMaxRows];
+        __shared__ int si[kWaves][kMaxRows];
+        __shared__ float sss[kWaves][kMaxSel][kMaxRows];
+        if (lane < p.M) {
+            sv[wave][lane] = best_v;
+            si[wave][lane] = best_i;
 #pragma unroll
-        for (int s = 0; s < kMaxSel; ++s) sss[wave][s][lane] = ss[s];
-    }
-    __syncthreads();
-    if (threadIdx.x < p.M) {
-        const int m = threadIdx.x;
-        if (logits) {
-            float v = sv[0][m];
-            int i = si[0][m];
-            for (int w = 1; w < kWaves; ++w) argmax_merge(v, i, sv[w][m], si[w][m]);
-            p.part_val[(int64_t)(p.m0 + m) * gridDim.x + blockIdx.x] = v;
-            p.part_idx[(int64_t)(p.m0 + m) * gridDim.x + blockIdx.x] = i;
+            for (int s = 0; s < kMaxSel; ++s) sss[wave][s][lane] = ss[s];
         }
-        for (int s = 0; s < p.n_norm_sel; ++s) {
-            float t = sss[0][s][m];
-            for (int w = 1; w < kWaves; ++w) t += sss[w][s][m];
-            p.ss[(int64_t)s * p.ss_sel_stride + (int64_t)(p.m0 + m) * gridDim.x + blockIdx.x] = t;
+        __syncthreads();
+        if (threadIdx.x < p.M) {
+            const int m = threadIdx.x;
+            if constexpr (EPI == EPI_LOGITS) {
+                float v = sv[0][m];
+                int i = si[0][m];
+                for (int w = 1; w < kWaves; ++w) argmax_merge(v, i, sv[w][m], si[w][m]);
+                p.part_val[(int64_t)(p.m0 + m) * gridDim.x + blockIdx.x] = v;
+                p.part_idx[(int64_t)(p.m0 + m) * gridDim.x + blockIdx.x] = i;
+            } else {
+                for (int s = 0; s < p.n_norm_sel; ++s) {
+                    float t = sss[0][s][m];
+                    for (int w = 1; w < kWaves; ++w) t += sss[w][s][m];
+                    p.ss[(int64_t)s * p.ss_sel_stride + (int64_t)(p.m0 + m) * gridDim.x + blockIdx.x] = t;
+                }
+            }
         }
     }
 }
 
-template <typename T, bool kLogits>
-hipError_t launch_tl(const GemvParams &p, int grid, hipStream_t s) {
+template <typename T, int EPI, int XM>
+void launch_tex(const GemvParams &p, int grid, int ks, hipStream_t s) {
     dim3 g(grid), b(256);
-    if (p.M <= 1) hipLaunchKernelGGL((k_gemv<T, 1, kLogits>), g, b, 0, s, p);
-    else if (p.M <= 2) hipLaunchKernelGGL((k_gemv<T, 2, kLogits>), g, b, 0, s, p);
-    else if (p.M <= 4) hipLaunchKernelGGL((k_gemv<T, 4, kLogits>), g, b, 0, s, p);
-    else hipLaunchKernelGGL((k_gemv<T, 8, kLogits>), g, b, 0, s, p);
-    return hipGetLastError();
+    if (p.M <= 1) hipLaunchKernelGGL((k_gemv<T, 1, EPI, XM>), g, b, 0, s, p, ks);
+    else if (p.M <= 2) hipLaunchKernelGGL((k_gemv<T, 2, EPI, XM>), g, b, 0, s, p, ks);
+    else if (p.M <= 4) hipLaunchKernelGGL((k_gemv<T, 4, EPI, XM>), g, b, 0, s, p, ks);
+    else hipLaunchKernelGGL((k_gemv<T, 8, EPI, XM>), g, b, 0, s, p, ks);
 }
 
+// normalised operands go through LDS when every set member's rows fit
 template <typename T>
-hipError_t launch_t(const GemvParams &p, int grid, hipStream_t s) {
-    return p.epi == EPI_LOGITS ? launch_tl<T, true>(p, grid, s) : launch_tl<T, false>(p, grid, s);
+bool gemv_staged(const GemvParams &p) {
+    const int mr = p.M <= 1 ? 1 : (p.M <= 2 ? 2 : (p.M <= 4 ? 4 : 8));
+    const int64_t n_sel = (int64_t)p.n_units * 2 / p.rows_per_sel;
+    return n_sel * mr * p.K * (int64_t)sizeof(T) <= kStageBytes;
+}
+
+template <typename T, int EPI>
+void launch_ten(const GemvParams &p, int grid, int ks, bool norm, hipStream_t s) {
+    if (!norm) launch_tex<T, EPI, XM_PLAIN>(p, grid, ks, s);
+    else if (gemv_staged<T>(p)) launch_tex<T, EPI, XM_STAGED>(p, grid, ks, s);
+    else launch_tex<T, EPI, XM_DIRECT>(p, grid, ks, s);
+}
+
+// The decoder's products: QKV, gate/up and the head read normalised
+// residual rows, the others plain activation rows.
+template <typename T>
+hipError_t launch_t(const GemvParams &p, int grid, int ks, hipStream_t s) {
+    const bool nrm = p.xmode == X_NORM;
+    switch (p.epi) {
+    case EPI_STORE:
+        launch_ten<T, EPI_STORE>(p, grid, ks, nrm, s);
+        break;
+    case EPI_QKV_ROPE:
+        launch_ten<T, EPI_QKV_ROPE>(p, grid, ks, nrm, s);
+        break;
+    case EPI_SILU_MUL:
+        launch_ten<T, EPI_SILU_MUL>(p, grid, ks, nrm, s);
+        break;
+    case EPI_RESID_ADD:
+        if (nrm) return hipErrorInvalidValue;
+        launch_tex<T, EPI_RESID_ADD, XM_PLAIN>(p, grid, ks, s);
+        break;
+    case EPI_LOGITS:
+        launch_ten<T, EPI_LOGITS>(p, grid, ks, nrm, s);
+        break;
+    case EPI_ATTN_OUT:
+        if (nrm) return hipErrorInvalidValue;
+        launch_tex<T, EPI_ATTN_OUT, XM_PLAIN>(p, grid, ks, s);
+        break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ norm
@@ -186,13 +314,8 @@ hipError_t launch_t(const GemvParams &p, int grid, hipStream_t s) {
 template <typename T>
 __global__ __launch_bounds__(256) void k_norm_rows(GemvParams p, void *xn) {
     const int m = blockIdx.y, sel = blockIdx.z;
-    const int lane = threadIdx.x & 63;
     const int hrow = x_row(p, p.m0 + m);
-    const float *src = p.xss + (int64_t)hrow * p.xnparts;
-    float s = 0.f;
-    for (int i = lane; i < p.xnparts; i += 64) s += src[i];
-    s = wave_sum(s);
-    const float inv = 1.0f / sqrtf(s / (float)p.K + p.eps);
+    const float inv = row_inv_rms(p, hrow);
     const int k = (blockIdx.x * 256 + threadIdx.x) * 8;
     if (k >= p.K) return;
     float f[8];
@@ -261,13 +384,28 @@ __global__ __launch_bounds__(256) void k_embed(EmbedParams p) {
 
 int gemv_max_rows() { return kMaxRows; }
 
-int gemv_grid(int n_units) {
-    int g = (n_units + kWaves - 1) / kWaves;
-    return g < kMaxGrid ? (g < 1 ? 1 : g) : kMaxGrid;
+// Waves per unit: split K while the launch has fewer than 4096 waves and each
+// part keeps at least one 16-byte step per lane.
+int gemv_splits(const GemvParams &p, int elem_bytes) {
+    const int step = kWave * 16 / elem_bytes;
+    int ks = 1;
+    while (ks < kWaves && (int64_t)p.n_units * ks < 4096 && p.K >= 2 * ks * step) ks *= 2;
+    return ks;
 }
 
-hipError_t launch_gemv(int dtype, const GemvParams &p, int grid, hipStream_t s) {
-    return dtype ? launch_t<uint16_t>(p, grid, s) : launch_t<float>(p, grid, s);
+// Workgroups: every unit once, at most kMaxGrid; normalised-operand launches
+// keep about three workgroups per CU so that each stages its operand once
+// for several units.
+int gemv_grid(const GemvParams &p, int ks) {
+    const int upb = kWaves / ks;
+    int g = (p.n_units + upb - 1) / upb;
+    const int cap = p.xmode == X_NORM ? 3 * 256 : kMaxGrid;
+    return g < cap ? (g < 1 ? 1 : g) : cap;
+}
+
+hipError_t launch_gemv(int dtype, const GemvParams &p, int grid, int ks, hipStream_t s) {
+    if (ks != 1 && ks != 2 && ks != 4) return hipErrorInvalidValue;
+    return dtype ? launch_t<uint16_t>(p, grid, ks, s) : launch_t<float>(p, grid, ks, s);
 }
 
 hipError_t launch_norm_rows(int dtype, const GemvParams &p, int n_sel, void *xn, hipStream_t s) {

@@ -94,15 +94,15 @@ struct ProfScope {
     }
 };
 
-std::string gemv_name(int dtype, int M, bool logits) {
+std::string gemv_name(int dtype, int M, int epi) {
     const int mr = M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : 8));
     return std::string("k_gemv<") + (dtype ? "unsigned short" : "float") + ", " + std::to_string(mr) + ", " +
-           (logits ? "true" : "false") + ">";
+           std::to_string(epi) + ">";
 }
 
-std::string mfma_name(int M, bool logits, bool single) {
-    return std::string("k_gemm_mfma<") + (M <= 16 ? "1" : "2") + ", " + (logits ? "true" : "false") + ", " +
-           (single ? "true" : "false") + ">";
+std::string mfma_name(int M, int epi, int ks) {
+    return std::string("k_gemm_mfma<") + (M <= 16 ? "1" : "2") + ", " + std::to_string(epi) + ", " +
+           std::to_string(ks) + ">";
 }
 
 // Workspace layout for R activation rows and sets of at most G layers.
@@ -170,64 +170,61 @@ int mfma_min_rows() {
 }
 
 // Weight-streaming product over the call's p.Mtot activation rows, chunked by
-// the kernel's row limit.  *grid_out: the grid of the launches (= partials
-// per row of its sum-of-squares or sampling output).
-hipError_t product(const Fwd &f, GemvParams p, int *grid_out = nullptr) {
+// the kernel's row limit.  *parts_out: the sum-of-squares or sampling
+// partials each output row now has.
+hipError_t product(const Fwd &f, GemvParams p, int *parts_out = nullptr) {
     const spec_model *m = f.m;
     const int Mtot = p.Mtot;
     p.ss = at<float>(f.ws, f.c.ss);
     p.ss_sel_stride = f.c.ss_sel_stride;
     p.part_val = at<float>(f.ws, f.c.pval);
     p.part_idx = at<int32_t>(f.ws, f.c.pidx);
+    const bool pair = p.epi == EPI_QKV_ROPE || p.epi == EPI_SILU_MUL;
+    const int rows = p.n_units * 2;
     GemvParams q = p;
-    q.pair_block = p.pair_block == 2 ? 32 : p.pair_block;   // adjacent rows -> adjacent 16-row blocks
+    q.n_units = pair ? rows / 32 : rows / 16;   // 16-row blocks (pairs of them for paired epilogues)
     q.M = Mtot < 32 ? Mtot : 32;
-    const bool mfma = m->d.dtype == SPEC_BF16 && Mtot >= mfma_min_rows() && gemm_mfma_supported(q) &&
-                      (p.n_units * 2) % 32 == 0;
-    const double wbytes = (double)p.n_units * 2 * p.K * m->xs;   // every weight row once
+    const bool mfma = m->d.dtype == SPEC_BF16 && Mtot >= mfma_min_rows() && rows % (pair ? 32 : 16) == 0 &&
+                      gemm_mfma_supported(q);
+    const double wbytes = (double)rows * p.K * m->xs;   // every weight row once
     if (mfma) {
-        const bool single = p.pair_block == 2;
-        q.n_units = single ? p.n_units / 8 : p.n_units / 16;   // row pairs -> 16-row units
-        const int grid = gemm_mfma_grid(q.n_units);
-        const int ks = gemm_mfma_splits(q.n_units, p.K, single);
-        if (grid_out) *grid_out = grid;
+        const int grid = gemm_mfma_grid(q);
+        const int ks = gemm_mfma_splits(q);
+        if (parts_out) *parts_out = (p.epi == EPI_LOGITS) ? grid : p.rows_per_sel / 16;
         const int mr = gemm_mfma_max_rows();
         for (int m0 = 0; m0 < Mtot; m0 += mr) {
             q.m0 = m0;
             q.M = (Mtot - m0) < mr ? (Mtot - m0) : mr;
+            GemvParams r = q;
+            double xbytes = (double)q.M * p.K * m->xs;
             if (p.xmode == X_NORM) {
                 // normalise once into xn, then stream the weights against it
-                const int n_sel = (p.n_units * 2) / p.rows_per_sel;
+                const int n_sel = rows / p.rows_per_sel;
                 void *xn = at<char>(f.ws, f.c.xn);
                 hipError_t e = launch_norm_rows(m->d.dtype, q, n_sel, xn, f.s);
                 if (e != hipSuccess) return e;
-                GemvParams r = q;
                 r.xmode = X_PLAIN;
                 r.X = xn;   // rows (sel * Mtot + m0 + m); the kernel adds m0 * K
                 r.x_sel_stride = (int64_t)Mtot * p.K;
-                ProfScope ps(f.s);
-                e = launch_gemm_mfma(r, grid, ks, single, f.s);
-                ps.done(mfma_name(q.M, p.epi == EPI_LOGITS, single), wbytes + (double)q.M * p.K * m->xs * n_sel);
-                if (e != hipSuccess) return e;
-                continue;
+                xbytes *= n_sel;
             }
             ProfScope ps(f.s);
-            hipError_t e = launch_gemm_mfma(q, grid, ks, single, f.s);
-            ps.done(mfma_name(q.M, p.epi == EPI_LOGITS, single), wbytes + (double)q.M * p.K * m->xs);
+            hipError_t e = launch_gemm_mfma(r, grid, ks, f.s);
+            ps.done(mfma_name(q.M, p.epi, ks), wbytes + xbytes);
             if (e != hipSuccess) return e;
         }
         return hipSuccess;
     }
     const int mr = gemv_max_rows();
-    const int grid = gemv_grid(p.n_units);
-    if (grid_out) *grid_out = grid;
+    const int ks = gemv_splits(p, m->xs);
+    const int grid = gemv_grid(p, ks);
+    if (parts_out) *parts_out = grid;
     for (int m0 = 0; m0 < Mtot; m0 += mr) {
         p.m0 = m0;
         p.M = (Mtot - m0) < mr ? (Mtot - m0) : mr;
         ProfScope ps(f.s);
-        hipError_t e = launch_gemv(m->d.dtype, p, grid, f.s);
-        ps.done(gemv_name(m->d.dtype, p.M, p.epi == EPI_LOGITS),
-                wbytes + (double)p.M * p.K * (p.xmode == X_NORM ? 4 : m->xs));
+        hipError_t e = launch_gemv(m->d.dtype, p, grid, ks, f.s);
+        ps.done(gemv_name(m->d.dtype, p.M, p.epi), wbytes + (double)p.M * p.K * (p.xmode == X_NORM ? 4 : m->xs));
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

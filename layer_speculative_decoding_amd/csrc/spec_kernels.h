@@ -95,22 +95,26 @@ struct GemvParams {
 };
 
 // dtype: 0 float32, 1 bfloat16 (weights and activation buffers share it).
-// VALU GEMV: units are row pairs, M <= gemv_max_rows() per launch.
-hipError_t launch_gemv(int dtype, const GemvParams &p, int grid, hipStream_t s);
+// VALU GEMV: units are row pairs, M <= gemv_max_rows() per launch; ks waves
+// (1, 2 or 4) split each unit's K.
+hipError_t launch_gemv(int dtype, const GemvParams &p, int grid, int ks, hipStream_t s);
 int gemv_max_rows();
-int gemv_grid(int n_units);
-// MFMA skinny GEMM (bf16): units are pairs of 16-row blocks (n_units = rows /
-// 32), M <= 32 per launch, K a multiple of 64, pair_block a multiple of 32.
-// single: units are single 16-row blocks whose epilogue pairs rows (r, r + 8)
-// (products whose rows need no partner); otherwise pairs of 16-row blocks.
-hipError_t launch_gemm_mfma(const GemvParams &p, int grid, int ks, bool single, hipStream_t s);
+int gemv_splits(const GemvParams &p, int elem_bytes);
+int gemv_grid(const GemvParams &p, int ks);
+// MFMA skinny GEMM (bf16), M <= 32 per launch, K a multiple of 32.  Units:
+// pairs of 16-row blocks for the paired epilogues (QKV RoPE, SiLU; n_units =
+// rows / 32, pair_block a multiple of 32), single 16-row blocks otherwise
+// (n_units = rows / 16).  ks waves per workgroup (4, 8 or 16).  Residual
+// writers run one unit per workgroup and leave rows_per_sel / 16 partials
+// per row and set member.
+hipError_t launch_gemm_mfma(const GemvParams &p, int grid, int ks, hipStream_t s);
 // X_NORM operands written once as activation-dtype rows xn[sel][m][K] for
 // rows m0 .. m0 + M - 1 (the matrix-core products then read them plainly).
 hipError_t launch_norm_rows(int dtype, const GemvParams &p, int n_sel, void *xn, hipStream_t s);
 bool gemm_mfma_supported(const GemvParams &p);
 int gemm_mfma_max_rows();
-int gemm_mfma_grid(int n_units);
-int gemm_mfma_splits(int n_units, int K, bool single);
+int gemm_mfma_grid(const GemvParams &p);
+int gemm_mfma_splits(const GemvParams &p);
 
 // Embedding of every row (h = E[token]), its sum of squares (one partial),
 // and the RoPE (cos, sin) of its position.
