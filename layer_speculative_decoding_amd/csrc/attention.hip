@@ -368,8 +368,11 @@ int attention_split_max() { return kSplitMax; }
 
 // Key splits so that the workgroups of a call fill the GPU: about
 // kTargetWG workgroups, each split at least one round of the four waves.
+// Calls with more than 64 rows (prompt prefills) have many query blocks and
+// never split (the split partials are sized for 64 rows).
 int attention_splits(int n_group, int batch, int hq, int hkv, int mseq, int max_pos) {
     constexpr int kTargetWG = 512;
+    if ((long)batch * mseq > 64) return 1;
     const int G = hq / hkv;
     const int QB = 16 * qv_blocks(G, mseq) / G;
     const int nqb = (mseq + QB - 1) / QB;

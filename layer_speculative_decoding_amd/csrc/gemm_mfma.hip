@@ -9,17 +9,17 @@
 // the weight stream:
 //
 //  * A workgroup owns one unit: a 16-row block of W, or for paired epilogues
-//    (RoPE partners, gate/up) the two blocks r0 and r0 + pair_block/2, so the
-//    pair meets in the same lane's registers.  Its KS waves split K into
-//    contiguous ranges of 256-element tiles.
+//    (RoPE partners, gate/up) the two blocks r0 and r0 + pair_block/2.  KS
+//    waves per block split K into contiguous ranges of 256-element tiles.
 //  * Weights are read with whole-row coalescing: each 16-byte-per-lane load
 //    instruction covers two rows x 512 contiguous bytes.  The MFMA operand
 //    layout needs 16 rows x 64 bytes per instruction instead, which halves the
 //    bytes per memory request, so each wave stages its tile through a private
 //    LDS buffer (padded rows keep the operand reads conflict-free) and loads
 //    the next tile while the matrix cores consume the current one.
-//  * The KS partial tiles are summed in wave order through LDS; the first
-//    wave runs the epilogue straight from its accumulators.
+//  * The partial tiles are summed in wave order through LDS by the first
+//    wave, which then holds both blocks of a pair in the same lane layout
+//    and runs the epilogue straight from registers.
 #include "epilogue.h"
 #include "spec_device.h"
 #include "spec_kernels.h"
@@ -33,7 +33,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTK = 256;          // K elements per staged tile
 constexpr int kLD = kTK + 8;      // LDS row stride in elements (16 bytes of padding)
-constexpr int kMaxKS = 16;        // waves per workgroup
+constexpr int kMaxKS = 8;         // waves per 16-row block
 constexpr int kLogitGrid = 2048;  // workgroups of a sampling product (= arg-max partials per row)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &v) {
@@ -57,18 +57,22 @@ __device__ __forceinline__ void group16_argmax(float &v, int &i) {
     }
 }
 
-// MT: 16-row activation tiles (1: M <= 16, 2: M <= 32).  Paired epilogues
-// take two 16-row blocks per unit, the others one.  KS waves per workgroup.
+// MT: 16-row activation tiles (1: M <= 16, 2: M <= 32).  A unit has NB
+// 16-row blocks (2 for the paired epilogues, else 1); the workgroup runs KS
+// waves per block, wave w streaming block w / KS over K part w % KS.
 template <int MT, int EPI, int KS>
-__global__ __launch_bounds__(64 * KS) void k_gemm_mfma(GemvParams p, int ups) {
+__global__ __launch_bounds__(64 * KS * (epi_is_pair(EPI) ? 2 : 1)) void k_gemm_mfma(GemvParams p, int ups) {
     constexpr bool kPair = epi_is_pair(EPI);
-    constexpr int B = kPair ? 2 : 1;        // 16-row blocks per unit
-    constexpr int NL = 8 * B;               // 16-byte loads per lane per tile
-    __shared__ __align__(16) uint16_t smem[KS * 16 * B * kLD];
+    constexpr int NB = kPair ? 2 : 1;       // 16-row blocks per unit
+    constexpr int NW = NB * KS;             // waves per workgroup
+    constexpr int NL = 8;                   // 16-byte loads per lane per tile
+    constexpr int TILE = 16 * kLD;          // elements of one wave's LDS tile
+    __shared__ __align__(16) uint16_t smem[NW * TILE];
     const int lane = threadIdx.x & 63;
-    const int part = threadIdx.x >> 6;
+    const int wave = threadIdx.x >> 6;
+    const int blk = wave / KS, part = wave - blk * KS;
     const int li = lane & 15, lg = lane >> 4;
-    uint16_t *tile = smem + (size_t)part * (16 * B) * kLD;
+    uint16_t *tile = smem + (size_t)wave * TILE;
     const int K = p.K;
     const int ntile = (K + kTK - 1) / kTK;
     const int per = (ntile + KS - 1) / KS;
@@ -95,7 +99,8 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_mfma(GemvParams p, int ups) {
             r1b = r0b;
         }
         const int sel = r0b / p.rows_per_sel;
-        const uint16_t *W = reinterpret_cast<const uint16_t *>(p.W);
+        const int rb = blk ? r1b : r0b;         // this wave's block
+        const uint16_t *W = reinterpret_cast<const uint16_t *>(p.W) + (int64_t)rb * K;
         const uint16_t *xb = reinterpret_cast<const uint16_t *>(p.X) + (int64_t)sel * p.x_sel_stride;
         bool xok[MT];
         const uint16_t *xr[MT];
@@ -104,21 +109,16 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_mfma(GemvParams p, int ups) {
             xok[t] = t * 16 + li < p.M;
             xr[t] = xb + (int64_t)(p.m0 + t * 16 + li) * K + 8 * lg;
         }
-        f32x4 acc[MT][B];
+        f32x4 acc[MT];
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
-#pragma unroll
-            for (int j = 0; j < B; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         uint4 wv[NL];
         auto load = [&](int tt) {
             const int k = tt * kTK + lcol;
 #pragma unroll
-            for (int i = 0; i < NL; ++i) {
-                const int tr = 2 * i + lrow;                      // tile row
-                const int grow = (tr < 16 ? r0b : r1b) + (tr & 15);
-                wv[i] = k < K ? ld16_stream(W + (int64_t)grow * K + k) : make_uint4(0, 0, 0, 0);
-            }
+            for (int i = 0; i < NL; ++i)
+                wv[i] = k < K ? ld16_stream(W + (int64_t)(2 * i + lrow) * K + k) : make_uint4(0, 0, 0, 0);
         };
         if (t0 < t1) load(t0);
         for (int tt = t0; tt < t1; ++tt) {
@@ -137,51 +137,56 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_mfma(GemvParams p, int ups) {
 #pragma unroll
             for (int s2 = 0; s2 < kTK / 32; ++s2) {
                 if (s2 < nsteps) {
+                    const uint4 wt = *reinterpret_cast<const uint4 *>(&tile[li * kLD + 32 * s2 + 8 * lg]);
 #pragma unroll
-                    for (int j = 0; j < B; ++j) {
-                        const uint4 wt =
-                            *reinterpret_cast<const uint4 *>(&tile[(16 * j + li) * kLD + 32 * s2 + 8 * lg]);
-#pragma unroll
-                        for (int t = 0; t < MT; ++t)
-                            acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xv[s2][t]), as_bf16x8(wt),
-                                                                                 acc[t][j], 0, 0, 0);
-                    }
+                    for (int t = 0; t < MT; ++t)
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xv[s2][t]), as_bf16x8(wt), acc[t],
+                                                                          0, 0, 0);
                 }
             }
         }
-        // fixed-order sum of the K parts; C layout: lane l, register r holds
-        // C[4 * (l / 16) + r][l % 16] = (activation row, weight row of the block)
-        if (KS > 1) {
+        // fixed-order sum of the K parts of each block by wave 0; C layout:
+        // lane l, register r holds C[4 * (l / 16) + r][l % 16] = (activation
+        // row, weight row of the block)
+        f32x4 res[NB][MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) res[0][t] = acc[t];
+        if (NW > 1) {
             __syncthreads();   // every wave is done with its tile
             f32x4 *red = reinterpret_cast<f32x4 *>(tile);
 #pragma unroll
-            for (int t = 0; t < MT; ++t)
-#pragma unroll
-                for (int j = 0; j < B; ++j) red[(t * B + j) * 64 + lane] = acc[t][j];
+            for (int t = 0; t < MT; ++t) red[t * 64 + lane] = acc[t];
             __syncthreads();
-            if (part == 0) {
-                for (int q = 1; q < KS; ++q) {
-                    const f32x4 *o = reinterpret_cast<const f32x4 *>(smem + (size_t)q * (16 * B) * kLD);
+            if (wave == 0) {
 #pragma unroll
-                    for (int t = 0; t < MT; ++t)
+                for (int j = 0; j < NB; ++j) {
+                    for (int q = (j == 0 ? 1 : 0); q < KS; ++q) {
+                        const f32x4 *o = reinterpret_cast<const f32x4 *>(smem + (size_t)(j * KS + q) * TILE);
 #pragma unroll
-                        for (int j = 0; j < B; ++j) acc[t][j] += o[(t * B + j) * 64 + lane];
+                        for (int t = 0; t < MT; ++t) {
+                            if (j == 0) res[0][t] += o[t * 64 + lane];
+                            else if (q == 0) res[j][t] = o[t * 64 + lane];
+                            else res[j][t] += o[t * 64 + lane];
+                        }
+                    }
                 }
             }
             __syncthreads();
         }
-        if (part != 0) continue;
+        if (wave != 0) continue;
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
             float ssv[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
+            // one activation row at a time (keeps the epilogue's registers
+            // out of the streaming loop's budget)
+#pragma unroll 1
             for (int r = 0; r < 4; ++r) {
                 const int m = t * 16 + 4 * lg + r;
                 if (m >= p.M) continue;
                 if constexpr (kPair) {
-                    epi_pair<uint16_t, EPI>(p, r0b + li, r0b + li, r1b + li, sel, m, acc[t][0][r], acc[t][1][r]);
+                    epi_pair<uint16_t, EPI>(p, r0b + li, r0b + li, r1b + li, sel, m, res[0][t][r], res[NB - 1][t][r]);
                 } else {
-                    epi_row<uint16_t, EPI>(p, r0b + li, sel, m, acc[t][0][r], ssv[r], best_v[t][r], best_i[t][r]);
+                    epi_row<uint16_t, EPI>(p, r0b + li, sel, m, res[0][t][r], ssv[r], best_v[t][r], best_i[t][r]);
                 }
             }
             if constexpr (epi_has_ss(EPI)) {
@@ -200,7 +205,7 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_mfma(GemvParams p, int ups) {
         }
     }
     if constexpr (EPI == EPI_LOGITS) {
-        if (part != 0) return;
+        if (wave != 0) return;
 #pragma unroll
         for (int t = 0; t < MT; ++t)
 #pragma unroll
@@ -219,9 +224,12 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_mfma(GemvParams p, int ups) {
 
 template <int MT, int EPI>
 void launch_epi(const GemvParams &p, dim3 g, int ks, int ups, hipStream_t s) {
-    if (ks == 4) hipLaunchKernelGGL((k_gemm_mfma<MT, EPI, 4>), g, dim3(256), 0, s, p, ups);
-    else if (ks == 8) hipLaunchKernelGGL((k_gemm_mfma<MT, EPI, 8>), g, dim3(512), 0, s, p, ups);
-    else if constexpr (!epi_is_pair(EPI)) hipLaunchKernelGGL((k_gemm_mfma<MT, EPI, 16>), g, dim3(1024), 0, s, p, ups);
+    if constexpr (epi_is_pair(EPI)) {
+        hipLaunchKernelGGL((k_gemm_mfma<MT, EPI, 4>), g, dim3(512), 0, s, p, ups);
+    } else {
+        if (ks == 4) hipLaunchKernelGGL((k_gemm_mfma<MT, EPI, 4>), g, dim3(256), 0, s, p, ups);
+        else hipLaunchKernelGGL((k_gemm_mfma<MT, EPI, 8>), g, dim3(512), 0, s, p, ups);
+    }
 }
 
 template <int MT>
@@ -249,14 +257,14 @@ int gemm_mfma_grid(const GemvParams &p) {
     return p.epi == EPI_LOGITS && n > kLogitGrid ? kLogitGrid : n;
 }
 
-// Waves per workgroup (4, 8 or 16; 8 at most for paired units, whose LDS
-// tiles are twice as tall): enough for about 3K waves per launch while every
-// wave keeps at least one tile.
+// Waves per block (4 or 8): 8 when the launch would otherwise have fewer than
+// about 3K waves and every wave keeps at least one tile.  Paired units keep 4
+// (8 would make 1024-thread workgroups, whose register budget spills).
 int gemm_mfma_splits(const GemvParams &p) {
-    const int B = epi_is_pair(p.epi) ? 2 : 1;
+    if (epi_is_pair(p.epi)) return 4;
     const int ntile = (p.K + kTK - 1) / kTK;
     int ks = 4;
-    while (ks < kMaxKS / B && (int64_t)p.n_units * ks < 3072 && ks * 2 <= ntile) ks *= 2;
+    while (ks < kMaxKS && (int64_t)p.n_units * ks < 3072 && ks * 2 <= ntile) ks *= 2;
     return ks;
 }
 
@@ -267,7 +275,7 @@ bool gemm_mfma_supported(const GemvParams &p) {
 }
 
 hipError_t launch_gemm_mfma(const GemvParams &p, int grid, int ks, hipStream_t s) {
-    if ((ks != 4 && ks != 8 && ks != 16) || (epi_is_pair(p.epi) && ks > kMaxKS / 2)) return hipErrorInvalidValue;
+    if ((ks != 4 && ks != 8) || (epi_is_pair(p.epi) && ks != 4)) return hipErrorInvalidValue;
     // partial index of a residual writer: the unit within its set member
     const int ups = p.rows_per_sel / 16;
     if (epi_has_ss(p.epi) && p.n_norm_sel > 0 && grid != p.n_units) return hipErrorInvalidValue;
