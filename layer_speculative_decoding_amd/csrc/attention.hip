@@ -72,6 +72,48 @@ __device__ __forceinline__ void store_span(T *p, const float *v) {
     for (int i = 0; i < N; ++i) p[i] = Store<T>::from_f32(v[i]);
 }
 
+// N consecutive cache elements kept as loaded (bf16 pairs stay packed until
+// used, which halves the registers a K or V slice needs).
+template <typename T, int N> struct Raw;
+template <int N> struct Raw<uint16_t, N> {
+    static constexpr int W = N >= 2 ? N / 2 : 1;
+    uint32_t w[W];
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int i = 0; i < W; ++i) w[i] = 0u;
+    }
+    __device__ __forceinline__ void load(const uint16_t *p) {
+        if constexpr (N % 8 == 0) {
+#pragma unroll
+            for (int i = 0; i < N / 8; ++i) {
+                const uint4 v = ld16(p + 8 * i);
+                w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+            }
+        } else if constexpr (N == 4) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(p);
+            w[0] = v.x; w[1] = v.y;
+        } else if constexpr (N == 2) {
+            w[0] = *reinterpret_cast<const uint32_t *>(p);
+        } else {
+            static_assert(N == 1, "span");
+            w[0] = p[0];
+        }
+    }
+    __device__ __forceinline__ float operator[](int e) const {
+        if constexpr (N == 1) return bf16_lo(w[0]);
+        else return (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+    }
+};
+template <int N> struct Raw<float, N> {
+    float v[N];
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] = 0.f;
+    }
+    __device__ __forceinline__ void load(const float *p) { load_span<N>(p, v); }
+    __device__ __forceinline__ float operator[](int e) const { return v[e]; }
+};
+
 // The workgroup's query vector qv -> (row of the call, q head); -1 if padding.
 struct QvMap {
     int G, QV, row0, head0;
@@ -122,6 +164,26 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
     const T *Kc = reinterpret_cast<const T *>(p.kc) + cache_off;
     const T *Vc = reinterpret_cast<const T *>(p.vc) + cache_off;
 
+    // K / V slices of one key block: A operand of QK (K[key kb + c][dims of
+    // lane group g]) and B operand of PV (V[key kb + 4 g + r][dims DV c ...])
+    Raw<T, DK> kr[NP];
+    Raw<T, DV> vr[4];
+    auto load_kv = [&](int kb) {
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            kr[i].zero();
+            if (kb + c < ke) kr[i].load(Kc + (int64_t)(kb + c) * HD + DK * g + 4 * DK * i);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            vr[r].zero();
+            if (kb + 4 * g + r < ke) vr[r].load(Vc + (int64_t)(kb + 4 * g + r) * HD + DV * c);
+        }
+    };
+    // the first block is requested before the query vectors, the next one
+    // before the current one is consumed
+    if (ks + kKB * wave < ke) load_kv(ks + kKB * wave);
+
     // B operand of QK: q[qv = 16 nb + c][dim (4 DK) i + DK g + e] at t = DK i + e
     float qreg[NQB][NT];
     int qpos[NQB];
@@ -156,33 +218,21 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
     }
 
     for (int kb = ks + kKB * wave; kb < ke; kb += kSpan) {
-        // A operand of QK: K[key kb + c][dims of lane group g]
-        float kf[NT];
-        if (kb + c < ke) {
-            const T *kp = Kc + (int64_t)(kb + c) * HD + DK * g;
+        Raw<T, DK> kcur[NP];
+        Raw<T, DV> vcur[4];
 #pragma unroll
-            for (int i = 0; i < NP; ++i) load_span<DK>(kp + 4 * DK * i, &kf[DK * i]);
-        } else {
+        for (int i = 0; i < NP; ++i) kcur[i] = kr[i];
 #pragma unroll
-            for (int t = 0; t < NT; ++t) kf[t] = 0.f;
-        }
-        // B operand of PV: V[key kb + 4 g + r][dims DV c ...]
-        float vf[4][DV];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int key = kb + 4 * g + r;
-            if (key < ke) {
-                load_span<DV>(Vc + (int64_t)key * HD + DV * c, vf[r]);
-            } else {
-#pragma unroll
-                for (int j = 0; j < DV; ++j) vf[r][j] = 0.f;
-            }
-        }
+        for (int r = 0; r < 4; ++r) vcur[r] = vr[r];
+        if (kb + kSpan < ke) load_kv(kb + kSpan);
 #pragma unroll
         for (int nb = 0; nb < NQB; ++nb) {
             f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int t = 0; t < NT; ++t) sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t], qreg[nb][t], sc, 0, 0, 0);
+            for (int i = 0; i < NP; ++i)
+#pragma unroll
+                for (int e = 0; e < DK; ++e)
+                    sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kcur[i][e], qreg[nb][DK * i + e], sc, 0, 0, 0);
             // lane holds S[key kb + 4 g + r][qv 16 nb + c]
             float pr[4];
             float mx = -INFINITY;
@@ -217,7 +267,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
             for (int r = 0; r < 4; ++r)
 #pragma unroll
                 for (int j = 0; j < DV; ++j)
-                    acc[nb][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(pr[r], vf[r][j], acc[nb][j], 0, 0, 0);
+                    acc[nb][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(pr[r], vcur[r][j], acc[nb][j], 0, 0, 0);
         }
     }
 
