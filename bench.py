@@ -28,6 +28,75 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 
 
+PROBE_COPY_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "pmc_traffic.md")
+
+
+def kernel_source_hash():
+    """sha256 over the HIP sources, so stored counter figures are used only
+    for the kernels they were taken on."""
+    import hashlib
+    d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "layer_speculative_decoding_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    or None if there is none for it or the kernels changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.strip().split(": ", 1) for line in f if line.startswith(("kernel: ", "traffic_bytes_per_launch: ", "source_sha256: ")))
+    except OSError:
+        return None
+    if kv.get("kernel") != kernel or kv.get("source_sha256") != kernel_source_hash():
+        return None
+    return int(kv["traffic_bytes_per_launch"])
+
+
+def pmc_summary(fetch_csv, write_csv, kernel, command):
+    """Markdown summary of two counter runs (FETCH_SIZE, WRITE_SIZE; KiB per
+    dispatch) of `bench.py --pmc-probe`: each counter is scaled by what it
+    reads for the probe's device copy of PROBE_COPY_BYTES, then averaged over
+    the dispatches of `kernel`."""
+    import csv
+
+    def load(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]][-1]
+        factor = PROBE_COPY_BYTES / 1024 / copy
+        vals = [float(r["Counter_Value"]) for r in rows if kernel + "(" in r["Kernel_Name"]]
+        return copy, factor, vals
+
+    fc, ff, fv = load(fetch_csv, "FETCH_SIZE")
+    wc, wf, wv = load(write_csv, "WRITE_SIZE")
+    fetch = sum(fv) / len(fv) * ff * 1024
+    write = sum(wv) / len(wv) * wf * 1024
+    print(f"# HBM traffic of {kernel} (hardware counters)")
+    print()
+    print("Commands (from the repository root, TMPDIR=/tmp):")
+    print()
+    for c in command:
+        print(f"    {c}")
+    print()
+    print(f"Calibration: the probe's device copy of {PROBE_COPY_BYTES} bytes reads FETCH_SIZE {fc:.1f} KiB and "
+          f"WRITE_SIZE {wc:.1f} KiB, so the counters are scaled by {ff:.4f} (fetch) and {wf:.4f} (write).")
+    print()
+    print(f"| counter | dispatches | raw avg KiB | scaled avg bytes |")
+    print(f"|---|---|---|---|")
+    print(f"| FETCH_SIZE | {len(fv)} | {sum(fv) / len(fv):.1f} | {fetch:.0f} |")
+    print(f"| WRITE_SIZE | {len(wv)} | {sum(wv) / len(wv):.1f} | {write:.0f} |")
+    print()
+    print(f"kernel: {kernel}")
+    print(f"traffic_bytes_per_launch: {int(round(fetch + write))}")
+    print(f"source_sha256: {kernel_source_hash()}")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -57,7 +126,20 @@ def main():
     ap.add_argument("--temperature", type=float, default=0.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-vanilla", action="store_true")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="run a few rounds and one device copy of known size, for hardware-counter runs")
+    ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL"),
+                    help="print the traffic summary of two counter runs of --pmc-probe")
     args = ap.parse_args()
+    if args.pmc_summary:
+        f, w, kname = args.pmc_summary
+        pmc_summary(f, w, kname, [
+            "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run "
+            "-- python bench.py --warmup 1 --pmc-probe",
+            "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run "
+            "-- python bench.py --warmup 1 --pmc-probe",
+            f"python bench.py --pmc-summary {f} {w} '{kname}' > profiles/pmc_traffic.md"])
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer-parallel path here "
               f"is a single-GPU build", file=sys.stderr)
@@ -104,6 +186,18 @@ def main():
     for _ in range(W):
         dec.step(big)
     torch.cuda.synchronize()
+    if args.pmc_probe:
+        # rounds of the timed mix, then a plain device copy of PROBE_COPY_BYTES
+        # (read once, written once) that calibrates the byte counters
+        for _ in range(3):
+            dec.step(big)
+        src = torch.ones(PROBE_COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"  probe: 3 rounds and one {PROBE_COPY_BYTES} byte device copy")
+        return
 
     # timed region: K whole rounds; phase events recorded on the same stream
     n_before = sum(len(o) for o in dec.out)
@@ -148,6 +242,7 @@ def main():
     dom = max(prof.items(), key=lambda kv: kv[1][1])
     dom_name, (dom_n, dom_ms, dom_bytes) = dom
     dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = stored_traffic(dom_name)
     log(f"  dominant kernel {dom_name}: {dom_n} launches, avg {dom_ms / dom_n * 1e3:.1f} us, "
         f"{dom_bytes / dom_n / 1e6:.1f} MB/launch, {dom_gbs:.0f} GB/s")
     for name, (n, t, by) in sorted(prof.items(), key=lambda kv: -kv[1][1]):
@@ -192,7 +287,7 @@ def main():
         "prefill_ms": round(prefill_ms, 2),
         "vanilla_tokens_per_s": vanilla,
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "launches": dom_n, "avg_launch_us": round(dom_ms / dom_n * 1e3, 2),
                      "bytes_per_launch": int(dom_bytes / dom_n)},
         "roofline_draft_step": {"bound": "hbm", "achieved": round(d_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
