@@ -166,14 +166,15 @@ spec_status spec_draft_group_step(const spec_model *draft, const spec_kv *kv,
  * overwriting the draft KV there; the last position of each sequence gives
  * the draft distribution of the next token, which is sampled (purpose 0, for
  * position start_pos[b]+n_tokens[b]).  Also the draft's prompt prefill.
- *   tokens (dev) [batch][max_m]; start_pos, n_tokens (dev) [batch];
- *   n_tokens may be NULL (= max_m for all).  max_pos (host) bounds
+ *   tokens (dev): sequence b's tokens at tokens + b * tokens_stride
+ *   (tokens_stride >= max_m); start_pos, n_tokens (dev) [batch]; n_tokens
+ *   may be NULL (= max_m for all).  max_pos (host) bounds
  *   start_pos[b] + n_tokens[b] - 1.
  *   last_logits_out (dev, nullable): float32 logits of sequence b at
  *     last_logits_out + b * logits_stride (logits_stride >= vocab);
  *   token_out (dev) at token_out[b * token_out_stride]. */
 spec_status spec_calibrate_kv(const spec_model *draft, const spec_kv *kv, int batch,
-                              const int32_t *tokens, const int32_t *start_pos,
+                              const int32_t *tokens, int tokens_stride, const int32_t *start_pos,
                               const int32_t *n_tokens, int max_m, int max_pos,
                               float inv_temperature, uint64_t seed,
                               float *last_logits_out, int64_t logits_stride,

@@ -68,8 +68,8 @@ def load() -> C.CDLL:
         "spec_workspace_bytes": (sz, [vp, i32, i32, i32]),
         "spec_draft_group_step": (i32, [vp, C.POINTER(KV), C.POINTER(C.c_int32), i32, i32, i32, vp, i32, vp, i32,
                                         f32, u64, vp, i64, vp, i32, vp, sz, vp]),
-        "spec_calibrate_kv": (i32, [vp, C.POINTER(KV), i32, vp, vp, vp, i32, i32, f32, u64, vp, i64, vp, i32, vp, sz,
-                                    vp]),
+        "spec_calibrate_kv": (i32, [vp, C.POINTER(KV), i32, vp, i32, vp, vp, i32, i32, f32, u64, vp, i64, vp, i32, vp,
+                                    sz, vp]),
         "spec_verify_forward": (i32, [vp, C.POINTER(KV), i32, vp, vp, i32, i32, vp, vp, sz, vp]),
         "spec_accept_workspace_bytes": (sz, [i32, i32, i32]),
         "spec_accept_resample": (i32, [i32, i32, i32, vp, vp, vp, i32, vp, f32, u64, vp, vp, i32, vp, vp, sz, vp]),

@@ -109,9 +109,12 @@ def spec_draft_group_step(model: SpecModel, kv: KVCache, plan_offsets, flags: in
 def spec_calibrate_kv(model: SpecModel, kv: KVCache, batch: int, tokens: torch.Tensor, start_pos: torch.Tensor,
                       n_tokens: Optional[torch.Tensor], max_m: int, max_pos: int, inv_temperature: float,
                       seed: int, last_logits_out: Optional[torch.Tensor], logits_stride: int,
-                      token_out: torch.Tensor, token_out_stride: int, workspace: torch.Tensor, stream=None):
+                      token_out: torch.Tensor, token_out_stride: int, workspace: torch.Tensor, stream=None,
+                      tokens_stride: Optional[int] = None):
+    """tokens_stride: elements between sequences' token rows (default max_m)."""
     check(load().spec_calibrate_kv(
-        model.handle, C.byref(kv.c), batch, _ptr(tokens), _ptr(start_pos), _ptr(n_tokens), max_m, max_pos,
+        model.handle, C.byref(kv.c), batch, _ptr(tokens), max_m if tokens_stride is None else tokens_stride,
+        _ptr(start_pos), _ptr(n_tokens), max_m, max_pos,
         C.c_float(inv_temperature), C.c_uint64(seed), _ptr(last_logits_out), logits_stride, _ptr(token_out),
         token_out_stride, _ptr(workspace), workspace.numel(), _stream(stream)))
 

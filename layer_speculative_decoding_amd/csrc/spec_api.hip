@@ -552,11 +552,12 @@ spec_status spec_draft_group_step(const spec_model *draft, const spec_kv *kv, co
 }
 
 static spec_status precise_forward(const spec_model *m, const spec_kv *kv, int batch, const int32_t *tokens,
-                                   const int32_t *start_pos, const int32_t *n_tokens, int mseq, int max_pos,
+                                   int tokens_stride, const int32_t *start_pos, const int32_t *n_tokens, int mseq,
+                                   int max_pos,
                                    void *ws, hipStream_t s, Fwd &f) {
     f = Fwd{m, kv, batch, mseq, max_pos, RowMap{start_pos, n_tokens, mseq, kv->capacity}, ws,
             carve(m, batch, mseq, 1), s, {0}};
-    hipError_t e = run_embed(f, tokens, mseq, 1);
+    hipError_t e = run_embed(f, tokens, tokens_stride, 1);
     if (e != hipSuccess) return hip_fail(e, "embed");
     for (int l = 0; l < m->d.n_layers; ++l) {
         e = run_stage(f, l, 1, SPEC_MLP_SEQUENTIAL);
@@ -566,7 +567,8 @@ static spec_status precise_forward(const spec_model *m, const spec_kv *kv, int b
 }
 
 spec_status spec_calibrate_kv(const spec_model *draft, const spec_kv *kv, int batch, const int32_t *tokens,
-                              const int32_t *start_pos, const int32_t *n_tokens, int max_m, int max_pos,
+                              int tokens_stride, const int32_t *start_pos, const int32_t *n_tokens, int max_m,
+                              int max_pos,
                               float inv_temperature, uint64_t seed, float *last_logits_out, int64_t logits_stride,
                               int32_t *token_out, int token_out_stride, void *workspace, size_t ws_bytes,
                               void *stream) {
@@ -574,6 +576,7 @@ spec_status spec_calibrate_kv(const spec_model *draft, const spec_kv *kv, int ba
     if (st) return st;
     if (!tokens || !start_pos || !token_out) return fail(SPEC_ERR_INVALID_ARG, "NULL tokens/start_pos/token_out");
     if (max_m < 1) return fail(SPEC_ERR_INVALID_ARG, "max_m %d < 1", max_m);
+    if (tokens_stride < max_m) return fail(SPEC_ERR_INVALID_ARG, "tokens_stride %d < max_m %d", tokens_stride, max_m);
     if (token_out_stride < 1) return fail(SPEC_ERR_INVALID_ARG, "token_out_stride < 1");
     if (last_logits_out && logits_stride < draft->d.vocab) return fail(SPEC_ERR_INVALID_ARG, "logits_stride < vocab");
     if (max_pos < 0 || max_pos >= kv->capacity)
@@ -581,8 +584,8 @@ spec_status spec_calibrate_kv(const spec_model *draft, const spec_kv *kv, int ba
     if (!(inv_temperature >= 0.f)) return fail(SPEC_ERR_INVALID_ARG, "inv_temperature must be >= 0");
     if ((st = check_ws(draft, batch, max_m, 1, workspace, ws_bytes))) return st;
     Fwd f;
-    if ((st = precise_forward(draft, kv, batch, tokens, start_pos, n_tokens, max_m, max_pos, workspace,
-                              (hipStream_t)stream, f)))
+    if ((st = precise_forward(draft, kv, batch, tokens, tokens_stride, start_pos, n_tokens, max_m, max_pos,
+                              workspace, (hipStream_t)stream, f)))
         return st;
     // the sampled token is the one after the last calibrated position:
     // start_pos[b] + n_tokens[b] (n_tokens NULL: every sequence has max_m)
@@ -603,7 +606,7 @@ spec_status spec_verify_forward(const spec_model *base, const spec_kv *kv, int b
         return fail(SPEC_ERR_CAPACITY, "max_pos %d outside KV capacity %d", max_pos, kv->capacity);
     if ((st = check_ws(base, batch, m, 1, workspace, ws_bytes))) return st;
     Fwd f;
-    if ((st = precise_forward(base, kv, batch, tokens, start_pos, nullptr, m, max_pos, workspace,
+    if ((st = precise_forward(base, kv, batch, tokens, m, start_pos, nullptr, m, max_pos, workspace,
                               (hipStream_t)stream, f)))
         return st;
     if (logits_out) {

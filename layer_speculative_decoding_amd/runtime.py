@@ -173,9 +173,12 @@ class SpecDecoder:
                 marks[4].record()
             return False
         self.tab[k:].copy_(th[k:], non_blocking=True)
-        api.spec_calibrate_kv(self.draft, self.dkv, B, self.commit, self.tab[k], self.tab[k + 1], k + 1,
+        # the calibration covers exactly the emitted tokens: its row bound is
+        # the longest a + 1 of the round (token rows keep their k + 1 stride)
+        rows = max(1, max(int(th[k + 1, b]) for b in range(B)))
+        api.spec_calibrate_kv(self.draft, self.dkv, B, self.commit, self.tab[k], self.tab[k + 1], rows,
                               max(self.t), self.inv_temp, self.seed, self.q_logits[:, 0], k * self.V,
-                              self.vtok[:, 1], k + 1, self.ws)
+                              self.vtok[:, 1], k + 1, self.ws, tokens_stride=k + 1)
         if marks:
             marks[4].record()
         return True

@@ -126,13 +126,16 @@ def test_verify_calibrate_accept_host_validation():
     assert lib.spec_verify_forward(h, C.byref(kv), 1, 0x10, 0x20, 0, 3, 0x30, 0x40, big, None) == -1
     assert lib.spec_verify_forward(h, C.byref(kv), 1, None, 0x20, 2, 3, 0x30, 0x40, big, None) == -1
     assert lib.spec_verify_forward(h, C.byref(kv), 1, 0x10, 0x20, 2, 3, 0x30, 0x40, 8, None) == -6
-    assert lib.spec_calibrate_kv(h, C.byref(kv), 1, 0x10, 0x20, None, 4, 16, 0.0, 0, None, 0, 0x50, 1, 0x40, big,
+    assert lib.spec_calibrate_kv(h, C.byref(kv), 1, 0x10, 4, 0x20, None, 4, 16, 0.0, 0, None, 0, 0x50, 1, 0x40, big,
                                  None) == -5
-    assert lib.spec_calibrate_kv(h, C.byref(kv), 1, 0x10, 0x20, None, 0, 3, 0.0, 0, None, 0, 0x50, 1, 0x40, big,
+    assert lib.spec_calibrate_kv(h, C.byref(kv), 1, 0x10, 1, 0x20, None, 0, 3, 0.0, 0, None, 0, 0x50, 1, 0x40, big,
                                  None) == -1
-    assert lib.spec_calibrate_kv(h, C.byref(kv), 1, 0x10, 0x20, None, 2, 3, 0.0, 0, None, 0, None, 1, 0x40, big,
+    assert lib.spec_calibrate_kv(h, C.byref(kv), 1, 0x10, 2, 0x20, None, 2, 3, 0.0, 0, None, 0, None, 1, 0x40, big,
                                  None) == -1
-    assert lib.spec_calibrate_kv(h, C.byref(kv), 1, 0x10, 0x20, None, 2, 3, 0.0, 0, 0x60, 100, 0x50, 1, 0x40, big,
+    assert lib.spec_calibrate_kv(h, C.byref(kv), 1, 0x10, 2, 0x20, None, 2, 3, 0.0, 0, 0x60, 100, 0x50, 1, 0x40, big,
+                                 None) == -1
+    # token rows closer together than max_m
+    assert lib.spec_calibrate_kv(h, C.byref(kv), 1, 0x10, 1, 0x20, None, 2, 3, 0.0, 0, None, 0, 0x50, 1, 0x40, big,
                                  None) == -1
     acc = lib.spec_accept_resample
     assert lib.spec_accept_workspace_bytes(1, 4, 256) > 0
