@@ -223,19 +223,22 @@ spec_status spec_accept_resample(int batch, int k, int vocab,
                                  void *workspace, size_t ws_bytes, void *stream);
 
 /* Measurement hook (not part of the method).  While enabled, every
- * weight-streaming product launch (the GEMV / MFMA kernels that read the
- * weights) is bracketed by two HIP events recorded on the caller's stream and
- * attributed to its kernel instance, e.g. "k_gemm_mfma<1, false, false>",
- * together with the bytes the launch must read (every weight row once plus
- * the activation rows).  spec_profile_collect synchronises the recorded
- * events, folds them into per-instance totals and returns the number of
- * instances; spec_profile_entry reads one.  Enabling adds two event records
- * per launch, so time the method with it off. */
+ * weight-streaming product launch (the GEMV / matrix-core kernels that read
+ * the weights) and every grouped-attention launch is bracketed by two HIP
+ * events recorded on the caller's stream and attributed to its kernel
+ * instance, e.g. "k_gemm_mfma<1, 2, 4>", together with the bytes the launch
+ * must read (every weight row once plus the activation rows; for attention
+ * the K/V rows up to the call's max_pos, a bound) and, for the products, the
+ * flops 2 * rows * K * activation rows.  spec_profile_collect synchronises
+ * the recorded events, folds them into per-instance totals and returns the
+ * number of instances; spec_profile_entry reads one (any output pointer may
+ * be NULL).  Enabling adds two event records per launch, so time the method
+ * with it off. */
 spec_status spec_profile_enable(int on);
 void spec_profile_reset(void);
 int spec_profile_collect(void);
 spec_status spec_profile_entry(int i, char *name, int name_cap, int64_t *launches, double *total_ms,
-                               double *total_bytes);
+                               double *total_bytes, double *total_flops);
 
 const char *spec_status_string(spec_status s);
 const char *spec_last_error(void);

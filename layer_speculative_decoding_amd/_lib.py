@@ -80,7 +80,7 @@ def load() -> C.CDLL:
         "spec_profile_reset": (None, []),
         "spec_profile_collect": (i32, []),
         "spec_profile_entry": (i32, [i32, C.c_char_p, i32, C.POINTER(C.c_int64), C.POINTER(C.c_double),
-                                     C.POINTER(C.c_double)]),
+                                     C.POINTER(C.c_double), C.POINTER(C.c_double)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -151,14 +151,15 @@ def spec_profile_reset():
 
 
 def spec_profile_collect() -> dict:
-    """{kernel instance: (launches, total_ms, total_bytes)} of the launches
-    recorded while profiling was enabled (synchronises their events)."""
+    """{kernel instance: (launches, total_ms, total_bytes, total_flops)} of
+    the launches recorded while profiling was enabled (synchronises their
+    events)."""
     lib = load()
     n = lib.spec_profile_collect()
     out = {}
     buf = C.create_string_buffer(256)
     for i in range(n):
-        la, ms, by = C.c_int64(), C.c_double(), C.c_double()
-        check(lib.spec_profile_entry(i, buf, 256, C.byref(la), C.byref(ms), C.byref(by)))
-        out[buf.value.decode()] = (la.value, ms.value, by.value)
+        la, ms, by, fl = C.c_int64(), C.c_double(), C.c_double(), C.c_double()
+        check(lib.spec_profile_entry(i, buf, 256, C.byref(la), C.byref(ms), C.byref(by), C.byref(fl)))
+        out[buf.value.decode()] = (la.value, ms.value, by.value, fl.value)
     return out

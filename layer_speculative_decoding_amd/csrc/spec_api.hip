@@ -43,18 +43,19 @@ spec_status hip_fail(hipError_t e, const char *where) {
 inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ------------------------------------------------------------ measurement
-// While enabled, each weight-streaming product launch is bracketed by two
-// HIP events on its stream and attributed to its kernel instance with the
-// bytes the launch must read (weights + activation rows).
+// While enabled, each product and attention launch is bracketed by two HIP
+// events on its stream and attributed to its kernel instance with the bytes
+// the launch must read (weights + activation rows; the K/V rows attention
+// reads) and, for the products, the multiply-add flops 2 * M * rows * K.
 struct ProfPending {
     std::string name;
-    double bytes;
+    double bytes, flops;
     hipEvent_t a, b;
 };
 struct ProfAgg {
     std::string name;
     int64_t launches;
-    double ms, bytes;
+    double ms, bytes, flops;
 };
 std::mutex g_prof_mu;
 bool g_prof_on = false;
@@ -85,12 +86,12 @@ struct ProfScope {
             (void)hipEventRecord(a, s);
         }
     }
-    void done(const std::string &name, double bytes) {
+    void done(const std::string &name, double bytes, double flops = 0.0) {
         if (!on) return;
         std::lock_guard<std::mutex> g(g_prof_mu);
         hipEvent_t b = prof_event();
         (void)hipEventRecord(b, s);
-        g_prof_pending.push_back({name, bytes, a, b});
+        g_prof_pending.push_back({name, bytes, flops, a, b});
     }
 };
 
@@ -169,6 +170,22 @@ int mfma_min_rows() {
     return v;
 }
 
+// Activation-row count from which bf16 products use the tiled matrix-core
+// GEMM (SPEC_TILED_MIN_ROWS overrides).
+int tiled_min_rows() {
+    static int v = [] {
+        const char *e = getenv("SPEC_TILED_MIN_ROWS");
+        return e ? atoi(e) : gemm_tiled_min_rows();
+    }();
+    return v;
+}
+
+std::string tiled_name(const GemvParams &p) {
+    const bool pair = p.epi == EPI_QKV_ROPE || p.epi == EPI_SILU_MUL;
+    const int nh = (pair && (p.pair_block / 2) % 64 != 0) ? 32 : 64;
+    return "k_gemm_tile<" + std::to_string(p.epi) + ", " + std::to_string(nh) + ">";
+}
+
 // Weight-streaming product over the call's p.Mtot activation rows, chunked by
 // the kernel's row limit.  *parts_out: the sum-of-squares or sampling
 // partials each output row now has.
@@ -187,6 +204,28 @@ hipError_t product(const Fwd &f, GemvParams p, int *parts_out = nullptr) {
     const bool mfma = m->d.dtype == SPEC_BF16 && Mtot >= mfma_min_rows() && rows % (pair ? 32 : 16) == 0 &&
                       gemm_mfma_supported(q);
     const double wbytes = (double)rows * p.K * m->xs;   // every weight row once
+    GemvParams t = p;
+    t.m0 = 0;
+    t.M = Mtot;
+    if (m->d.dtype == SPEC_BF16 && Mtot >= tiled_min_rows() && gemm_tiled_supported(t)) {
+        // prompt-length row counts: one tiled launch over every row
+        if (parts_out) *parts_out = gemm_tiled_parts(t);
+        double xbytes = (double)Mtot * p.K * m->xs;
+        if (p.xmode == X_NORM) {
+            const int n_sel = rows / p.rows_per_sel;
+            void *xn = at<char>(f.ws, f.c.xn);
+            hipError_t e = launch_norm_rows(m->d.dtype, t, n_sel, xn, f.s);
+            if (e != hipSuccess) return e;
+            t.xmode = X_PLAIN;
+            t.X = xn;
+            t.x_sel_stride = (int64_t)Mtot * p.K;
+            xbytes *= n_sel;
+        }
+        ProfScope ps(f.s);
+        hipError_t e = launch_gemm_tiled(t, f.s);
+        ps.done(tiled_name(t), wbytes + xbytes, 2.0 * Mtot * rows * (double)p.K);
+        return e;
+    }
     if (mfma) {
         const int grid = gemm_mfma_grid(q);
         const int ks = gemm_mfma_splits(q);
@@ -210,7 +249,7 @@ hipError_t product(const Fwd &f, GemvParams p, int *parts_out = nullptr) {
             }
             ProfScope ps(f.s);
             hipError_t e = launch_gemm_mfma(r, grid, ks, f.s);
-            ps.done(mfma_name(q.M, p.epi, ks), wbytes + xbytes);
+            ps.done(mfma_name(q.M, p.epi, ks), wbytes + xbytes, 2.0 * q.M * rows * (double)p.K);
             if (e != hipSuccess) return e;
         }
         return hipSuccess;
@@ -224,7 +263,8 @@ hipError_t product(const Fwd &f, GemvParams p, int *parts_out = nullptr) {
         p.M = (Mtot - m0) < mr ? (Mtot - m0) : mr;
         ProfScope ps(f.s);
         hipError_t e = launch_gemv(m->d.dtype, p, grid, ks, f.s);
-        ps.done(gemv_name(m->d.dtype, p.M, p.epi), wbytes + (double)p.M * p.K * (p.xmode == X_NORM ? 4 : m->xs));
+        ps.done(gemv_name(m->d.dtype, p.M, p.epi), wbytes + (double)p.M * p.K * (p.xmode == X_NORM ? 4 : m->xs),
+                2.0 * p.M * rows * (double)p.K);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -286,7 +326,14 @@ hipError_t run_stage(Fwd &f, int l0, int n, int mlp_mode) {
     ap.splits = attention_splits(n, f.batch, d.n_q_heads, d.n_kv_heads, f.mseq, f.max_pos);
     ap.o = o; ap.o_sel_stride = (int64_t)R * qd;
     ap.part_acc = at<float>(f.ws, f.c.pacc); ap.part_ml = at<float>(f.ws, f.c.pml); ap.Mtot = R;
-    if ((e = launch_attention(d.dtype, ap, f.s)) != hipSuccess) return e;
+    {
+        // K/V rows of every set member, every sequence, up to max_pos (a bound)
+        ProfScope ps(f.s);
+        e = launch_attention(d.dtype, ap, f.s);
+        ps.done(ap.splits > 1 ? "k_attn (split)" : "k_attn",
+                2.0 * n * f.batch * (f.max_pos + 1.0) * d.n_kv_heads * d.head_dim * xs);
+        if (e != hipSuccess) return e;
+    }
 
     // 3. grouped O projection: a_0 goes into the residual (sequential MLPs),
     //    the others wait in abuf; partial sums give the MLP inputs' RMS
@@ -405,12 +452,13 @@ int spec_profile_collect(void) {
         for (auto &x : g_prof_agg)
             if (x.name == p.name) agg = &x;
         if (!agg) {
-            g_prof_agg.push_back({p.name, 0, 0.0, 0.0});
+            g_prof_agg.push_back({p.name, 0, 0.0, 0.0, 0.0});
             agg = &g_prof_agg.back();
         }
         agg->launches += 1;
         agg->ms += ms;
         agg->bytes += p.bytes;
+        agg->flops += p.flops;
         g_prof_pool.push_back(p.a);
         g_prof_pool.push_back(p.b);
     }
@@ -419,7 +467,7 @@ int spec_profile_collect(void) {
 }
 
 spec_status spec_profile_entry(int i, char *name, int name_cap, int64_t *launches, double *total_ms,
-                               double *total_bytes) {
+                               double *total_bytes, double *total_flops) {
     std::lock_guard<std::mutex> g(g_prof_mu);
     if (i < 0 || i >= (int)g_prof_agg.size() || !name || name_cap < 1)
         return fail(SPEC_ERR_INVALID_ARG, "profile entry %d out of range", i);
@@ -428,6 +476,7 @@ spec_status spec_profile_entry(int i, char *name, int name_cap, int64_t *launche
     if (launches) *launches = a.launches;
     if (total_ms) *total_ms = a.ms;
     if (total_bytes) *total_bytes = a.bytes;
+    if (total_flops) *total_flops = a.flops;
     return SPEC_OK;
 }
 const char *spec_last_error(void) { return g_err; }

@@ -188,3 +188,51 @@ def test_draft_group_step_matches_oracle(name, mlp, inv_temp):
         ek, ev = _kv_rel(gkv, okv, int(pos.max()))
         assert ek < tol and ev < tol
 
+
+
+@pytest.mark.parametrize("name", ["gqa-bf16", "hd64-bias-bf16", "hd128-bf16"])
+def test_prompt_prefill_matches_oracle(name):
+    """Prompt-length row counts (several 128-row activation tiles and a ragged
+    last tile) through the tiled matrix-core products: base-style verify
+    prefill with every row's logits, and draft-style calibration prefill with
+    ragged prompt lengths."""
+    from layer_speculative_decoding_amd import api
+    B, P = 2, 150
+    shape, tol, om, gm, gkv, okv, prompts = _setup(name, B, P, cap=P + 8)
+    say(f"prompt prefill {name} B={B} P={P}")
+    w = ws(api.spec_workspace_bytes(gm, B, P, 1))
+    logits = torch.zeros(B, P, shape.vocab, device="cuda")
+    api.spec_verify_forward(gm, gkv, B, i32(prompts), i32([0, 0]), P, P - 1, logits, w)
+    torch.cuda.synchronize()
+    zg = logits.cpu().numpy()
+    for b in range(B):
+        zo = forward(om, okv, b, prompts[b], range(P), logits="all")
+        err = rel_linf(zg[b], zo)
+        say(f"  verify b={b} logits rel {err:.2e}")
+        assert err < tol
+    ek, ev = _kv_rel(gkv, okv, P)
+    say(f"  kv rel {ek:.2e} {ev:.2e}")
+    assert ek < tol and ev < tol
+
+    # calibration prefill, ragged: sequence 1 covers P - 41 tokens
+    gkv.k.zero_(); gkv.v.zero_()
+    okv = KVCache(shape, B, gkv.capacity)
+    lens = np.array([P, P - 41], dtype=np.int32)
+    last = torch.zeros(B, shape.vocab, device="cuda")
+    tok = torch.zeros(B, dtype=torch.int32, device="cuda")
+    api.spec_calibrate_kv(gm, gkv, B, i32(prompts), i32([0, 0]), i32(lens), P, P - 1, 1.0, 5, last, shape.vocab,
+                          tok, 1, w)
+    torch.cuda.synchronize()
+    zg, tg = last.cpu().numpy(), tok.cpu().numpy()
+    for b in range(B):
+        zo = forward(om, okv, b, prompts[b, :lens[b]], range(lens[b]), logits="last")
+        err = rel_linf(zg[b], zo)
+        say(f"  calibrate b={b} n={lens[b]} logits rel {err:.2e}")
+        assert err < tol
+        t_or, mg = sample_from_logits(zo, 1.0, 5, b, int(lens[b]), philox.DRAFT)
+        if mg >= exclusion(zg[b], zo, 1.0):
+            assert tg[b] == t_or
+    k = gkv.k.float().cpu().numpy()
+    assert not np.any(k[:, 1, :, lens[1]:])      # rows past n_tokens leave the cache alone
+    ek, ev = _kv_rel(gkv, okv, int(lens[0]))
+    assert ek < tol and ev < tol
