@@ -180,12 +180,6 @@ int tiled_min_rows() {
     return v;
 }
 
-std::string tiled_name(const GemvParams &p) {
-    const bool pair = p.epi == EPI_QKV_ROPE || p.epi == EPI_SILU_MUL;
-    const int nh = (pair && (p.pair_block / 2) % 64 != 0) ? 32 : 64;
-    return "k_gemm_tile<" + std::to_string(p.epi) + ", " + std::to_string(nh) + ">";
-}
-
 // Weight-streaming product over the call's p.Mtot activation rows, chunked by
 // the kernel's row limit.  *parts_out: the sum-of-squares or sampling
 // partials each output row now has.
@@ -223,7 +217,7 @@ hipError_t product(const Fwd &f, GemvParams p, int *parts_out = nullptr) {
         }
         ProfScope ps(f.s);
         hipError_t e = launch_gemm_tiled(t, f.s);
-        ps.done(tiled_name(t), wbytes + xbytes, 2.0 * Mtot * rows * (double)p.K);
+        ps.done(gemm_tiled_name(t), wbytes + xbytes, 2.0 * Mtot * rows * (double)p.K);
         return e;
     }
     if (mfma) {
