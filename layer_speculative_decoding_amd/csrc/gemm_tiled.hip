@@ -18,10 +18,15 @@
 //    the weights two steps ahead of the matrix instructions (HBM latency),
 //    the activations one step ahead (they stay in L2);
 //  * the 64-row weight tile is chosen when 128-row tiles would leave CUs
-//    without a workgroup.
+//    without a workgroup, and when even those are too few, K is split: each
+//    K slice stores its float32 accumulators, and a second kernel adds the
+//    slices in slice order and applies the epilogue.
 #include "epilogue.h"
 #include "spec_device.h"
 #include "spec_kernels.h"
+
+#include <stdio.h>
+#include <stdlib.h>
 
 namespace spec {
 
@@ -32,7 +37,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBK = 64;           // K elements per step
 constexpr int kLDK = kBK + 8;     // LDS row stride in elements (16 bytes of padding)
-constexpr int kXcds = 8;
+constexpr int kWMB = 4;           // 16-row activation blocks per wave
+constexpr int kBM = 128;          // activation rows per tile (2 wave rows)
+constexpr int kMaxSplit = 8;
 
 __device__ __forceinline__ bf16x8 as_bf8(const uint4 &v) {
     bf16x8 r;
@@ -49,41 +56,107 @@ __device__ __forceinline__ float sum16(float v) {
 struct TileArgs {
     int gm, gn;        // activation tiles, weight tiles
     int parts;         // sum-of-squares partials per row and set member
-    int remap;         // number tiles XCD by XCD
+    int ks;            // K slices (1: no split)
+    int kc;            // K steps per slice
+    float *part;       // ks > 1: [ks][tile][WMB * WNB][256 lanes] float4
 };
 
+// Where tile t sits: first activation row, first weight row (unpaired), first
+// unit (paired), set member.
+struct TilePos {
+    int m0, n0, u0, sel;
+};
+template <int EPI, int BN>
+__device__ __forceinline__ TilePos tile_pos(const GemvParams &p, const TileArgs &ta, int t) {
+    TilePos q;
+    const int mt = t % ta.gm, nt = t / ta.gm;
+    q.m0 = mt * kBM;
+    q.u0 = nt * (BN / 2);
+    q.n0 = nt * BN;
+    if (epi_is_pair(EPI)) q.sel = ((q.u0 / (p.pair_block / 2)) * p.pair_block) / p.rows_per_sel;
+    else q.sel = q.n0 / p.rows_per_sel;
+    return q;
+}
+
+// The fused epilogue of one tile.  Lane (li, lg) of wave (wm, wn), register r
+// of block (a, c) holds activation row 64 wm + 16 a + 4 lg + r and unit
+// (NH / 2) wn + 16 (c % HB) + li of member c / HB.
+template <int EPI, int WNB>
+__device__ __forceinline__ void tile_epilogue(const GemvParams &p, const TileArgs &ta, const TilePos &q,
+                                              const f32x4 (&acc)[kWMB][WNB]) {
+    constexpr bool kPair = epi_is_pair(EPI);
+    constexpr int BN = 32 * WNB, NH = BN / 2, HB = WNB / 2;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int li = lane & 15, lg = lane >> 4;
+    float best_v = -INFINITY;
+    int best_i = 0;
+#pragma unroll
+    for (int a = 0; a < kWMB; ++a) {
+        float ssv[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = q.m0 + 64 * wm + 16 * a + 4 * lg + r;
+            if (m >= p.M) continue;
+#pragma unroll
+            for (int c = 0; c < HB; ++c) {
+                const int j = (NH / 2) * wn + 16 * c + li;
+                if constexpr (kPair) {
+                    const int hb = p.pair_block / 2, u = q.u0 + j;
+                    const int r0 = (u / hb) * p.pair_block + u % hb;
+                    epi_pair<uint16_t, EPI>(p, u, r0, r0 + hb, q.sel, m, acc[a][c][r], acc[a][c + HB][r]);
+                } else {
+                    epi_row<uint16_t, EPI>(p, q.n0 + j, q.sel, m, acc[a][c][r], ssv[r], best_v, best_i);
+                    epi_row<uint16_t, EPI>(p, q.n0 + NH + j, q.sel, m, acc[a][c + HB][r], ssv[r], best_v, best_i);
+                }
+            }
+        }
+        if constexpr (epi_has_ss(EPI)) {
+            if (p.n_norm_sel > 0 && (EPI == EPI_RESID_ADD || p.par_mlp || q.sel == 0)) {
+                const int si = (EPI == EPI_ATTN_OUT && p.par_mlp) ? q.sel : 0;
+                const int part = ((q.n0 - q.sel * p.rows_per_sel) / BN) * 2 + wn;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float s = sum16(ssv[r]);
+                    const int m = q.m0 + 64 * wm + 16 * a + 4 * lg + r;
+                    if (li == 0 && m < p.M)
+                        p.ss[(int64_t)si * p.ss_sel_stride + (int64_t)(p.m0 + m) * ta.parts + part] = s;
+                }
+            }
+        }
+    }
+}
+
 // 4 waves (2 x 2), each 64 activation rows x 16 WNB weight rows; K steps of
-// 64 through one LDS stage, with the global loads of step k + DIST issued
-// before step k's matrix instructions (DIST register sets in flight).
-template <int EPI, int WNB, int DIST>
+// 64 through one LDS stage, the weights of step k + 2 requested before step
+// k's matrix instructions, the activations of step k + 1.  SPLIT: workgroup
+// b covers tile b % T over K slice b / T and stores its accumulators.
+template <int EPI, int WNB, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void k_gemm_tile(GemvParams p, TileArgs ta) {
     constexpr bool kPair = epi_is_pair(EPI);
-    constexpr int WMB = 4, NWM = 2, NWN = 2;
-    constexpr int BM = 16 * WMB * NWM, BN = 16 * WNB * NWN, NH = BN / 2;
-    constexpr int HB = WNB / 2;                 // 16-unit blocks per wave per member
-    constexpr int RPP = 32;                     // rows per load pass (8 lanes x 16 bytes per row)
-    constexpr int LA = BM / RPP, LB = BN / RPP; // load passes per step
-    static_assert(WNB % 2 == 0 && BN % RPP == 0, "tile shape");
-    __shared__ __align__(16) uint16_t lds[(BM + BN) * kLDK];
+    constexpr int BN = 32 * WNB, NH = BN / 2;
+    constexpr int HB = WNB / 2;                  // 16-unit blocks per wave per member
+    constexpr int RPP = 32;                      // rows per load pass (8 lanes x 16 bytes per row)
+    constexpr int LA = kBM / RPP, LB = BN / RPP; // load passes per step
+    constexpr int DIST = 2;
+    __shared__ __align__(16) uint16_t lds[(kBM + BN) * kLDK];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave % NWM, wn = wave / NWM;
+    const int wm = wave & 1, wn = wave >> 1;
     const int li = lane & 15, lg = lane >> 4;
     const int K = p.K;
+    const int T = ta.gm * ta.gn;
+    const int t = SPLIT ? (int)blockIdx.x % T : (int)blockIdx.x;
+    const int slice = SPLIT ? (int)blockIdx.x / T : 0;
+    const TilePos q = tile_pos<EPI, BN>(p, ta, t);
+    const int kbeg = slice * ta.kc;
+    const int nk = SPLIT ? min(ta.kc, K / kBK - kbeg) : K / kBK;
 
-    const int L = blockIdx.x, T = ta.gm * ta.gn;
-    const int Q = (ta.remap && T % kXcds == 0) ? (L % kXcds) * (T / kXcds) + L / kXcds : L;
-    const int mt = Q % ta.gm, nt = Q / ta.gm;
-    const int m0 = mt * BM;
-    const int u0 = nt * NH;                    // first unit (pairs)
-    const int n0 = nt * BN;                    // first row (unpaired)
-    int sel;
-    if (kPair) sel = (((u0 / (p.pair_block / 2)) * p.pair_block) / p.rows_per_sel);
-    else sel = n0 / p.rows_per_sel;
     // operands as a uniform base plus 32-bit per-lane byte offsets
     const char *Xb = reinterpret_cast<const char *>(reinterpret_cast<const uint16_t *>(p.X) +
-                                                    (int64_t)sel * p.x_sel_stride + (int64_t)p.m0 * K);
-    const char *Wb = reinterpret_cast<const char *>(p.W);
+                                                    (int64_t)q.sel * p.x_sel_stride + (int64_t)p.m0 * K +
+                                                    (int64_t)kbeg * kBK);
+    const char *Wb = reinterpret_cast<const char *>(reinterpret_cast<const uint16_t *>(p.W) + (int64_t)kbeg * kBK);
 
     // loader: thread t moves 16 bytes of tile rows t / 8 + 32 i, elements 8 (t % 8)
     const int lr = tid >> 3, lc = 8 * (tid & 7);
@@ -91,19 +164,19 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(GemvParams p, TileArgs ta)
     bool va[LA];
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
-        const int m = m0 + lr + RPP * i;
+        const int m = q.m0 + lr + RPP * i;
         va[i] = m < p.M;
-        oa[i] = (uint32_t)(((va[i] ? m : 0) * K + lc) * 2);
+        oa[i] = ((uint32_t)(va[i] ? m : 0) * (uint32_t)K + (uint32_t)lc) * 2u;
     }
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
         const int r = lr + RPP * i;          // tile row: member r / NH, unit r % NH
         int w;
         if (kPair) {
-            const int hb = p.pair_block / 2, u = u0 + r % NH;
+            const int hb = p.pair_block / 2, u = q.u0 + r % NH;
             w = (u / hb) * p.pair_block + u % hb + (r / NH) * hb;
         } else {
-            w = n0 + r;
+            w = q.n0 + r;
         }
         ob[i] = (uint32_t)w * (uint32_t)K * 2u + (uint32_t)lc * 2u;
     }
@@ -123,32 +196,32 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(GemvParams p, TileArgs ta)
 #pragma unroll
         for (int i = 0; i < LA; ++i) *reinterpret_cast<uint4 *>(&lds[(lr + RPP * i) * kLDK + lc]) = xa[i];
 #pragma unroll
-        for (int i = 0; i < LB; ++i) *reinterpret_cast<uint4 *>(&lds[(BM + lr + RPP * i) * kLDK + lc]) = xb[i];
+        for (int i = 0; i < LB; ++i) *reinterpret_cast<uint4 *>(&lds[(kBM + lr + RPP * i) * kLDK + lc]) = xb[i];
     };
 
-    f32x4 acc[WMB][WNB];
+    f32x4 acc[kWMB][WNB];
 #pragma unroll
-    for (int a = 0; a < WMB; ++a)
+    for (int a = 0; a < kWMB; ++a)
 #pragma unroll
         for (int c = 0; c < WNB; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // LDS rows of this lane's fragments: activation block a, weight block c
     // (member c / HB, unit block c % HB of this wave column)
-    const int arow = (16 * WMB * wm + li) * kLDK + 8 * lg;
-    const int brow = (BM + (NH / NWN) * wn + li) * kLDK + 8 * lg;
+    const int arow = (64 * wm + li) * kLDK + 8 * lg;
+    const int brow = (kBM + (NH / 2) * wn + li) * kLDK + 8 * lg;
     auto compute = [&]() {
 #pragma unroll
         for (int ks = 0; ks < kBK / 32; ++ks) {
-            uint4 av[WMB], bv[WNB];
+            uint4 av[kWMB], bv[WNB];
 #pragma unroll
-            for (int a = 0; a < WMB; ++a)
+            for (int a = 0; a < kWMB; ++a)
                 av[a] = *reinterpret_cast<const uint4 *>(&lds[arow + 16 * a * kLDK + 32 * ks]);
 #pragma unroll
             for (int c = 0; c < WNB; ++c)
                 bv[c] = *reinterpret_cast<const uint4 *>(
                     &lds[brow + ((c / HB) * NH + 16 * (c % HB)) * kLDK + 32 * ks]);
 #pragma unroll
-            for (int a = 0; a < WMB; ++a)
+            for (int a = 0; a < kWMB; ++a)
 #pragma unroll
                 for (int c = 0; c < WNB; ++c)
                     acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(av[a]), as_bf8(bv[c]), acc[a][c],
@@ -156,7 +229,6 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(GemvParams p, TileArgs ta)
         }
     };
 
-    const int nk = K / kBK;
     load_x(0);
 #pragma unroll
     for (int d = 0; d < DIST; ++d)
@@ -176,66 +248,59 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(GemvParams p, TileArgs ta)
         }
     }
 
-    // epilogue: lane (li, lg), register r of block (a, c) holds activation
-    // row 16 WMB wm + 16 a + 4 lg + r and unit (NH / NWN) wn + 16 (c % HB) + li
-    // of member c / HB
-    float best_v = -INFINITY;
-    int best_i = 0;
+    if constexpr (SPLIT) {
+        float4 *dst = reinterpret_cast<float4 *>(ta.part) + ((int64_t)slice * T + t) * (kWMB * WNB) * 256 + tid;
 #pragma unroll
-    for (int a = 0; a < WMB; ++a) {
-        float ssv[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int a = 0; a < kWMB; ++a)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = m0 + 16 * WMB * wm + 16 * a + 4 * lg + r;
-            if (m >= p.M) continue;
-#pragma unroll
-            for (int c = 0; c < HB; ++c) {
-                const int j = (NH / NWN) * wn + 16 * c + li;
-                if constexpr (kPair) {
-                    const int hb = p.pair_block / 2, u = u0 + j;
-                    const int r0 = (u / hb) * p.pair_block + u % hb;
-                    epi_pair<uint16_t, EPI>(p, u, r0, r0 + hb, sel, m, acc[a][c][r], acc[a][c + HB][r]);
-                } else {
-                    epi_row<uint16_t, EPI>(p, n0 + j, sel, m, acc[a][c][r], ssv[r], best_v, best_i);
-                    epi_row<uint16_t, EPI>(p, n0 + NH + j, sel, m, acc[a][c + HB][r], ssv[r], best_v, best_i);
-                }
-            }
-        }
-        if constexpr (epi_has_ss(EPI)) {
-            if (p.n_norm_sel > 0 && (EPI == EPI_RESID_ADD || p.par_mlp || sel == 0)) {
-                const int si = (EPI == EPI_ATTN_OUT && p.par_mlp) ? sel : 0;
-                const int part = ((n0 - sel * p.rows_per_sel) / BN) * NWN + wn;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float s = sum16(ssv[r]);
-                    const int m = m0 + 16 * WMB * wm + 16 * a + 4 * lg + r;
-                    if (li == 0 && m < p.M)
-                        p.ss[(int64_t)si * p.ss_sel_stride + (int64_t)(p.m0 + m) * ta.parts + part] = s;
-                }
-            }
-        }
+            for (int c = 0; c < WNB; ++c)
+                dst[(a * WNB + c) * 256] = make_float4(acc[a][c][0], acc[a][c][1], acc[a][c][2], acc[a][c][3]);
+    } else {
+        tile_epilogue<EPI, WNB>(p, ta, q, acc);
     }
 }
 
-template <int WNB, int DIST, int EPI>
-void launch_one(const GemvParams &p, const TileArgs &ta, hipStream_t s) {
-    hipLaunchKernelGGL((k_gemm_tile<EPI, WNB, DIST>), dim3(ta.gm * ta.gn), dim3(256), 0, s, p, ta);
+// Sum of a split product's K slices (in slice order) and its epilogue; one
+// workgroup per tile, lanes as in the product kernel.
+template <int EPI, int WNB>
+__global__ __launch_bounds__(256) void k_gemm_tile_epi(GemvParams p, TileArgs ta) {
+    constexpr int BN = 32 * WNB;
+    const int T = ta.gm * ta.gn, t = blockIdx.x;
+    const float4 *src = reinterpret_cast<const float4 *>(ta.part) + (int64_t)t * (kWMB * WNB) * 256 + threadIdx.x;
+    f32x4 acc[kWMB][WNB];
+#pragma unroll
+    for (int a = 0; a < kWMB; ++a)
+#pragma unroll
+        for (int c = 0; c < WNB; ++c) {
+            float4 s = src[(a * WNB + c) * 256];
+            for (int k = 1; k < ta.ks; ++k) {
+                const float4 v = src[((int64_t)k * T * (kWMB * WNB) + a * WNB + c) * 256];
+                s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+            }
+            acc[a][c] = f32x4{s.x, s.y, s.z, s.w};
+        }
+    tile_epilogue<EPI, WNB>(p, ta, tile_pos<EPI, BN>(p, ta, t), acc);
 }
 
-template <int WNB, int DIST>
-hipError_t launch_shape(const GemvParams &p, int remap, hipStream_t s) {
-    constexpr int BM = 128, BN = 32 * WNB;
-    TileArgs ta;
-    ta.gm = (p.M + BM - 1) / BM;
-    ta.gn = (p.n_units * 2) / BN;
-    ta.parts = (p.rows_per_sel / BN) * 2;
-    ta.remap = remap;
+template <int WNB, int EPI>
+void launch_one(const GemvParams &p, const TileArgs &ta, hipStream_t s) {
+    const int T = ta.gm * ta.gn;
+    if (ta.ks > 1) {
+        hipLaunchKernelGGL((k_gemm_tile<EPI, WNB, true>), dim3(T * ta.ks), dim3(256), 0, s, p, ta);
+        hipLaunchKernelGGL((k_gemm_tile_epi<EPI, WNB>), dim3(T), dim3(256), 0, s, p, ta);
+    } else {
+        hipLaunchKernelGGL((k_gemm_tile<EPI, WNB, false>), dim3(T), dim3(256), 0, s, p, ta);
+    }
+}
+
+template <int WNB>
+hipError_t launch_shape(const GemvParams &p, TileArgs ta, hipStream_t s) {
     switch (p.epi) {
-    case EPI_STORE: launch_one<WNB, DIST, EPI_STORE>(p, ta, s); break;
-    case EPI_QKV_ROPE: launch_one<WNB, DIST, EPI_QKV_ROPE>(p, ta, s); break;
-    case EPI_SILU_MUL: launch_one<WNB, DIST, EPI_SILU_MUL>(p, ta, s); break;
-    case EPI_RESID_ADD: launch_one<WNB, DIST, EPI_RESID_ADD>(p, ta, s); break;
-    case EPI_ATTN_OUT: launch_one<WNB, DIST, EPI_ATTN_OUT>(p, ta, s); break;
+    case EPI_STORE: launch_one<WNB, EPI_STORE>(p, ta, s); break;
+    case EPI_QKV_ROPE: launch_one<WNB, EPI_QKV_ROPE>(p, ta, s); break;
+    case EPI_SILU_MUL: launch_one<WNB, EPI_SILU_MUL>(p, ta, s); break;
+    case EPI_RESID_ADD: launch_one<WNB, EPI_RESID_ADD>(p, ta, s); break;
+    case EPI_ATTN_OUT: launch_one<WNB, EPI_ATTN_OUT>(p, ta, s); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -247,22 +312,47 @@ bool fits(const GemvParams &p, int bn) {
     return p.rows_per_sel % bn == 0;
 }
 
-// Launch choice (overridable for measurement: SPEC_TILE = "<bn> <dist> <remap>").
+// Launch choice: tile width bn and K slices.  SPEC_TILE="<bn> <slices>"
+// overrides it (read at every call, for measurement and tests).
 struct Pick {
-    int bn, dist, remap;
+    int bn, ks;
 };
-Pick pick(const GemvParams &p) {
-    static const Pick forced = [] {
-        Pick f{0, 0, 0};
-        if (const char *e = getenv("SPEC_TILE")) sscanf(e, "%d %d %d", &f.bn, &f.dist, &f.remap);
-        return f;
-    }();
-    const int rows = p.n_units * 2;
-    if (forced.bn && fits(p, forced.bn)) return forced;
-    const int gm = (p.M + 127) / 128;
-    if (fits(p, 128) && (int64_t)gm * (rows / 128) >= 256) return {128, 2, 0};
-    if (fits(p, 64)) return {64, 2, 0};
-    return {0, 0, 0};
+Pick pick(const GemvParams &p, size_t part_bytes) {
+    const int rows = p.n_units * 2, nk = p.K / kBK;
+    const int gm = (p.M + kBM - 1) / kBM;
+    Pick k{0, 1};
+    if (const char *e = getenv("SPEC_TILE")) {
+        Pick f{0, 1};
+        if (sscanf(e, "%d %d", &f.bn, &f.ks) >= 1 && (f.bn == 64 || f.bn == 128) && fits(p, f.bn)) k = f;
+    }
+    if (k.bn == 0) {
+        if (fits(p, 128) && (int64_t)gm * (rows / 128) >= 256) return {128, 1};
+        if (!fits(p, 64)) return {0, 1};
+        k.bn = 64;
+        // fewer than 384 tiles: slices so that about 1024 workgroups run,
+        // each over >= 2 K steps (more tiles run better unsplit: the
+        // slices' float32 partials cost a write and a read each)
+        const int64_t T = (int64_t)gm * (rows / 64);
+        k.ks = T >= 384 ? 1 : (int)((1024 + T - 1) / T);
+    }
+    k.ks = k.ks < 1 ? 1 : (k.ks > kMaxSplit ? kMaxSplit : k.ks);
+    if (k.ks > nk / 2) k.ks = nk / 2 < 1 ? 1 : nk / 2;
+    // the partial buffer bounds the slices
+    const int64_t tile_bytes = (int64_t)gm * (rows / k.bn) * kBM * k.bn * 4;
+    while (k.ks > 1 && (size_t)(tile_bytes * k.ks) > part_bytes) --k.ks;
+    return k;
+}
+
+TileArgs tile_args(const GemvParams &p, Pick k, float *part) {
+    TileArgs ta;
+    const int nk = p.K / kBK;
+    ta.gm = (p.M + kBM - 1) / kBM;
+    ta.gn = (p.n_units * 2) / k.bn;
+    ta.parts = (p.rows_per_sel / k.bn) * 2;
+    ta.kc = (nk + k.ks - 1) / k.ks;
+    ta.ks = (nk + ta.kc - 1) / ta.kc;      // every slice non-empty
+    ta.part = part;
+    return ta;
 }
 
 }  // namespace
@@ -271,26 +361,30 @@ int gemm_tiled_min_rows() { return 64; }
 
 bool gemm_tiled_supported(const GemvParams &p) {
     if (p.K % kBK != 0 || p.epi == EPI_LOGITS || p.M < 1) return false;
-    return pick(p).bn != 0;
+    return pick(p, 0).bn != 0;
 }
 
 // Sum-of-squares partials per row and set member a residual writer leaves
 // (two per weight tile: one per wave column).
-int gemm_tiled_parts(const GemvParams &p) { return (p.rows_per_sel / pick(p).bn) * 2; }
+int gemm_tiled_parts(const GemvParams &p) { return (p.rows_per_sel / pick(p, 0).bn) * 2; }
 
-std::string gemm_tiled_name(const GemvParams &p) {
-    const Pick k = pick(p);
-    return "k_gemm_tile<" + std::to_string(p.epi) + ", " + std::to_string(k.bn / 32) + ", " +
-           std::to_string(k.dist) + ">";
+std::string gemm_tiled_name(const GemvParams &p, size_t part_bytes) {
+    const Pick k = pick(p, part_bytes);
+    const TileArgs ta = tile_args(p, k, nullptr);
+    return "k_gemm_tile<" + std::to_string(p.epi) + ", " + std::to_string(k.bn / 32) +
+           (ta.ks > 1 ? ", split " + std::to_string(ta.ks) + ">" : ">");
 }
+
+size_t gemm_tiled_part_bytes() { return (size_t)64 << 20; }
 
 // p.n_units: row pairs (rows / 2) as for the other products; p.M rows from
 // p.m0 (the kernel reads X rows m0 .. m0 + M - 1 and the epilogue writes them).
-hipError_t launch_gemm_tiled(const GemvParams &p, hipStream_t s) {
+hipError_t launch_gemm_tiled(const GemvParams &p, float *part, size_t part_bytes, hipStream_t s) {
     if (!gemm_tiled_supported(p)) return hipErrorInvalidValue;
-    const Pick k = pick(p);
-    if (k.bn == 128) return k.dist == 2 ? launch_shape<4, 2>(p, k.remap, s) : launch_shape<4, 1>(p, k.remap, s);
-    return k.dist == 2 ? launch_shape<2, 2>(p, k.remap, s) : launch_shape<2, 1>(p, k.remap, s);
+    const Pick k = pick(p, part ? part_bytes : 0);
+    const TileArgs ta = tile_args(p, k, part);
+    if (k.bn == 128) return launch_shape<4>(p, ta, s);
+    return launch_shape<2>(p, ta, s);
 }
 
 }  // namespace spec

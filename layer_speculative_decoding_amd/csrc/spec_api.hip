@@ -108,7 +108,7 @@ std::string mfma_name(int M, int epi, int ks) {
 
 // Workspace layout for R activation rows and sets of at most G layers.
 struct Carve {
-    size_t h, h0, abuf, xn, q, o, act, pacc, pml, pval, pidx, ss, rope, total;
+    size_t h, h0, abuf, xn, q, o, act, pacc, pml, pval, pidx, ss, rope, tpart, tpart_bytes, total;
     int64_t ss_sel_stride;   // floats per set member in ss
 };
 
@@ -137,6 +137,9 @@ Carve carve(const spec_model *m, int batch, int max_m, int G) {
     c.ss_sel_stride = (int64_t)R * kPartialsMax;
     c.ss = take(nsel * R * kPartialsMax * 4);
     c.rope = take(R * (hd / 2) * 8);
+    // K-slice partials of the tiled products (prompt-length calls only)
+    c.tpart_bytes = R >= (size_t)gemm_tiled_min_rows() ? gemm_tiled_part_bytes() : 0;
+    c.tpart = take(c.tpart_bytes);
     c.total = off;
     return c;
 }
@@ -216,8 +219,9 @@ hipError_t product(const Fwd &f, GemvParams p, int *parts_out = nullptr) {
             xbytes *= n_sel;
         }
         ProfScope ps(f.s);
-        hipError_t e = launch_gemm_tiled(t, f.s);
-        ps.done(gemm_tiled_name(t), wbytes + xbytes, 2.0 * Mtot * rows * (double)p.K);
+        float *part = f.c.tpart_bytes ? at<float>(f.ws, f.c.tpart) : nullptr;
+        hipError_t e = launch_gemm_tiled(t, part, f.c.tpart_bytes, f.s);
+        ps.done(gemm_tiled_name(t, f.c.tpart_bytes), wbytes + xbytes, 2.0 * Mtot * rows * (double)p.K);
         return e;
     }
     if (mfma) {

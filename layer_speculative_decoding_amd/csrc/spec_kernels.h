@@ -112,15 +112,17 @@ int gemv_grid(const GemvParams &p, int ks);
 hipError_t launch_gemm_mfma(const GemvParams &p, int grid, int ks, hipStream_t s);
 // Tiled matrix-core GEMM (bf16) for prompt-length row counts: every row of
 // the call in one launch (p.m0 = 0, p.M = rows), K a multiple of 64, no
-// LOGITS epilogue, a set member's rows a whole number of 128-row tiles (units
-// of 64 pairs for the paired epilogues).  n_units as for the VALU GEMV (row
-// pairs).  Residual writers leave gemm_tiled_parts(p) partials per row and
-// set member.
-hipError_t launch_gemm_tiled(const GemvParams &p, hipStream_t s);
+// LOGITS epilogue, a set member's rows a whole number of 64-row tiles (32
+// units for the paired epilogues).  n_units as for the VALU GEMV (row pairs).
+// part: float32 scratch of part_bytes (at most gemm_tiled_part_bytes() is
+// used) for the K slices of small products; NULL: no K split.  Residual
+// writers leave gemm_tiled_parts(p) partials per row and set member.
+hipError_t launch_gemm_tiled(const GemvParams &p, float *part, size_t part_bytes, hipStream_t s);
 bool gemm_tiled_supported(const GemvParams &p);
 int gemm_tiled_min_rows();
 int gemm_tiled_parts(const GemvParams &p);
-std::string gemm_tiled_name(const GemvParams &p);   // kernel instance, for measurement
+size_t gemm_tiled_part_bytes();
+std::string gemm_tiled_name(const GemvParams &p, size_t part_bytes);   // kernel instance, for measurement
 // X_NORM operands written once as activation-dtype rows xn[sel][m][K] for
 // rows m0 .. m0 + M - 1 (the matrix-core products then read them plainly).
 hipError_t launch_norm_rows(int dtype, const GemvParams &p, int n_sel, void *xn, hipStream_t s);

@@ -191,15 +191,19 @@ def test_draft_group_step_matches_oracle(name, mlp, inv_temp):
 
 
 @pytest.mark.parametrize("name", ["gqa-bf16", "hd64-bias-bf16", "hd128-bf16"])
-def test_prompt_prefill_matches_oracle(name):
+@pytest.mark.parametrize("tile", [None, "64 3", "128 1"])
+def test_prompt_prefill_matches_oracle(name, tile, monkeypatch):
     """Prompt-length row counts (several 128-row activation tiles and a ragged
     last tile) through the tiled matrix-core products: base-style verify
     prefill with every row's logits, and draft-style calibration prefill with
-    ragged prompt lengths."""
+    ragged prompt lengths.  `tile` forces the tile width and the number of K
+    slices (3 slices over 4..16 K steps: ragged last slice)."""
     from layer_speculative_decoding_amd import api
+    if tile is not None:
+        monkeypatch.setenv("SPEC_TILE", tile)
     B, P = 2, 150
     shape, tol, om, gm, gkv, okv, prompts = _setup(name, B, P, cap=P + 8)
-    say(f"prompt prefill {name} B={B} P={P}")
+    say(f"prompt prefill {name} B={B} P={P} tile={tile}")
     w = ws(api.spec_workspace_bytes(gm, B, P, 1))
     logits = torch.zeros(B, P, shape.vocab, device="cuda")
     api.spec_verify_forward(gm, gkv, B, i32(prompts), i32([0, 0]), P, P - 1, logits, w)
