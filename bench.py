@@ -98,6 +98,60 @@ def pmc_summary(fetch_csv, write_csv, kernel, command):
     print(f"source_sha256: {kernel_source_hash()}")
 
 
+def pmc_mfma_summary(csv_path, command):
+    """Markdown summary of one counter run of `bench.py --pmc-probe` with the
+    matrix-core counters: per kernel family, the matrix-core flops the
+    hardware counted (MOPS x 512), the dispatch durations (the run's own
+    timestamps; counter runs serialise dispatches) and the MFMA-busy share of
+    the SIMDs: SQ_VALU_MFMA_BUSY_CYCLES / (active cycles x 1024 SIMDs), where
+    the active cycles are GRBM_GUI_ACTIVE / 8 (the CSV value sums the eight
+    XCDs' GRBM instances; per XCD it tracks the dispatch's duration at the
+    shader clock)."""
+    import csv
+    import re
+    disp = {}
+    for r in csv.DictReader(open(csv_path)):
+        d = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"],
+                                                    "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    fam = {}
+    for d in disp.values():
+        m = re.search(r"(k_\w+)<([^()]*)>\(", d["name"])
+        if not m:
+            continue
+        key = f"{m.group(1)}<{m.group(2)}>"
+        f = fam.setdefault(key, {"n": 0, "ns": 0.0, "bf16": 0.0, "f32": 0.0, "busy": 0.0, "gui": 0.0})
+        f["n"] += 1
+        f["ns"] += d["ns"]
+        f["bf16"] += d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+        f["f32"] += d.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0.0) * 512
+        f["busy"] += d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        f["gui"] += d.get("GRBM_GUI_ACTIVE", 0.0)
+    print("# Matrix-core utilisation per kernel (hardware counters)")
+    print()
+    print("Commands (from the repository root, TMPDIR=/tmp):")
+    print()
+    for c in command:
+        print(f"    {c}")
+    print()
+    print("The run covers the llama-1b-8b workload: three prompt prefills (base 511 rows, draft 512 rows:"
+          " k_gemm_tile), then four rounds of draft steps (k_gemv, one row), verify and calibration (k_gemm_mfma,"
+          " 6 rows) and attention (k_attn, float32 matrix instructions).  Flops are what the matrix cores"
+          " executed (padding rows included); the bf16 peak is 2500 TFLOP/s, the float32 one 157.3.")
+    print()
+    top, ft = max(fam.items(), key=lambda kv: kv[1]["ns"])
+    print(f"GRBM_GUI_ACTIVE / 8 per ns of `{top}` (the longest-running kernel): {ft['gui'] / 8 / ft['ns']:.2f} GHz.")
+    print()
+    print("| kernel | dispatches | avg us | MFMA bf16 TFLOP/s | of bf16 peak | MFMA f32 TFLOP/s | MFMA busy |")
+    print("|---|---|---|---|---|---|---|")
+    for key, f in sorted(fam.items(), key=lambda kv: -kv[1]["ns"]):
+        sec = f["ns"] * 1e-9
+        bf, f32 = f["bf16"] / sec / 1e12, f["f32"] / sec / 1e12
+        busy = f["busy"] / (f["gui"] / 8 * 1024) if f["gui"] else 0.0
+        print(f"| `{key}` | {f['n']} | {f['ns'] / f['n'] / 1e3:.1f} | {bf:.1f} | {bf / MFMA_BF16_PEAK_TFS:.1%} | "
+              f"{f32:.2f} | {busy:.1%} |")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -131,7 +185,16 @@ def main():
                     help="run a few rounds and one device copy of known size, for hardware-counter runs")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL"),
                     help="print the traffic summary of two counter runs of --pmc-probe")
+    ap.add_argument("--pmc-mfma-summary", metavar="CSV",
+                    help="print the matrix-core utilisation summary of a counter run of --pmc-probe")
     args = ap.parse_args()
+    if args.pmc_mfma_summary:
+        pmc_mfma_summary(args.pmc_mfma_summary, [
+            "timeout -s KILL 240 rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 "
+            "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d gpurun_out/pmc_mfma -o run "
+            "-- python bench.py --warmup 1 --pmc-probe",
+            f"python bench.py --pmc-mfma-summary {args.pmc_mfma_summary} > profiles/mfma_util.md"])
+        return
     if args.pmc_summary:
         f, w, kname = args.pmc_summary
         pmc_summary(f, w, kname, [
