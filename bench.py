@@ -152,6 +152,71 @@ def pmc_mfma_summary(csv_path, command):
               f"{f32:.2f} | {busy:.1%} |")
 
 
+def rocprof_summary(stats_csv, trace_csv, command):
+    """Markdown summary of a `rocprofv3 --kernel-trace --stats` run of the
+    default workload: the per-kernel statistics, then the kernels of one
+    steady-state round split into its phases (a round runs calibration, the
+    draft steps, verify, accept; every calibration and draft step ends with
+    k_sample_reduce, accept starts with k_acc_stats)."""
+    import collections
+    import csv
+
+    def short(n):
+        n = n.replace("spec::(anonymous namespace)::", "").replace("void ", "")
+        return n.split("(spec::")[0].split("(float const")[0][:70]
+
+    rows = list(csv.DictReader(open(stats_csv)))
+    print("# rocprofv3 kernel statistics: llama-1b-8b workload (bench.py default)")
+    print()
+    print("Workload: Llama-3.2-1B-shaped draft -> Llama-3-8B-shaped base, bf16, vocab 128256, 512-token prompt, "
+          "k = 5, layer-parallel set size N = 2, batch 1, greedy; three prompt prefills (k_gemm_tile: base 511 "
+          "rows, draft 512 rows), 2 warm-up + 10 timed + 5 instrumented rounds, and the weight generation "
+          "(the at::native kernels).  Template arguments: k_gemm_mfma<row tiles, epilogue, waves per block>, "
+          "k_gemv<type, rows, epilogue, operand mode>, k_gemm_tile<epilogue, 32-row weight blocks, K split>; "
+          "epilogues 0 store, 1 QKV RoPE + KV append, 2 SiLU gate, 3 residual add, 4 logits + arg-max, "
+          "5 attention-output routing.")
+    print()
+    print("Commands (from the repository root, TMPDIR=/tmp):")
+    print()
+    for c in command:
+        print(f"    {c}")
+    print()
+    print("Source: run_kernel_stats.csv (durations in microseconds).")
+    print()
+    print("| kernel | calls | avg us | min us | max us | total ms | % |")
+    print("|---|---|---|---|---|---|---|")
+    for r in rows[:24]:
+        print(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+              f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+              f"{float(r['TotalDurationNs']) / 1e6:.2f} | {float(r['Percentage']):.1f} |")
+    tr = list(csv.DictReader(open(trace_csv)))
+    tr.sort(key=lambda r: int(r["Start_Timestamp"]))
+    ks = [(short(r["Kernel_Name"]), int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
+           int(r["Grid_Size_X"]) // max(int(r["Workgroup_Size_X"]), 1), int(r["Workgroup_Size_X"])) for r in tr]
+    idx = [i for i, r in enumerate(ks) if r[0] == "k_acc_stats"]
+    seg = ks[idx[-2]:idx[-1]]
+    sr = [i for i, r in enumerate(seg) if r[0] == "k_sample_reduce"]
+    phases = {"calibration (a + 1 rows: 1 at acceptance 0)": seg[3:sr[0] + 1],
+              "one draft step (1 row)": seg[sr[0] + 1:sr[1] + 1], "verify (k + 1 = 6 rows)": seg[sr[-1] + 1:]}
+    print()
+    print("One steady-state round from run_kernel_trace.csv (the last instrumented round; busy = sum of kernel "
+          "durations, which excludes the profiler's own dispatch gaps):")
+    for name, st in phases.items():
+        busy = sum(r[2] - r[1] for r in st) / 1e3
+        print()
+        print(f"**{name}**: {len(st)} kernels, busy {busy:.1f} us")
+        print()
+        print("| kernel | grid x block | launches | total us | avg us |")
+        print("|---|---|---|---|---|")
+        agg = collections.defaultdict(lambda: [0, 0.0])
+        for r in st:
+            key = (r[0], f"{r[3]} x {r[4]}")
+            agg[key][0] += 1
+            agg[key][1] += (r[2] - r[1]) / 1e3
+        for k, v in sorted(agg.items(), key=lambda x: -x[1][1])[:10]:
+            print(f"| {k[0]} | {k[1]} | {v[0]} | {v[1]:.1f} | {v[1] / v[0]:.2f} |")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -187,7 +252,16 @@ def main():
                     help="print the traffic summary of two counter runs of --pmc-probe")
     ap.add_argument("--pmc-mfma-summary", metavar="CSV",
                     help="print the matrix-core utilisation summary of a counter run of --pmc-probe")
+    ap.add_argument("--rocprof-summary", nargs=2, metavar=("STATS_CSV", "TRACE_CSV"),
+                    help="print the kernel statistics and one round's phases of a kernel-trace run")
     args = ap.parse_args()
+    if args.rocprof_summary:
+        st, tr = args.rocprof_summary
+        rocprof_summary(st, tr, [
+            "timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof -o run "
+            "-- python bench.py --steps 10 --warmup 2 --no-cpu-baseline --no-vanilla",
+            f"python bench.py --rocprof-summary {st} {tr} > profiles/kernel_stats_llama-1b-8b_k5_N2.md"])
+        return
     if args.pmc_mfma_summary:
         pmc_mfma_summary(args.pmc_mfma_summary, [
             "timeout -s KILL 240 rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 "

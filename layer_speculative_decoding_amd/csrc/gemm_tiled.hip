@@ -267,18 +267,27 @@ __global__ __launch_bounds__(256) void k_gemm_tile_epi(GemvParams p, TileArgs ta
     constexpr int BN = 32 * WNB;
     const int T = ta.gm * ta.gn, t = blockIdx.x;
     const float4 *src = reinterpret_cast<const float4 *>(ta.part) + (int64_t)t * (kWMB * WNB) * 256 + threadIdx.x;
+    // slice by slice, all of a slice's blocks requested before any is added
     f32x4 acc[kWMB][WNB];
 #pragma unroll
     for (int a = 0; a < kWMB; ++a)
 #pragma unroll
         for (int c = 0; c < WNB; ++c) {
-            float4 s = src[(a * WNB + c) * 256];
-            for (int k = 1; k < ta.ks; ++k) {
-                const float4 v = src[((int64_t)k * T * (kWMB * WNB) + a * WNB + c) * 256];
-                s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-            }
-            acc[a][c] = f32x4{s.x, s.y, s.z, s.w};
+            const float4 v = src[(a * WNB + c) * 256];
+            acc[a][c] = f32x4{v.x, v.y, v.z, v.w};
         }
+    for (int k = 1; k < ta.ks; ++k) {
+        const float4 *sk = src + (int64_t)k * T * (kWMB * WNB) * 256;
+        float4 v[kWMB][WNB];
+#pragma unroll
+        for (int a = 0; a < kWMB; ++a)
+#pragma unroll
+            for (int c = 0; c < WNB; ++c) v[a][c] = sk[(a * WNB + c) * 256];
+#pragma unroll
+        for (int a = 0; a < kWMB; ++a)
+#pragma unroll
+            for (int c = 0; c < WNB; ++c) acc[a][c] += f32x4{v[a][c].x, v[a][c].y, v[a][c].z, v[a][c].w};
+    }
     tile_epilogue<EPI, WNB>(p, ta, tile_pos<EPI, BN>(p, ta, t), acc);
 }
 

@@ -178,6 +178,82 @@ def test_fullsize_forward_entry_points(cfg_name, which, ctx, batch, layers):
     torch.cuda.empty_cache()
 
 
+PREFILL_CASES = [
+    # (config, which model, prompt rows per sequence, batch, layers of the model to keep)
+    ("llama-1b-8b", "draft", 512, 1, None),
+    ("llama-1b-8b", "base", 511, 1, None),
+    ("qwen-0.5b-7b", "draft", 1024, 1, None),
+    ("qwen-0.5b-7b", "base", 1023, 1, 8),
+    ("llama-8b-70b", "base", 256, 4, 2),
+]
+
+
+@pytest.mark.parametrize("cfg_name,which,P,batch,layers", PREFILL_CASES)
+def test_fullsize_prompt_prefill(cfg_name, which, P, batch, layers):
+    """The prompt prefill at the workload's shapes, through the tiled
+    matrix-core products the benchmark's prefill runs: the draft's
+    calibration over the whole prompt (last-row logits and the sampled d_1)
+    and the base's prefill (here with every row's logits), each with the KV
+    it writes, against the oracle."""
+    from layer_speculative_decoding_amd import api
+    cfg = get_config(cfg_name)
+    shape = cfg.draft if which == "draft" else cfg.base
+    seed = cfg.seed_draft if which == "draft" else cfg.seed_base
+    say(f"fullsize prefill {cfg_name} {which} P={P} B={batch} layers={layers or shape.n_layers}")
+    sh, w, gm, gkv, om, okv = _setup(shape, seed, batch, 0, P, layers)
+    rng = np.random.default_rng(seed + 3)
+    V = sh.vocab
+    toks = rng.integers(0, V, size=(batch, P)).astype(np.int32)
+    wsb = ws(api.spec_workspace_bytes(gm, batch, P, 1))
+    zero = i32([0] * batch)
+    tols = []
+    if which == "draft":
+        inv_t = float(np.float32(1.0 / cfg.temperatures[-1])) if cfg.temperatures[-1] > 0 else 1.0
+        last = torch.zeros(batch, V, device="cuda")
+        out = torch.zeros(batch, dtype=torch.int32, device="cuda")
+        api.spec_calibrate_kv(gm, gkv, batch, i32(toks), zero, None, P, P - 1, inv_t, 79, last, V, out, 1, wsb)
+        torch.cuda.synchronize()
+        zg, tg = last.cpu().numpy(), out.cpu().numpy()
+        for b in range(batch):
+            fn = lambda kv: forward(om, kv, b, toks[b], range(P), logits="last")
+            zo, zn = _sensitive(fn, okv)
+            forward(om, okv, b, toks[b], range(P), logits=None)       # the KV it writes
+            err, tol = rel_linf(zg[b], zo), _tol(zo, zn)
+            tols.append(tol)
+            say(f"  calibrate prefill b={b} logits rel {err:.2e} (self-sensitivity {rel_linf(zn, zo):.2e})")
+            assert err < tol
+            t_or, mg = sample_from_logits(zo, inv_t, 79, b, P, philox.DRAFT)
+            if mg >= exclusion(zg[b], zo, inv_t):
+                assert tg[b] == t_or
+    else:
+        logits = torch.zeros(batch, P, V, device="cuda")
+        api.spec_verify_forward(gm, gkv, batch, i32(toks), zero, P, P - 1, logits, wsb)
+        torch.cuda.synchronize()
+        zg = logits.cpu().numpy()
+        del logits
+        for b in range(batch):
+            fn = lambda kv: forward(om, kv, b, toks[b], range(P), logits="all")
+            zo, zn = _sensitive(fn, okv)
+            forward(om, okv, b, toks[b], range(P), logits=None)
+            err, tol = rel_linf(zg[b], zo), _tol(zo, zn)
+            tols.append(tol)
+            say(f"  base prefill b={b} logits rel {err:.2e} (self-sensitivity {rel_linf(zn, zo):.2e})")
+            assert err < tol
+            srt = np.sort(zo, axis=1)
+            ok = (srt[:, -1] - srt[:, -2]) >= exclusion(zg[b], zo, 0.0)
+            np.testing.assert_array_equal(np.argmax(zg[b], 1)[ok], np.argmax(zo, 1)[ok])
+    kg, vg = gkv.k.float().cpu().numpy(), gkv.v.float().cpu().numpy()
+    for b in range(batch):
+        e0 = rel_linf(kg[0, b, :, :P], okv.k[0, b, :, :P])
+        ek = rel_linf(kg[:, b, :, :P], okv.k[:, b, :, :P])
+        ev = rel_linf(vg[:, b, :, :P], okv.v[:, b, :, :P])
+        say(f"  prefill KV b={b}: layer 0 K rel {e0:.2e}, all layers K {ek:.2e} V {ev:.2e}")
+        assert e0 < 1e-2 and ek < tols[b] and ev < tols[b], (e0, ek, ev)
+    del gm, w, om, okv, gkv
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("cfg_name", ["llama-1b-8b", "qwen-0.5b-7b", "llama-8b-70b"])
 def test_fullsize_accept_resample(cfg_name):
     """accept / resample at the workload's vocabulary, batch and k, on logits
