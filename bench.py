@@ -246,6 +246,9 @@ def main():
     ap.add_argument("--temperature", type=float, default=0.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-vanilla", action="store_true")
+    ap.add_argument("--n1-compare", action="store_true",
+                    help="also run the timed rounds with the sequential draft plan (N = 1) and report its "
+                         "acceptance and tokens/s")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run a few rounds and one device copy of known size, for hardware-counter runs")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL"),
@@ -286,7 +289,6 @@ def main():
     import torch
     from layer_speculative_decoding_amd import api
     from layer_speculative_decoding_amd.runtime import SpecDecoder, VanillaDecoder
-    from oracle.plan import default_group_plan, plan_offsets
     from synth import get_config, make_prompts, make_weights
 
     cfg = get_config(args.config)
@@ -302,8 +304,8 @@ def main():
     bw = make_weights(cfg.base, cfg.seed_base, device=dev)
     torch.cuda.synchronize()
     log(f"  weights ready in {time.time() - t0:.1f}s")
-    sets = default_group_plan(cfg.draft.n_layers, cfg.group_size)
-    offs = plan_offsets(sets)
+    offs = api.spec_default_group_plan(cfg.draft.n_layers, cfg.group_size)
+    seq_offs = list(range(cfg.draft.n_layers + 1))      # every layer its own stage (N = 1)
     P = cfg.prompt_len
     rounds_cap = W + K + 4
     cap = P + rounds_cap * (k + 1) + k + 2
@@ -408,6 +410,45 @@ def main():
     mf_ms, mf_fl = sum(v[1] for v in mf.values()), sum(v[3] for v in mf.values())
     mf_tfs = mf_fl / (mf_ms * 1e-3) / 1e12 if mf_ms > 0 else 0.0
 
+    # drafting speedup of the layer-parallel plan over the sequential draft
+    # (every layer its own stage): the k-1 draft steps of a round, at the
+    # round's current positions, each plan timed alternately
+    t_plan = {"n": [], "seq": []}
+    for _ in range(5):
+        for key, plan in (("seq", seq_offs), ("n", offs)):
+            dec.plan = plan
+            dec._upload_positions()
+            a_, b_ = ev(), ev()
+            a_.record()
+            dec.draft_phase()
+            b_.record()
+            torch.cuda.synchronize()
+            t_plan[key].append(a_.elapsed_time(b_) / max(k - 1, 1))
+    dec.plan = offs
+    step_n, step_seq = float(np.median(t_plan["n"])), float(np.median(t_plan["seq"]))
+    log(f"  draft step: plan {step_n * 1e3:.0f} us, sequential (N = 1) {step_seq * 1e3:.0f} us -> drafting "
+        f"speedup {step_seq / step_n:.3f}x")
+
+    n1 = None
+    if args.n1_compare:
+        d1 = SpecDecoder(cfg.draft, dw, cfg.base, bw, cfg.batch, cap, k, seq_offs, P, inv_t, cfg.sample_seed)
+        d1.prefill(prompts)
+        for _ in range(W):
+            d1.step(big)
+        nb = sum(len(o) for o in d1.out)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(K):
+            d1.step(big)
+        torch.cuda.synchronize()
+        el1 = time.perf_counter() - t1
+        tok1 = sum(len(o) for o in d1.out) - nb
+        acc1 = (tok1 - K * cfg.batch) / (K * cfg.batch * k)
+        n1 = {"tokens_per_s": round(tok1 / el1, 3), "acceptance_rate": round(acc1, 4)}
+        log(f"  sequential draft plan (N = 1): {tok1 / el1:.1f} tok/s, acceptance {acc1:.3f} "
+            f"(layer-parallel plan: {value:.1f} tok/s, acceptance {acc_rate:.3f})")
+        del d1
+
     vanilla = None
     if not args.no_vanilla:
         vd = VanillaDecoder(cfg.base, bw, cfg.batch, P + 64 + 2, P, inv_t, cfg.sample_seed)
@@ -446,6 +487,9 @@ def main():
         "calibrate_us": round(ms["calib"] * 1e3, 1),
         "prefill_ms": round(prefill_ms, 2),
         "vanilla_tokens_per_s": vanilla,
+        "draft_step_us_sequential_plan": round(step_seq * 1e3, 1),
+        "drafting_speedup": round(step_seq / step_n, 4),
+        "sequential_plan": n1,
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "launches": dom_n, "avg_launch_us": round(dom_ms / dom_n * 1e3, 2),
