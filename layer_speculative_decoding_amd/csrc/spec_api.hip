@@ -137,7 +137,7 @@ Carve carve(const spec_model *m, int batch, int max_m, int G) {
     c.ss_sel_stride = (int64_t)R * kPartialsMax;
     c.ss = take(nsel * R * kPartialsMax * 4);
     c.rope = take(R * (hd / 2) * 8);
-    // K-slice partials of the tiled products (prompt-length calls only)
+    // K-slice partials of the tiled products (calls of more than 16 rows)
     c.tpart_bytes = R >= (size_t)gemm_tiled_min_rows() ? gemm_tiled_part_bytes() : 0;
     c.tpart = take(c.tpart_bytes);
     c.total = off;
@@ -205,7 +205,7 @@ hipError_t product(const Fwd &f, GemvParams p, int *parts_out = nullptr) {
     t.m0 = 0;
     t.M = Mtot;
     if (m->d.dtype == SPEC_BF16 && Mtot >= tiled_min_rows() && gemm_tiled_supported(t)) {
-        // prompt-length row counts: one tiled launch over every row
+        // more than 16 rows: one tiled launch over every row
         if (parts_out) *parts_out = gemm_tiled_parts(t);
         double xbytes = (double)Mtot * p.K * m->xs;
         if (p.xmode == X_NORM) {

@@ -51,6 +51,7 @@ struct GemvParams {
     int xmode;
     const void *X;        // X_PLAIN
     int64_t x_sel_stride;
+    int64_t x_ld;         // X_PLAIN row stride in elements (0: K; matrix-core products)
     const float *xh;      // X_NORM: residual rows [Mtot][K]
     const float *xadd;    // X_NORM, nullable: [sel][Mtot][K]
     int64_t xadd_sel_stride;
@@ -110,7 +111,7 @@ int gemv_grid(const GemvParams &p, int ks);
 // writers run one unit per workgroup and leave rows_per_sel / 16 partials
 // per row and set member.
 hipError_t launch_gemm_mfma(const GemvParams &p, int grid, int ks, hipStream_t s);
-// Tiled matrix-core GEMM (bf16) for prompt-length row counts: every row of
+// Tiled matrix-core GEMM (bf16) for more than 16 rows: every row of
 // the call in one launch (p.m0 = 0, p.M = rows), K a multiple of 64, no
 // LOGITS epilogue, a set member's rows a whole number of 64-row tiles (32
 // units for the paired epilogues).  n_units as for the VALU GEMV (row pairs).
