@@ -107,7 +107,7 @@ __global__ __launch_bounds__(64 * KS * (epi_is_pair(EPI) ? 2 : 1)) void k_gemm_m
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
             xok[t] = t * 16 + li < p.M;
-            xr[t] = xb + (int64_t)(p.m0 + t * 16 + li) * (p.x_ld ? p.x_ld : K) + 8 * lg;
+            xr[t] = xb + (int64_t)(p.m0 + t * 16 + li) * K + 8 * lg;
         }
         f32x4 acc[MT];
 #pragma unroll

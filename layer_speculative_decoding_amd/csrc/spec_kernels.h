@@ -51,7 +51,6 @@ struct GemvParams {
     int xmode;
     const void *X;        // X_PLAIN
     int64_t x_sel_stride;
-    int64_t x_ld;         // X_PLAIN row stride in elements (0: K; matrix-core products)
     const float *xh;      // X_NORM: residual rows [Mtot][K]
     const float *xadd;    // X_NORM, nullable: [sel][Mtot][K]
     int64_t xadd_sel_stride;
