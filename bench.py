@@ -246,6 +246,10 @@ def main():
     ap.add_argument("--temperature", type=float, default=0.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-vanilla", action="store_true")
+    ap.add_argument("--group-size", type=int, default=0,
+                    help="layer-parallel set size N of the default plan (0: the workload's own)")
+    ap.add_argument("--no-calibration", action="store_true",
+                    help="ablation: keep the fuzzy KV of accepted drafts, run only the emitted token precisely")
     ap.add_argument("--n1-compare", action="store_true",
                     help="also run the timed rounds with the sequential draft plan (N = 1) and report its "
                          "acceptance and tokens/s")
@@ -304,14 +308,16 @@ def main():
     bw = make_weights(cfg.base, cfg.seed_base, device=dev)
     torch.cuda.synchronize()
     log(f"  weights ready in {time.time() - t0:.1f}s")
-    offs = api.spec_default_group_plan(cfg.draft.n_layers, cfg.group_size)
+    N = args.group_size or cfg.group_size
+    offs = api.spec_default_group_plan(cfg.draft.n_layers, N)
     seq_offs = list(range(cfg.draft.n_layers + 1))      # every layer its own stage (N = 1)
     P = cfg.prompt_len
     rounds_cap = W + K + 4
     cap = P + rounds_cap * (k + 1) + k + 2
     prompts = make_prompts(cfg.draft.vocab, P, cfg.batch, cfg.prompt_seed)
     inv_t = 0.0 if args.temperature == 0 else 1.0 / args.temperature
-    dec = SpecDecoder(cfg.draft, dw, cfg.base, bw, cfg.batch, cap, k, offs, P, inv_t, cfg.sample_seed)
+    dec = SpecDecoder(cfg.draft, dw, cfg.base, bw, cfg.batch, cap, k, offs, P, inv_t, cfg.sample_seed,
+                      calibrate=not args.no_calibration)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
     e0, e1 = ev(), ev()
@@ -431,7 +437,8 @@ def main():
 
     n1 = None
     if args.n1_compare:
-        d1 = SpecDecoder(cfg.draft, dw, cfg.base, bw, cfg.batch, cap, k, seq_offs, P, inv_t, cfg.sample_seed)
+        d1 = SpecDecoder(cfg.draft, dw, cfg.base, bw, cfg.batch, cap, k, seq_offs, P, inv_t, cfg.sample_seed,
+                         calibrate=not args.no_calibration)
         d1.prefill(prompts)
         for _ in range(W):
             d1.step(big)
@@ -478,7 +485,8 @@ def main():
         "data": "synthetic (seeded random-init weights, uniform-random prompt)",
         "config": {"workload": f"{cfg.name}: draft {cfg.draft.n_layers}L d{cfg.draft.d_model} -> base "
                                f"{cfg.base.n_layers}L d{cfg.base.d_model}, V {cfg.draft.vocab}, P {P}, k {k}, "
-                               f"N {cfg.group_size}, batch {cfg.batch}, T {args.temperature}",
+                               f"N {N}, batch {cfg.batch}, T {args.temperature}"
+                               + (", no KV calibration" if args.no_calibration else ""),
                    "plan": offs, "global_batch": cfg.batch, "seq_len": P},
         "acceptance_rate": round(acc_rate, 4),
         "draft_step_us": round(d_step_ms * 1e3, 1),

@@ -38,7 +38,7 @@ class RoundRecord:
 class SpecDecoder:
     def __init__(self, draft_shape, draft_w, base_shape, base_w, batch: int, capacity: int, k: int,
                  plan_offsets, prompt_len: int, inv_temp: float, seed: int,
-                 mlp_mode: int = SPEC_MLP_SEQUENTIAL, device="cuda"):
+                 mlp_mode: int = SPEC_MLP_SEQUENTIAL, device="cuda", calibrate: bool = True):
         if k < 1:
             raise ValueError("k must be >= 1")
         self.dev = torch.device(device)
@@ -50,6 +50,10 @@ class SpecDecoder:
         self.plan = list(plan_offsets)
         self.G = max(self.plan[i + 1] - self.plan[i] for i in range(len(self.plan) - 1))
         self.mlp_mode = mlp_mode
+        # calibrate=False is the ablation without KV calibration: the fuzzy
+        # entries of accepted drafts stay, and only the emitted token's own
+        # forward (which yields the next d_1) runs precisely
+        self.calibrate = calibrate
         self.inv_temp = float(np.float32(inv_temp))
         self.seed = int(seed)
         self.dkv = api.KVCache(draft_shape, batch, capacity, device)
@@ -167,6 +171,9 @@ class SpecDecoder:
                 continue
             th[k + 1, b] = a[b] + 1
             self.t[b] += int(a[b]) + 1
+            if not self.calibrate:
+                th[k, b] = self.t[b]
+                th[k + 1, b] = 1
             more = True
         if not more:
             if marks:
@@ -176,7 +183,10 @@ class SpecDecoder:
         # the calibration covers exactly the emitted tokens: its row bound is
         # the longest a + 1 of the round (token rows keep their k + 1 stride)
         rows = max(1, max(int(th[k + 1, b]) for b in range(B)))
-        api.spec_calibrate_kv(self.draft, self.dkv, B, self.commit, self.tab[k], self.tab[k + 1], rows,
+        # without calibration the one row is the emitted token y, which the
+        # accept step left in vtok[:, 0]
+        toks = self.commit if self.calibrate else self.vtok
+        api.spec_calibrate_kv(self.draft, self.dkv, B, toks, self.tab[k], self.tab[k + 1], rows,
                               max(self.t), self.inv_temp, self.seed, self.q_logits[:, 0], k * self.V,
                               self.vtok[:, 1], k + 1, self.ws, tokens_stride=k + 1)
         if marks:

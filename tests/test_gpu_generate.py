@@ -73,6 +73,29 @@ def test_near_copy_lockstep_batch(dtype, mlp, inv_temp):
 
 
 @pytest.mark.parametrize("dtype", [0, BF16])
+@pytest.mark.parametrize("inv_temp", [0.0, 1.0])
+def test_no_calibration_ablation_lockstep(dtype, inv_temp):
+    """The ablation without KV calibration: accepted drafts keep their fuzzy
+    KV entries and only the emitted token runs precisely; GPU and oracle run
+    the same loop in lock step."""
+    from layer_speculative_decoding_amd.runtime import SpecDecoder
+    sh, dw, bw = _near_copy_pair(dtype)
+    say(f"no-calibration lockstep dtype={dtype} invT={inv_temp}")
+    sets = default_group_plan(sh.n_layers, 2)
+    B, P, k, new = 3, 12, 4, 24
+    prompts = make_prompts(sh.vocab, P, B, lambda b: 91 + b)
+    dec = SpecDecoder(sh, to_dev(dw), sh, to_dev(bw), B, P + new + k + 2, k, plan_offsets(sets), P, inv_temp,
+                      515, MLP_SEQUENTIAL, calibrate=False)
+    tol = TOL_F32 if dtype == 0 else TOL_BF16
+    st = lockstep(dec, OracleModel.from_torch(sh, dw), OracleModel.from_torch(sh, bw), prompts, k, sets, new,
+                  dec.inv_temp, 515, MLP_SEQUENTIAL, tol, calibrate=False)
+    acc = sum(int(a) for r in dec.records for a in r.n_acc)
+    say(f"  checked {st['checked']} excluded {st['excluded']} max rel err {st['err']:.2e}; accepted {acc}")
+    assert acc > 0
+    assert st["excluded"] <= max(3, st["checked"] // 3)
+
+
+@pytest.mark.parametrize("dtype", [0, BF16])
 def test_greedy_speculative_equals_vanilla_on_gpu(dtype):
     """Lossless greedy decoding on the GPU.  float32: identical outputs.  bf16:
     verification (k+1 rows, matrix-core kernel) and vanilla decoding (one row)
