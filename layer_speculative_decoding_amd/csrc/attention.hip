@@ -378,7 +378,12 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnParams p) {
     }
 }
 
-int qv_blocks(int G, int mseq) { return (long)mseq * G <= 16 ? 1 : 2; }
+// 16 query vectors per workgroup: measured against 32 (two blocks), the
+// smaller register footprint and the doubled workgroup count win at every
+// decode shape (8B verify, 6 rows, context 560: 12.9 vs 15.5 us; 8B verify,
+// 9 rows, context 2100: 21.8 vs 33.6 us; 70B verify, 4 x 7 rows, context
+// 8200: 128 vs 138 us).
+int qv_blocks(int G, int mseq) { (void)G; (void)mseq; return 1; }
 
 template <typename T, int HD, int NQB>
 hipError_t launch_hd(const AttnParams &p, hipStream_t s) {
@@ -395,8 +400,7 @@ hipError_t launch_hd(const AttnParams &p, hipStream_t s) {
 
 template <typename T, int HD>
 hipError_t launch_nqb(const AttnParams &p, hipStream_t s) {
-    if (qv_blocks(p.hq / p.hkv, p.rows.mseq) == 1) return launch_hd<T, HD, 1>(p, s);
-    return launch_hd<T, HD, 2>(p, s);
+    return launch_hd<T, HD, 1>(p, s);
 }
 
 template <typename T>
