@@ -3,7 +3,7 @@
 //
 // A workgroup owns (query block, layer of the group, kv head, sequence, key
 // split).  Its query vectors are the rows of the block times the q heads that
-// share the kv head (GQA): 16 or 32 of them, zero-padded, held in registers as
+// share the kv head (GQA): 16 of them (NQB = 1), zero-padded, held in registers as
 // the B operand of float32 matrix-core products (v_mfma_f32_16x16x4_f32).
 // The four waves take interleaved 16-key blocks of the split's key range and
 // run independently, reading K and V straight from HBM (no LDS staging):
