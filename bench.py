@@ -262,26 +262,28 @@ def main():
     ap.add_argument("--rocprof-summary", nargs=2, metavar=("STATS_CSV", "TRACE_CSV"),
                     help="print the kernel statistics and one round's phases of a kernel-trace run")
     args = ap.parse_args()
+    # the profiler's output directory of a summarised run: where its CSV is
+    odir = lambda path: os.path.dirname(path) or "."
     if args.rocprof_summary:
         st, tr = args.rocprof_summary
         rocprof_summary(st, tr, [
-            "timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof -o run "
+            f"timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d {odir(st)} -o run "
             "-- python bench.py --steps 10 --warmup 2 --no-cpu-baseline --no-vanilla",
             f"python bench.py --rocprof-summary {st} {tr} > profiles/kernel_stats_llama-1b-8b_k5_N2.md"])
         return
     if args.pmc_mfma_summary:
         pmc_mfma_summary(args.pmc_mfma_summary, [
             "timeout -s KILL 240 rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 "
-            "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d gpurun_out/pmc_mfma -o run "
+            f"SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d {odir(args.pmc_mfma_summary)} -o run "
             "-- python bench.py --warmup 1 --pmc-probe",
             f"python bench.py --pmc-mfma-summary {args.pmc_mfma_summary} > profiles/mfma_util.md"])
         return
     if args.pmc_summary:
         f, w, kname = args.pmc_summary
         pmc_summary(f, w, kname, [
-            "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run "
+            f"timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d {odir(f)} -o run "
             "-- python bench.py --warmup 1 --pmc-probe",
-            "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run "
+            f"timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d {odir(w)} -o run "
             "-- python bench.py --warmup 1 --pmc-probe",
             f"python bench.py --pmc-summary {f} {w} '{kname}' > profiles/pmc_traffic.md"])
         return
