@@ -269,26 +269,32 @@ __global__ __launch_bounds__(256) void k_gemm_tile_epi(GemvParams p, TileArgs ta
     constexpr int BN = 32 * WNB;
     const int T = ta.gm * ta.gn, t = blockIdx.x;
     const float4 *src = reinterpret_cast<const float4 *>(ta.part) + (int64_t)t * (kWMB * WNB) * 256 + threadIdx.x;
-    // slice by slice, all of a slice's blocks requested before any is added
+    // the blocks of up to SG slices are requested together, then added in
+    // slice order (the sum's order is fixed: slice 0, 1, 2, ...)
+    constexpr int SG = WNB == 2 ? 4 : 2;
+    const int64_t sstride = (int64_t)T * (kWMB * WNB) * 256;
     f32x4 acc[kWMB][WNB];
 #pragma unroll
     for (int a = 0; a < kWMB; ++a)
 #pragma unroll
-        for (int c = 0; c < WNB; ++c) {
-            const float4 v = src[(a * WNB + c) * 256];
-            acc[a][c] = f32x4{v.x, v.y, v.z, v.w};
-        }
-    for (int k = 1; k < ta.ks; ++k) {
-        const float4 *sk = src + (int64_t)k * T * (kWMB * WNB) * 256;
-        float4 v[kWMB][WNB];
+        for (int c = 0; c < WNB; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < ta.ks; k0 += SG) {
+        float4 v[SG][kWMB][WNB];
 #pragma unroll
-        for (int a = 0; a < kWMB; ++a)
+        for (int g = 0; g < SG; ++g)
 #pragma unroll
-            for (int c = 0; c < WNB; ++c) v[a][c] = sk[(a * WNB + c) * 256];
+            for (int a = 0; a < kWMB; ++a)
 #pragma unroll
-        for (int a = 0; a < kWMB; ++a)
+                for (int c = 0; c < WNB; ++c)
+                    v[g][a][c] = k0 + g < ta.ks ? src[(k0 + g) * sstride + (a * WNB + c) * 256]
+                                                : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-            for (int c = 0; c < WNB; ++c) acc[a][c] += f32x4{v[a][c].x, v[a][c].y, v[a][c].z, v[a][c].w};
+        for (int g = 0; g < SG; ++g)
+#pragma unroll
+            for (int a = 0; a < kWMB; ++a)
+#pragma unroll
+                for (int c = 0; c < WNB; ++c)
+                    if (k0 + g < ta.ks) acc[a][c] += f32x4{v[g][a][c].x, v[g][a][c].y, v[g][a][c].z, v[g][a][c].w};
     }
     tile_epilogue<EPI, WNB>(p, ta, tile_pos<EPI, BN>(p, ta, t), acc);
 }
