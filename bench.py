@@ -437,6 +437,20 @@ def main():
     log(f"  draft step: plan {step_n * 1e3:.0f} us, sequential (N = 1) {step_seq * 1e3:.0f} us -> drafting "
         f"speedup {step_seq / step_n:.3f}x")
 
+    # cosine diagnostic of the fuzzy inputs (rebuttal discussion of Table 3):
+    # per layer, cos(set input h0, the state a sequential pass would feed the
+    # layer), for the round's first draft step at the current positions
+    Ld = cfg.draft.n_layers
+    cosv = torch.zeros(cfg.batch, Ld, device=dev)
+    dec._upload_positions()
+    api.spec_draft_attention_cosine(dec.draft, dec.dkv, offs, cfg.batch, dec.vtok[:, 1], k + 1, dec.tab[1],
+                                    max(dec.t) + 1, cosv, Ld, dec.ws)
+    cos_layers = [round(float(x), 5) for x in cosv.mean(0).cpu().numpy()]
+    firsts = set(offs[:-1])
+    inner = [c for l, c in enumerate(cos_layers) if l not in firsts]
+    log(f"  attention-input cosine (fuzzy vs sequential), layers not first in their set: "
+        f"min {min(inner) if inner else 1.0:.4f}, mean {float(np.mean(inner)) if inner else 1.0:.4f}")
+
     n1 = None
     if args.n1_compare:
         d1 = SpecDecoder(cfg.draft, dw, cfg.base, bw, cfg.batch, cap, k, seq_offs, P, inv_t, cfg.sample_seed,
@@ -500,6 +514,8 @@ def main():
         "draft_step_us_sequential_plan": round(step_seq * 1e3, 1),
         "drafting_speedup": round(step_seq / step_n, 4),
         "sequential_plan": n1,
+        "attention_input_cosine": {"per_layer": cos_layers,
+                                   "mean_fuzzy_layers": round(float(np.mean(inner)), 5) if inner else None},
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "launches": dom_n, "avg_launch_us": round(dom_ms / dom_n * 1e3, 2),

@@ -158,6 +158,25 @@ spec_status spec_draft_group_step(const spec_model *draft, const spec_kv *kv,
                                   int32_t *token_out, int token_out_stride,
                                   void *workspace, size_t ws_bytes, void *stream);
 
+/* Cosine-similarity diagnostic of the fuzzy inputs (review thread, the
+ * discussion of Table 3: the similarity of the hidden states a layer-parallel
+ * set feeds its attentions to the ones a sequential pass would feed, measured
+ * as a cosine because each attention normalises its input first).  Runs the
+ * layer-parallel step of spec_draft_group_step with sequential MLPs (and, like
+ * it, writes the fuzzy K/V at `positions`) and, for every layer l of set
+ * [l0, l0+n), writes
+ *   cos_out[b * cos_stride + l] = cos(h0, h_l),
+ * h0 = the set's input state (what all its attentions read), h_l = the state
+ * after the members l0 .. l-1 have added their attention and MLP outputs
+ * (what layer l's attention would read if the set ran in order; h_l0 = h0).
+ * No head, no sampling.  cos_stride >= n_layers; other arguments as for
+ * spec_draft_group_step.  Errors as for spec_draft_group_step. */
+spec_status spec_draft_attention_cosine(const spec_model *draft, const spec_kv *kv,
+                                        const int32_t *plan_offsets, int n_stages, int batch,
+                                        const int32_t *tokens, int tokens_stride,
+                                        const int32_t *positions, int max_pos, float *cos_out,
+                                        int cos_stride, void *workspace, size_t ws_bytes, void *stream);
+
 /* Bonus calibration / KV correction (EasySpec abstract: after each
  * drafting-and-verification iteration the draft KV cache is calibrated in a
  * single forward pass; rebuttal: calibrated entries replace the fuzzy ones).

@@ -24,7 +24,7 @@ EXPORTS = ("spec_model_create", "spec_model_destroy", "spec_check_pair", "spec_d
            "spec_workspace_bytes", "spec_draft_group_step", "spec_calibrate_kv", "spec_verify_forward",
            "spec_accept_workspace_bytes", "spec_accept_resample", "spec_status_string", "spec_last_error",
            "spec_version", "spec_profile_enable", "spec_profile_reset", "spec_profile_collect",
-           "spec_profile_entry")
+           "spec_profile_entry", "spec_draft_attention_cosine")
 
 
 class SpecError(RuntimeError):
@@ -76,6 +76,8 @@ def load() -> C.CDLL:
         "spec_status_string": (C.c_char_p, [i32]),
         "spec_last_error": (C.c_char_p, []),
         "spec_version": (C.c_char_p, []),
+        "spec_draft_attention_cosine": (i32, [vp, C.POINTER(KV), C.POINTER(C.c_int32), i32, i32, vp, i32, vp, i32,
+                                              vp, i32, vp, sz, vp]),
         "spec_profile_enable": (i32, [i32]),
         "spec_profile_reset": (None, []),
         "spec_profile_collect": (i32, []),

@@ -106,6 +106,15 @@ def spec_draft_group_step(model: SpecModel, kv: KVCache, plan_offsets, flags: in
         logits_stride, _ptr(token_out), token_out_stride, _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
+def spec_draft_attention_cosine(model: SpecModel, kv: KVCache, plan_offsets, batch: int, tokens: torch.Tensor,
+                                tokens_stride: int, positions: torch.Tensor, max_pos: int, cos_out: torch.Tensor,
+                                cos_stride: int, workspace: torch.Tensor, stream=None):
+    plan = _plan_array(plan_offsets)
+    check(load().spec_draft_attention_cosine(
+        model.handle, C.byref(kv.c), plan, len(plan_offsets) - 1, batch, _ptr(tokens), tokens_stride,
+        _ptr(positions), max_pos, _ptr(cos_out), cos_stride, _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
 def spec_calibrate_kv(model: SpecModel, kv: KVCache, batch: int, tokens: torch.Tensor, start_pos: torch.Tensor,
                       n_tokens: Optional[torch.Tensor], max_m: int, max_pos: int, inv_temperature: float,
                       seed: int, last_logits_out: Optional[torch.Tensor], logits_stride: int,

@@ -415,6 +415,50 @@ hipError_t launch_norm_rows(int dtype, const GemvParams &p, int n_sel, void *xn,
     return hipGetLastError();
 }
 
+// cos(x[r], y[r] - a[r]) over d elements of row r (a nullable), fixed
+// summation order: thread strides, then the waves in order.
+__global__ __launch_bounds__(256) void k_cosine(const float *x, const float *y, const float *a, int d, float *out,
+                                                int64_t out_stride) {
+    __shared__ float part[kWaves][3];
+    const int r = blockIdx.x;
+    const float *xr = x + (int64_t)r * d, *yr = y + (int64_t)r * d;
+    const float *ar = a ? a + (int64_t)r * d : nullptr;
+    float xy = 0.f, xx = 0.f, yy = 0.f;
+    for (int k = threadIdx.x; k < d; k += 256) {
+        const float u = xr[k], v = ar ? yr[k] - ar[k] : yr[k];
+        xy = fmaf(u, v, xy);
+        xx = fmaf(u, u, xx);
+        yy = fmaf(v, v, yy);
+    }
+    xy = wave_sum(xy);
+    xx = wave_sum(xx);
+    yy = wave_sum(yy);
+    if ((threadIdx.x & 63) == 0) {
+        part[threadIdx.x >> 6][0] = xy;
+        part[threadIdx.x >> 6][1] = xx;
+        part[threadIdx.x >> 6][2] = yy;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        xy = part[0][0];
+        xx = part[0][1];
+        yy = part[0][2];
+        for (int w = 1; w < kWaves; ++w) {
+            xy += part[w][0];
+            xx += part[w][1];
+            yy += part[w][2];
+        }
+        const float den = sqrtf(xx) * sqrtf(yy);
+        out[(int64_t)r * out_stride] = den > 0.f ? xy / den : 0.f;
+    }
+}
+
+hipError_t launch_cosine(const float *x, const float *y, const float *a, int rows, int d, float *out,
+                         int64_t out_stride, hipStream_t s) {
+    hipLaunchKernelGGL(k_cosine, dim3(rows), dim3(256), 0, s, x, y, a, d, out, out_stride);
+    return hipGetLastError();
+}
+
 hipError_t launch_sample_reduce(const float *pv, const int32_t *pi, int n, int M, int32_t *out, int stride,
                                 hipStream_t s) {
     hipLaunchKernelGGL(k_sample_reduce, dim3(M), dim3(256), 0, s, pv, pi, n, out, stride);

@@ -282,7 +282,10 @@ hipError_t run_embed(Fwd &f, const int32_t *tokens, int64_t tok_ld, int tok_step
 
 // One stage: attention of the set [l0, l0 + n) on the stage input h0, then
 // the set's MLPs.  A stage of one layer is the ordinary decoder layer.
-hipError_t run_stage(Fwd &f, int l0, int n, int mlp_mode) {
+// cos_out (nullable, sequential MLPs only): cos_out[b * cos_stride + l] for
+// each layer l of the set = the cosine between the input its attention read
+// (h0) and the running state a sequential layer would have read there.
+hipError_t run_stage(Fwd &f, int l0, int n, int mlp_mode, float *cos_out = nullptr, int64_t cos_stride = 0) {
     const spec_model *m = f.m;
     const spec_model_desc &d = m->d;
     const int R = f.batch * f.mseq;
@@ -297,6 +300,11 @@ hipError_t run_stage(Fwd &f, int l0, int n, int mlp_mode) {
     void *act = at<char>(f.ws, f.c.act);
     hipError_t e;
     int grid = 0;
+    if (cos_out) {
+        // keep the stage input; the first member reads exactly it
+        if ((e = hipMemcpyAsync(h0, h, (size_t)R * dm * 4, hipMemcpyDeviceToDevice, f.s)) != hipSuccess) return e;
+        if ((e = launch_cosine(h0, h0, nullptr, R, dm, cos_out + l0, cos_stride, f.s)) != hipSuccess) return e;
+    }
 
     // 1. grouped QKV over the N layers' concatenated rows: operand = one RMS
     //    of h0 with each layer's gain; epilogue = RoPE + KV append
@@ -373,6 +381,11 @@ hipError_t run_stage(Fwd &f, int l0, int n, int mlp_mode) {
         gp.n_norm_sel = 1;
         if ((e = product(f, gp, &grid)) != hipSuccess) return e;
         f.nparts[0] = grid;
+        if (cos_out && i + 1 < n) {
+            // h now also holds a_{i+1}: the state before it is h - a_{i+1}
+            e = launch_cosine(h0, h, abuf + (size_t)(i + 1) * R * dm, R, dm, cos_out + l0 + i + 1, cos_stride, f.s);
+            if (e != hipSuccess) return e;
+        }
     }
     return hipSuccess;
 }
@@ -556,6 +569,50 @@ size_t spec_workspace_bytes(const spec_model *m, int batch, int max_m, int max_g
     return carve(m, batch, max_m, max_group).total;
 }
 
+// Plan check shared by the layer-parallel entry points; *G = largest set.
+static spec_status check_plan(const spec_model *draft, const int32_t *plan_offsets, int n_stages, int flags,
+                              int *G) {
+    if (!plan_offsets || n_stages < 1) return fail(SPEC_ERR_PLAN, "empty plan");
+    if (flags != SPEC_MLP_SEQUENTIAL && flags != SPEC_MLP_PARALLEL) return fail(SPEC_ERR_INVALID_ARG, "flags %d", flags);
+    if (plan_offsets[0] != 0 || plan_offsets[n_stages] != draft->d.n_layers)
+        return fail(SPEC_ERR_PLAN, "plan must cover layers 0..%d", draft->d.n_layers - 1);
+    *G = 1;
+    for (int s = 0; s < n_stages; ++s) {
+        const int n = plan_offsets[s + 1] - plan_offsets[s];
+        if (n < 1) return fail(SPEC_ERR_PLAN, "stage %d is empty or out of order", s);
+        if (n > *G) *G = n;
+    }
+    if (flags == SPEC_MLP_PARALLEL && *G > kMaxSel)
+        return fail(SPEC_ERR_UNSUPPORTED, "parallel MLPs support sets of at most %d layers", kMaxSel);
+    return SPEC_OK;
+}
+
+spec_status spec_draft_attention_cosine(const spec_model *draft, const spec_kv *kv, const int32_t *plan_offsets,
+                                        int n_stages, int batch, const int32_t *tokens, int tokens_stride,
+                                        const int32_t *positions, int max_pos, float *cos_out, int cos_stride,
+                                        void *workspace, size_t ws_bytes, void *stream) {
+    spec_status st = check_model(draft, kv, batch);
+    if (st) return st;
+    int G = 1;
+    if ((st = check_plan(draft, plan_offsets, n_stages, SPEC_MLP_SEQUENTIAL, &G))) return st;
+    if (!tokens || !positions || !cos_out) return fail(SPEC_ERR_INVALID_ARG, "NULL tokens/positions/cos_out");
+    if (tokens_stride < 1 || cos_stride < draft->d.n_layers)
+        return fail(SPEC_ERR_INVALID_ARG, "tokens_stride >= 1 and cos_stride >= n_layers required");
+    if (max_pos < 0 || max_pos >= kv->capacity)
+        return fail(SPEC_ERR_CAPACITY, "max_pos %d outside KV capacity %d", max_pos, kv->capacity);
+    if ((st = check_ws(draft, batch, 1, G, workspace, ws_bytes))) return st;
+    Fwd f{draft, kv, batch, 1, max_pos, RowMap{positions, nullptr, 1, kv->capacity}, workspace,
+          carve(draft, batch, 1, G), (hipStream_t)stream, {0}};
+    hipError_t e = run_embed(f, tokens, tokens_stride, 0);
+    if (e != hipSuccess) return hip_fail(e, "embed");
+    for (int s = 0; s < n_stages; ++s) {
+        e = run_stage(f, plan_offsets[s], plan_offsets[s + 1] - plan_offsets[s], SPEC_MLP_SEQUENTIAL, cos_out,
+                      cos_stride);
+        if (e != hipSuccess) return hip_fail(e, "cosine stage");
+    }
+    return SPEC_OK;
+}
+
 spec_status spec_draft_group_step(const spec_model *draft, const spec_kv *kv, const int32_t *plan_offsets,
                                   int n_stages, int flags, int batch, const int32_t *tokens, int tokens_stride,
                                   const int32_t *positions, int max_pos, float inv_temperature, uint64_t seed,
@@ -563,18 +620,8 @@ spec_status spec_draft_group_step(const spec_model *draft, const spec_kv *kv, co
                                   int token_out_stride, void *workspace, size_t ws_bytes, void *stream) {
     spec_status st = check_model(draft, kv, batch);
     if (st) return st;
-    if (!plan_offsets || n_stages < 1) return fail(SPEC_ERR_PLAN, "empty plan");
-    if (flags != SPEC_MLP_SEQUENTIAL && flags != SPEC_MLP_PARALLEL) return fail(SPEC_ERR_INVALID_ARG, "flags %d", flags);
-    if (plan_offsets[0] != 0 || plan_offsets[n_stages] != draft->d.n_layers)
-        return fail(SPEC_ERR_PLAN, "plan must cover layers 0..%d", draft->d.n_layers - 1);
     int G = 1;
-    for (int s = 0; s < n_stages; ++s) {
-        const int n = plan_offsets[s + 1] - plan_offsets[s];
-        if (n < 1) return fail(SPEC_ERR_PLAN, "stage %d is empty or out of order", s);
-        if (n > G) G = n;
-    }
-    if (flags == SPEC_MLP_PARALLEL && G > kMaxSel)
-        return fail(SPEC_ERR_UNSUPPORTED, "parallel MLPs support sets of at most %d layers", kMaxSel);
+    if ((st = check_plan(draft, plan_offsets, n_stages, flags, &G))) return st;
     if (!tokens || !positions || !token_out) return fail(SPEC_ERR_INVALID_ARG, "NULL tokens/positions/token_out");
     if (tokens_stride < 1 || token_out_stride < 1) return fail(SPEC_ERR_INVALID_ARG, "strides must be >= 1");
     if (logits_out && logits_stride < draft->d.vocab) return fail(SPEC_ERR_INVALID_ARG, "logits_stride < vocab");

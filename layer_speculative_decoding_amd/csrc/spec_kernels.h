@@ -131,6 +131,10 @@ int gemm_mfma_max_rows();
 int gemm_mfma_grid(const GemvParams &p);
 int gemm_mfma_splits(const GemvParams &p);
 
+// out[r * out_stride] = cos(x[r], y[r] - a[r]) for rows of d floats (a nullable).
+hipError_t launch_cosine(const float *x, const float *y, const float *a, int rows, int d, float *out,
+                         int64_t out_stride, hipStream_t s);
+
 // Embedding of every row (h = E[token]), its sum of squares (one partial),
 // and the RoPE (cos, sin) of its position.
 struct EmbedParams {

@@ -240,3 +240,45 @@ def test_prompt_prefill_matches_oracle(name, tile, monkeypatch):
     assert not np.any(k[:, 1, :, lens[1]:])      # rows past n_tokens leave the cache alone
     ek, ev = _kv_rel(gkv, okv, int(lens[0]))
     assert ek < tol and ev < tol
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_attention_input_cosine_matches_oracle(name):
+    """The cosine diagnostic of the fuzzy inputs against the oracle's trace of
+    the same layer-parallel step (sequential MLPs): per layer, cos(h0, h_l)."""
+    from layer_speculative_decoding_amd import api
+    from oracle.model import fuzzy_step_hidden
+    B, P = 2, 19
+    shape, tol, om, gm, gkv, okv, prompts = _setup(name, B, P + 2)
+    L = shape.n_layers
+    for sets in PLANS[name]:
+        offs = plan_offsets(sets)
+        G = max(len(s) for s in sets)
+        say(f"cosine {name} plan={offs}")
+        gkv.k.zero_(); gkv.v.zero_()
+        okv = KVCache(shape, B, gkv.capacity)
+        w = ws(max(api.spec_workspace_bytes(gm, B, P, 1), api.spec_workspace_bytes(gm, B, 1, G)))
+        tok = torch.zeros(B, dtype=torch.int32, device="cuda")
+        api.spec_calibrate_kv(gm, gkv, B, i32(prompts[:, :P]), i32([0] * B), None, P, P - 1, 0.0, 0, None, 0, tok,
+                              1, w)
+        for b in range(B):
+            forward(om, okv, b, prompts[b, :P], range(P), logits=None)
+        cur = prompts[:, P].copy()
+        pos = np.full(B, P, dtype=np.int32)
+        cos = torch.full((B, L + 3), -7.0, device="cuda")
+        api.spec_draft_attention_cosine(gm, gkv, offs, B, i32(cur), 1, i32(pos), int(pos.max()), cos, L + 3, w)
+        torch.cuda.synchronize()
+        cg = cos.cpu().numpy()
+        assert np.all(cg[:, L:] == -7.0)                 # nothing past n_layers
+        for b in range(B):
+            tr = []
+            fuzzy_step_hidden(om, okv, b, int(cur[b]), int(pos[b]), sets, MLP_SEQUENTIAL, trace=tr)
+            co = np.zeros(L)
+            for l, h0, h in tr:
+                x, y = h0.reshape(-1), h.reshape(-1)
+                co[l] = float(np.dot(x, y) / (np.linalg.norm(x) * np.linalg.norm(y)))
+            err = float(np.max(np.abs(cg[b, :L] - co)))
+            say(f"  b={b} cos {np.round(co, 4).tolist()} max |gpu - oracle| {err:.1e}")
+            assert err < (1e-5 if tol == TOL_F32 else 1e-2)
+            for s in sets:                              # the first member reads exactly h0
+                assert abs(cg[b, s[0]] - 1.0) < 1e-5
