@@ -451,6 +451,41 @@ def main():
     log(f"  attention-input cosine (fuzzy vs sequential), layers not first in their set: "
         f"min {min(inner) if inner else 1.0:.4f}, mean {float(np.mean(inner)) if inner else 1.0:.4f}")
 
+    # stage overlap (PEARL-style, measurement only): a round's draft steps and
+    # its verify run back to back, then concurrently on two streams (the
+    # verify with its own workspace; the overlapped pair ignores their data
+    # dependence, so only the times mean anything)
+    ws2 = torch.empty_like(dec.ws)
+    s2 = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+
+    def verify_into(w):
+        api.spec_verify_forward(dec.base, dec.bkv, cfg.batch, dec.vtok, dec.tab[0], k + 1, max(dec.t) + k,
+                                dec.p_logits, w)
+    t_ser, t_ovl = [], []
+    dec._upload_positions()
+    for _ in range(5):
+        a_, b_ = ev(), ev()
+        a_.record()
+        dec.draft_phase()
+        verify_into(ws2)
+        b_.record()
+        torch.cuda.synchronize()
+        t_ser.append(a_.elapsed_time(b_))
+        a_, b_ = ev(), ev()
+        a_.record()
+        s2.wait_stream(main)
+        dec.draft_phase()
+        with torch.cuda.stream(s2):
+            verify_into(ws2)
+        main.wait_stream(s2)
+        b_.record()
+        torch.cuda.synchronize()
+        t_ovl.append(a_.elapsed_time(b_))
+    ser_ms, ovl_ms = float(np.median(t_ser)), float(np.median(t_ovl))
+    log(f"  draft steps + verify: back to back {ser_ms:.3f} ms, on two streams {ovl_ms:.3f} ms")
+    del ws2
+
     n1 = None
     if args.n1_compare:
         d1 = SpecDecoder(cfg.draft, dw, cfg.base, bw, cfg.batch, cap, k, seq_offs, P, inv_t, cfg.sample_seed,
@@ -514,6 +549,7 @@ def main():
         "draft_step_us_sequential_plan": round(step_seq * 1e3, 1),
         "drafting_speedup": round(step_seq / step_n, 4),
         "sequential_plan": n1,
+        "stage_overlap": {"back_to_back_ms": round(ser_ms, 3), "two_streams_ms": round(ovl_ms, 3)},
         "attention_input_cosine": {"per_layer": cos_layers,
                                    "mean_fuzzy_layers": round(float(np.mean(inner)), 5) if inner else None},
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
