@@ -310,16 +310,37 @@ hipError_t launch_t(const GemvParams &p, int grid, int ks, hipStream_t s) {
 // Normalised activations for the matrix-core products:
 // xn[sel][m][k] = round(gain_sel[k] * (xh[hrow][k] + xadd[sel][hrow][k]) / rms(hrow)),
 // rms from the row's sum-of-squares partials (summed in block order by every
-// wave, so all blocks agree bit for bit).  Grid (K / 2048, M, n_sel).
+// wave, so all blocks agree bit for bit).  Grid (K / 2048, M, n_sel).  The
+// row's values and gains are requested before the partials, so the two
+// memory round trips overlap (same arithmetic as x_norm8).
 template <typename T>
 __global__ __launch_bounds__(256) void k_norm_rows(GemvParams p, void *xn) {
     const int m = blockIdx.y, sel = blockIdx.z;
     const int hrow = x_row(p, p.m0 + m);
-    const float inv = row_inv_rms(p, hrow);
     const int k = (blockIdx.x * 256 + threadIdx.x) * 8;
-    if (k >= p.K) return;
-    float f[8];
-    x_norm8(p, sel, hrow, k, inv, f);
+    const bool live = k < p.K;
+    float4 h0 = make_float4(0.f, 0.f, 0.f, 0.f), h1 = h0, a0 = h0, a1 = h0, g0 = h0, g1 = h0;
+    if (live) {
+        const float *h = p.xh + (int64_t)hrow * p.K + k;
+        const float *g = p.xgain + (int64_t)sel * p.xgain_stride + k;
+        h0 = *reinterpret_cast<const float4 *>(h);
+        h1 = *reinterpret_cast<const float4 *>(h + 4);
+        g0 = *reinterpret_cast<const float4 *>(g);
+        g1 = *reinterpret_cast<const float4 *>(g + 4);
+        if (p.xadd) {
+            const float *a = p.xadd + (int64_t)sel * p.xadd_sel_stride + (int64_t)hrow * p.K + k;
+            a0 = *reinterpret_cast<const float4 *>(a);
+            a1 = *reinterpret_cast<const float4 *>(a + 4);
+        }
+    }
+    const float inv = row_inv_rms(p, hrow);   // whole wave
+    if (!live) return;
+    if (p.xadd) {
+        h0.x += a0.x; h0.y += a0.y; h0.z += a0.z; h0.w += a0.w;
+        h1.x += a1.x; h1.y += a1.y; h1.z += a1.z; h1.w += a1.w;
+    }
+    const float f[8] = {h0.x * inv * g0.x, h0.y * inv * g0.y, h0.z * inv * g0.z, h0.w * inv * g0.w,
+                        h1.x * inv * g1.x, h1.y * inv * g1.y, h1.z * inv * g1.z, h1.w * inv * g1.w};
     T *o = reinterpret_cast<T *>(xn) + ((int64_t)sel * p.Mtot + p.m0 + m) * p.K + k;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = Store<T>::from_f32(f[e]);
