@@ -9,14 +9,20 @@
 // run independently, reading K and V straight from HBM (no LDS staging):
 //   QK   S[key][qv] = sum_d K[key][d] q[qv][d]; lane (c, g) = (l % 16, l / 16)
 //        supplies K[key c][dims of group g] and q[qv c][the same dims], so
-//        each lane's K slice is contiguous in memory;
+//        each lane's K slice is contiguous in memory.  With a bfloat16 cache
+//        and head_dim a multiple of 32 the slices are eight dims, exactly the
+//        operand of v_mfma_f32_16x16x32_bf16: K goes in as loaded and q as
+//        three bfloat16 pieces (hi + mid + lo, float32 precision), three
+//        products per 32 dims instead of eight float32 ones, which matters
+//        where the matrix cores bound the kernel (long contexts, many rows);
 //   softmax  online (running max and sum per query vector) in float32; the
 //        scores of query vector c sit in lane group column c;
 //   PV   O[qv][dim] += P[qv][key] V[key][dim]: the probabilities are used in
 //        place as the A operand, lane (c, g) supplies V[key 4g + r][dims
 //        (HD / 16) c ...], so each lane reads HD / 16 contiguous elements.
-// Every product input is exact in float32 (K, V widened from the cache type),
-// so the result equals the float32 dot products up to summation order.  The
+// Every product input is exact in float32 (K, V widened from the cache type;
+// q's pieces sum to q up to the last bit of its float32 mantissa), so the
+// result equals the float32 dot products up to summation and that rounding.  The
 // waves' (max, sum, output) are merged in wave order through LDS; with several
 // key splits the workgroup publishes them and k_attn_merge combines the splits
 // in split order.
@@ -34,6 +40,29 @@ constexpr int kSplitMax = 64;
 constexpr int kMaxQV = 32;     // query vectors per workgroup at most
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Eight float32 values as three bfloat16 pieces hi + mid + lo whose sum
+// carries the value to float32 precision (each piece is the round-to-nearest
+// bfloat16 of what the previous pieces leave, and each subtraction is exact).
+// A bfloat16 K times a piece is exact in float32, so three matrix products on
+// the bfloat16 matrix cores give the float32 dot products up to summation
+// order (the float32 matrix instruction takes four dims per step, the
+// bfloat16 one thirty-two).
+__device__ __forceinline__ void split3_bf16(const float *x, bf16x8 &hi, bf16x8 &mid, bf16x8 &lo) {
+    uint16_t h[8], m[8], l[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        h[e] = f32_to_bf16(x[e]);
+        const float r1 = x[e] - bf16_to_f32(h[e]);
+        m[e] = f32_to_bf16(r1);
+        const float r2 = r1 - bf16_to_f32(m[e]);
+        l[e] = f32_to_bf16(r2);
+    }
+    __builtin_memcpy(&hi, h, 16);
+    __builtin_memcpy(&mid, m, 16);
+    __builtin_memcpy(&lo, l, 16);
+}
 
 // N consecutive elements of the cache type, widened to float.
 template <int N>
@@ -207,6 +236,18 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
         qpos[nb] = pos;
     }
 
+    // bfloat16 caches with 8 dims per lane and piece: QK on the bfloat16
+    // matrix cores (K slices are the A operand as loaded), q in three pieces
+    constexpr bool kBfQK = sizeof(T) == 2 && DK == 8;
+    bf16x8 qh[kBfQK ? NQB : 1][kBfQK ? NP : 1], qm2[kBfQK ? NQB : 1][kBfQK ? NP : 1],
+        ql[kBfQK ? NQB : 1][kBfQK ? NP : 1];
+    if constexpr (kBfQK) {
+#pragma unroll
+        for (int nb = 0; nb < NQB; ++nb)
+#pragma unroll
+            for (int i = 0; i < NP; ++i) split3_bf16(&qreg[nb][DK * i], qh[nb][i], qm2[nb][i], ql[nb][i]);
+    }
+
     float m_run[NQB], l_run[NQB];
     f32x4 acc[NQB][DV];
 #pragma unroll
@@ -228,11 +269,23 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
 #pragma unroll
         for (int nb = 0; nb < NQB; ++nb) {
             f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (kBfQK) {
+                // the small pieces first
 #pragma unroll
-            for (int i = 0; i < NP; ++i)
+                for (int i = 0; i < NP; ++i) {
+                    bf16x8 kv;
+                    __builtin_memcpy(&kv, kcur[i].w, 16);
+                    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, ql[nb][i], sc, 0, 0, 0);
+                    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qm2[nb][i], sc, 0, 0, 0);
+                    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qh[nb][i], sc, 0, 0, 0);
+                }
+            } else {
 #pragma unroll
-                for (int e = 0; e < DK; ++e)
-                    sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kcur[i][e], qreg[nb][DK * i + e], sc, 0, 0, 0);
+                for (int i = 0; i < NP; ++i)
+#pragma unroll
+                    for (int e = 0; e < DK; ++e)
+                        sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kcur[i][e], qreg[nb][DK * i + e], sc, 0, 0, 0);
+            }
             // lane holds S[key kb + 4 g + r][qv 16 nb + c]
             float pr[4];
             float mx = -INFINITY;
