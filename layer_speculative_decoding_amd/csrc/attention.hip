@@ -20,6 +20,13 @@
 //   PV   O[qv][dim] += P[qv][key] V[key][dim]: the probabilities are used in
 //        place as the A operand, lane (c, g) supplies V[key 4g + r][dims
 //        (HD / 16) c ...], so each lane reads HD / 16 contiguous elements.
+//        On the bfloat16 path a wave takes 32-key chunks (two blocks): lane
+//        (c, g) then holds P of keys 4g..4g+3 and 16+4g..16+4g+3, which is an
+//        A operand of v_mfma_f32_16x16x32_bf16 as it stands (the order of the
+//        summed keys inside one instruction is free as long as B matches);
+//        the chunk's V rows go to a per-wave LDS stage and each lane reads
+//        back the same eight keys of one dim (V is key-major in the cache, the
+//        instruction wants eight keys per lane), P in three bfloat16 pieces.
 // Every product input is exact in float32 (K, V widened from the cache type;
 // q's pieces sum to q up to the last bit of its float32 mantissa), so the
 // result equals the float32 dot products up to summation and that rounding.  The
@@ -159,8 +166,17 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
     constexpr int DV = HD / 16;                   // dims per lane per key in PV
     constexpr int QVB = 16 * NQB;
     constexpr int NREG = NQB * DV * 4;            // output values per lane
+    // bfloat16 caches with 8 dims per lane and piece run both products on the
+    // bfloat16 matrix cores (see split3_bf16): QK with the K slices as loaded,
+    // PV over 32-key chunks whose V rows are staged per wave in LDS and read
+    // back key-contiguous per lane, the layout of the B operand
+    constexpr bool kBf = sizeof(T) == 2 && DK == 8;
+    constexpr int CK = 32;                        // keys per chunk (two 16-key blocks)
+    constexpr int VLD = HD + 8;                   // staged V row stride (elements)
+    constexpr int NVL = kBf ? CK * HD / (8 * kWave) : 1;   // 16-byte V loads per lane and chunk
     __shared__ float m_s[kWaves][QVB], l_s[kWaves][QVB];
     __shared__ __align__(16) float o_s[kWaves - 1][NREG][64];
+    __shared__ __align__(16) uint16_t vst[kBf ? kWaves * CK * VLD : 8];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -209,9 +225,31 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
             if (kb + 4 * g + r < ke) vr[r].load(Vc + (int64_t)(kb + 4 * g + r) * HD + DV * c);
         }
     };
+    // bfloat16 path: K of the chunk's two blocks and its V rows (16-byte
+    // pieces, row-major, zero past the split's end)
+    Raw<T, DK> kn[kBf ? 2 : 1][NP];
+    uint4 vn[NVL];
+    auto load_chunk = [&](int kb) {
+#pragma unroll
+        for (int hb = 0; hb < (kBf ? 2 : 1); ++hb)
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                kn[hb][i].zero();
+                if (kb + 16 * hb + c < ke) kn[hb][i].load(Kc + (int64_t)(kb + 16 * hb + c) * HD + DK * g + 4 * DK * i);
+            }
+#pragma unroll
+        for (int v = 0; v < NVL; ++v) {
+            const int e = (v * kWave + lane) * 8, key = e / HD, dim = e - key * HD;
+            vn[v] = kb + key < ke ? ld16(Vc + (int64_t)(kb + key) * HD + dim) : make_uint4(0, 0, 0, 0);
+        }
+    };
     // the first block is requested before the query vectors, the next one
     // before the current one is consumed
-    if (ks + kKB * wave < ke) load_kv(ks + kKB * wave);
+    if constexpr (kBf) {
+        if (ks + CK * wave < ke) load_chunk(ks + CK * wave);
+    } else {
+        if (ks + kKB * wave < ke) load_kv(ks + kKB * wave);
+    }
 
     // B operand of QK: q[qv = 16 nb + c][dim (4 DK) i + DK g + e] at t = DK i + e
     float qreg[NQB][NT];
@@ -236,12 +274,9 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
         qpos[nb] = pos;
     }
 
-    // bfloat16 caches with 8 dims per lane and piece: QK on the bfloat16
-    // matrix cores (K slices are the A operand as loaded), q in three pieces
-    constexpr bool kBfQK = sizeof(T) == 2 && DK == 8;
-    bf16x8 qh[kBfQK ? NQB : 1][kBfQK ? NP : 1], qm2[kBfQK ? NQB : 1][kBfQK ? NP : 1],
-        ql[kBfQK ? NQB : 1][kBfQK ? NP : 1];
-    if constexpr (kBfQK) {
+    // q as three bfloat16 pieces (B operand of QK on the bfloat16 path)
+    bf16x8 qh[kBf ? NQB : 1][kBf ? NP : 1], qm2[kBf ? NQB : 1][kBf ? NP : 1], ql[kBf ? NQB : 1][kBf ? NP : 1];
+    if constexpr (kBf) {
 #pragma unroll
         for (int nb = 0; nb < NQB; ++nb)
 #pragma unroll
@@ -258,70 +293,144 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
         for (int j = 0; j < DV; ++j) acc[nb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    for (int kb = ks + kKB * wave; kb < ke; kb += kSpan) {
-        Raw<T, DK> kcur[NP];
-        Raw<T, DV> vcur[4];
+    if constexpr (kBf) {
+        uint16_t *vt = vst + wave * CK * VLD;
+        for (int kb = ks + CK * wave; kb < ke; kb += CK * kWaves) {
+            // stage this chunk's V rows, then request the next chunk
 #pragma unroll
-        for (int i = 0; i < NP; ++i) kcur[i] = kr[i];
+            for (int v = 0; v < NVL; ++v) {
+                const int e = (v * kWave + lane) * 8, key = e / HD, dim = e - key * HD;
+                *reinterpret_cast<uint4 *>(&vt[key * VLD + dim]) = vn[v];
+            }
+            Raw<T, DK> kc2[2][NP];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vcur[r] = vr[r];
-        if (kb + kSpan < ke) load_kv(kb + kSpan);
+            for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-        for (int nb = 0; nb < NQB; ++nb) {
-            f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (kBfQK) {
-                // the small pieces first
+                for (int i = 0; i < NP; ++i) kc2[hb][i] = kn[hb][i];
+            if (kb + CK * kWaves < ke) load_chunk(kb + CK * kWaves);
+            // the wave's own LDS writes precede its reads below (in-order LDS)
+            asm volatile("" ::: "memory");
 #pragma unroll
-                for (int i = 0; i < NP; ++i) {
-                    bf16x8 kv;
-                    __builtin_memcpy(&kv, kcur[i].w, 16);
-                    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, ql[nb][i], sc, 0, 0, 0);
-                    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qm2[nb][i], sc, 0, 0, 0);
-                    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qh[nb][i], sc, 0, 0, 0);
+            for (int nb = 0; nb < NQB; ++nb) {
+                // QK of both blocks: lane holds S[key kb + 16 hb + 4 g + r][qv 16 nb + c]
+                float pr[8];
+                float mx = -INFINITY;
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb) {
+                    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int i = 0; i < NP; ++i) {
+                        bf16x8 kv;
+                        __builtin_memcpy(&kv, kc2[hb][i].w, 16);
+                        // the small pieces first
+                        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, ql[nb][i], sc, 0, 0, 0);
+                        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qm2[nb][i], sc, 0, 0, 0);
+                        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qh[nb][i], sc, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int key = kb + 16 * hb + 4 * g + r;
+                        pr[4 * hb + r] = (key < ke && key <= qpos[nb]) ? sc[r] * scale : -INFINITY;
+                        mx = fmaxf(mx, pr[4 * hb + r]);
+                    }
                 }
-            } else {
+                mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+                mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+                const float m_new = fmaxf(m_run[nb], mx);
+                const bool none = m_new == -INFINITY;
+                float sum = 0.f;
 #pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    pr[j] = none ? 0.f : expf(pr[j] - m_new);
+                    sum += pr[j];
+                }
+                sum += __shfl_xor(sum, 16, kWave);
+                sum += __shfl_xor(sum, 32, kWave);
+                const float corr = none ? 1.f : expf(m_run[nb] - m_new);
+                l_run[nb] = l_run[nb] * corr + sum;
+                m_run[nb] = m_new;
+                f32x4 cr;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * g + r, kWave);
+#pragma unroll
+                for (int j = 0; j < DV; ++j) acc[nb][j] *= cr;
+                // PV: A = P[qv c][keys of lane group g: 4g..4g+3, 16+4g..16+4g+3]
+                // (as the QK output holds them), B = V[the same keys][dim DV c + j]
+                bf16x8 ph, pm, pl;
+                split3_bf16(pr, ph, pm, pl);
+#pragma unroll
+                for (int j = 0; j < DV; ++j) {
+                    uint16_t vv[8];
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        const int key = (t < 4 ? 0 : 16) + 4 * g + (t & 3);
+                        vv[t] = vt[key * VLD + DV * c + j];
+                    }
+                    bf16x8 vb;
+                    __builtin_memcpy(&vb, vv, 16);
+                    acc[nb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, acc[nb][j], 0, 0, 0);
+                    acc[nb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pm, vb, acc[nb][j], 0, 0, 0);
+                    acc[nb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, acc[nb][j], 0, 0, 0);
+                }
+            }
+            // this chunk's reads precede the next chunk's staging writes
+            asm volatile("" ::: "memory");
+        }
+    } else {
+        for (int kb = ks + kKB * wave; kb < ke; kb += kSpan) {
+            Raw<T, DK> kcur[NP];
+            Raw<T, DV> vcur[4];
+    #pragma unroll
+            for (int i = 0; i < NP; ++i) kcur[i] = kr[i];
+    #pragma unroll
+            for (int r = 0; r < 4; ++r) vcur[r] = vr[r];
+            if (kb + kSpan < ke) load_kv(kb + kSpan);
+    #pragma unroll
+            for (int nb = 0; nb < NQB; ++nb) {
+                f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
                 for (int i = 0; i < NP; ++i)
-#pragma unroll
+    #pragma unroll
                     for (int e = 0; e < DK; ++e)
                         sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kcur[i][e], qreg[nb][DK * i + e], sc, 0, 0, 0);
+                // lane holds S[key kb + 4 g + r][qv 16 nb + c]
+                float pr[4];
+                float mx = -INFINITY;
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = kb + 4 * g + r;
+                    pr[r] = (key < ke && key <= qpos[nb]) ? sc[r] * scale : -INFINITY;
+                    mx = fmaxf(mx, pr[r]);
+                }
+                mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+                mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+                const float m_new = fmaxf(m_run[nb], mx);
+                const bool none = m_new == -INFINITY;
+                float sum = 0.f;
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    pr[r] = none ? 0.f : expf(pr[r] - m_new);
+                    sum += pr[r];
+                }
+                sum += __shfl_xor(sum, 16, kWave);
+                sum += __shfl_xor(sum, 32, kWave);
+                const float corr = none ? 1.f : expf(m_run[nb] - m_new);
+                l_run[nb] = l_run[nb] * corr + sum;
+                m_run[nb] = m_new;
+                // rescale of the outputs of query vectors 16 nb + 4 g + r (held by lane 4 g + r)
+                f32x4 cr;
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * g + r, kWave);
+    #pragma unroll
+                for (int j = 0; j < DV; ++j) acc[nb][j] *= cr;
+    #pragma unroll
+                for (int r = 0; r < 4; ++r)
+    #pragma unroll
+                    for (int j = 0; j < DV; ++j)
+                        acc[nb][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(pr[r], vcur[r][j], acc[nb][j], 0, 0, 0);
             }
-            // lane holds S[key kb + 4 g + r][qv 16 nb + c]
-            float pr[4];
-            float mx = -INFINITY;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = kb + 4 * g + r;
-                pr[r] = (key < ke && key <= qpos[nb]) ? sc[r] * scale : -INFINITY;
-                mx = fmaxf(mx, pr[r]);
-            }
-            mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-            const float m_new = fmaxf(m_run[nb], mx);
-            const bool none = m_new == -INFINITY;
-            float sum = 0.f;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                pr[r] = none ? 0.f : expf(pr[r] - m_new);
-                sum += pr[r];
-            }
-            sum += __shfl_xor(sum, 16, kWave);
-            sum += __shfl_xor(sum, 32, kWave);
-            const float corr = none ? 1.f : expf(m_run[nb] - m_new);
-            l_run[nb] = l_run[nb] * corr + sum;
-            m_run[nb] = m_new;
-            // rescale of the outputs of query vectors 16 nb + 4 g + r (held by lane 4 g + r)
-            f32x4 cr;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * g + r, kWave);
-#pragma unroll
-            for (int j = 0; j < DV; ++j) acc[nb][j] *= cr;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int j = 0; j < DV; ++j)
-                    acc[nb][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(pr[r], vcur[r][j], acc[nb][j], 0, 0, 0);
         }
+
     }
 
     // merge the four waves in wave order
