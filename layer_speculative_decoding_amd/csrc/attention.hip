@@ -183,12 +183,31 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
     const int c = lane & 15, g = lane >> 4;
     const int G = p.hq / p.hkv;
     const int QB = QVB / G;                       // rows per workgroup
-    const int gi = blockIdx.y / p.hkv;
-    const int kvh = blockIdx.y - gi * p.hkv;
-    const int b = blockIdx.z / p.splits;
-    const int sp = blockIdx.z - b * p.splits;
+    // Workgroups are dispatched to the eight XCDs round robin by linear id,
+    // and each XCD has its own L2.  The query blocks of one (layer, kv head,
+    // sequence, split) read the same K / V, so the linear ids are renumbered
+    // to put them eight apart (same XCD, close in time); a tail of fewer
+    // than eight such groups keeps the plain order.
+    int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+    {
+        const int nqb = gridDim.x, ny = gridDim.y;
+        const int lin = bx + nqb * (by + ny * bz);
+        const int span = 8 * nqb;
+        const int full = (nqb * ny * (int)gridDim.z) / span * span;
+        if (nqb > 1 && lin < full) {
+            const int off = lin % span;
+            const int grp = (lin / span) * 8 + (off & 7);
+            bx = off >> 3;
+            by = grp % ny;
+            bz = grp / ny;
+        }
+    }
+    const int gi = by / p.hkv;
+    const int kvh = by - gi * p.hkv;
+    const int b = bz / p.splits;
+    const int sp = bz - b * p.splits;
     const int mseq = p.rows.mseq;
-    const int i0 = blockIdx.x * QB;
+    const int i0 = bx * QB;
     const int nrows = min(QB, mseq - i0);
     const int ntok = p.rows.n_tok ? p.rows.n_tok[b] : mseq;
     const int pos0 = p.rows.start_pos[b];
