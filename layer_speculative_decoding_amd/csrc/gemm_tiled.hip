@@ -17,7 +17,8 @@
 //  * K advances in 64-element steps through one LDS stage (rows padded by 16
 //    bytes, so the fragment reads of a wave spread over all banks); each
 //    lane moves 16 bytes per row (128 contiguous bytes per row per 8 lanes),
-//    the weights two steps ahead of the matrix instructions (HBM latency),
+//    the weights two (128-row tiles) or three (64-row) steps ahead of the
+//    matrix instructions (HBM latency),
 //    the activations one step ahead (they stay in L2);
 //  * the 64-row weight tile is chosen when 128-row tiles would leave CUs
 //    without a workgroup, and when even those are too few, K is split: each
@@ -130,8 +131,8 @@ __device__ __forceinline__ void tile_epilogue(const GemvParams &p, const TileArg
 }
 
 // 4 waves (2 x 2), each 64 activation rows x 16 WNB weight rows; K steps of
-// 64 through one LDS stage, the weights of step k + 2 requested before step
-// k's matrix instructions, the activations of step k + 1.  SPLIT: workgroup
+// 64 through one LDS stage, the weights of step k + DIST requested before
+// step k's matrix instructions, the activations of step k + 1.  SPLIT: workgroup
 // b covers tile b % T over K slice b / T and stores its accumulators.
 template <int EPI, int WNB, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void k_gemm_tile(GemvParams p, TileArgs ta) {
@@ -140,7 +141,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(GemvParams p, TileArgs ta)
     constexpr int HB = WNB / 2;                  // 16-unit blocks per wave per member
     constexpr int RPP = 32;                      // rows per load pass (8 lanes x 16 bytes per row)
     constexpr int LA = kBM / RPP, LB = BN / RPP; // load passes per step
-    constexpr int DIST = 2;
+    // weight steps in flight: three for 64-row tiles (their per-step bytes are
+    // half, and four workgroups share a CU), two for 128-row tiles (whose
+    // register budget has no room for a third)
+    constexpr int DIST = WNB == 2 ? 3 : 2;
     __shared__ __align__(16) uint16_t lds[(kBM + BN) * kLDK];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -251,12 +255,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(GemvParams p, TileArgs ta)
     }
 
     if constexpr (SPLIT) {
+        // 16-row activation blocks past the call's rows hold nothing; they
+        // are neither stored here nor read back by the slice sum
         float4 *dst = reinterpret_cast<float4 *>(ta.part) + ((int64_t)slice * T + t) * (kWMB * WNB) * 256 + tid;
 #pragma unroll
         for (int a = 0; a < kWMB; ++a)
+            if (q.m0 + 64 * wm + 16 * a < p.M)
 #pragma unroll
-            for (int c = 0; c < WNB; ++c)
-                dst[(a * WNB + c) * 256] = make_float4(acc[a][c][0], acc[a][c][1], acc[a][c][2], acc[a][c][3]);
+                for (int c = 0; c < WNB; ++c)
+                    dst[(a * WNB + c) * 256] = make_float4(acc[a][c][0], acc[a][c][1], acc[a][c][2], acc[a][c][3]);
     } else {
         tile_epilogue<EPI, WNB>(p, ta, q, acc);
     }
@@ -268,6 +275,8 @@ template <int EPI, int WNB>
 __global__ __launch_bounds__(256) void k_gemm_tile_epi(GemvParams p, TileArgs ta) {
     constexpr int BN = 32 * WNB;
     const int T = ta.gm * ta.gn, t = blockIdx.x;
+    const TilePos q = tile_pos<EPI, BN>(p, ta, t);
+    const int wm = (threadIdx.x >> 6) & 1;
     const float4 *src = reinterpret_cast<const float4 *>(ta.part) + (int64_t)t * (kWMB * WNB) * 256 + threadIdx.x;
     // the blocks of up to SG slices are requested together, then added in
     // slice order (the sum's order is fixed: slice 0, 1, 2, ...)
@@ -286,8 +295,9 @@ __global__ __launch_bounds__(256) void k_gemm_tile_epi(GemvParams p, TileArgs ta
             for (int a = 0; a < kWMB; ++a)
 #pragma unroll
                 for (int c = 0; c < WNB; ++c)
-                    v[g][a][c] = k0 + g < ta.ks ? src[(k0 + g) * sstride + (a * WNB + c) * 256]
-                                                : make_float4(0.f, 0.f, 0.f, 0.f);
+                    v[g][a][c] = (k0 + g < ta.ks && q.m0 + 64 * wm + 16 * a < p.M)
+                                     ? src[(k0 + g) * sstride + (a * WNB + c) * 256]
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int g = 0; g < SG; ++g)
 #pragma unroll
@@ -296,7 +306,7 @@ __global__ __launch_bounds__(256) void k_gemm_tile_epi(GemvParams p, TileArgs ta
                 for (int c = 0; c < WNB; ++c)
                     if (k0 + g < ta.ks) acc[a][c] += f32x4{v[g][a][c].x, v[g][a][c].y, v[g][a][c].z, v[g][a][c].w};
     }
-    tile_epilogue<EPI, WNB>(p, ta, tile_pos<EPI, BN>(p, ta, t), acc);
+    tile_epilogue<EPI, WNB>(p, ta, q, acc);
 }
 
 template <int WNB, int EPI>
@@ -346,11 +356,12 @@ Pick pick(const GemvParams &p, size_t part_bytes) {
         if (fits(p, 128) && (int64_t)gm * (rows / 128) >= 256) return {128, 1};
         if (!fits(p, 64)) return {0, 1};
         k.bn = 64;
-        // fewer than 384 tiles: slices so that about 1024 workgroups run,
-        // each over >= 2 K steps (more tiles run better unsplit: the
-        // slices' float32 partials cost a write and a read each)
+        // fewer than 384 tiles: slices so that at most 1024 workgroups run
+        // (four per CU resident at once: no tail round), each over >= 2 K
+        // steps (more tiles run better unsplit: the slices' float32 partials
+        // cost a write and a read each)
         const int64_t T = (int64_t)gm * (rows / 64);
-        k.ks = T >= 384 ? 1 : (int)((1024 + T - 1) / T);
+        k.ks = T >= 384 ? 1 : (int)(1024 / T);
     }
     k.ks = k.ks < 1 ? 1 : (k.ks > kMaxSplit ? kMaxSplit : k.ks);
     if (k.ks > nk / 2) k.ks = nk / 2 < 1 ? 1 : nk / 2;
