@@ -135,6 +135,38 @@ def test_verify_matches_oracle(name, m):
         np.testing.assert_array_equal(np.argmax(zg[b], 1)[ok], np.argmax(zo, 1)[ok])
 
 
+
+@pytest.mark.parametrize("name", ["hd64-bias-bf16", "hd128-bf16"])
+def test_verify_split_keys_ragged_batch(name):
+    """Verify rows of three sequences at a context long enough for several
+    key splits, with ragged start positions.  For hd64-bias-bf16 the
+    attention launch has twelve (kv head, sequence, split) groups of two
+    query blocks, so its workgroup renumbering covers eight groups and leaves
+    a tail of four in plain order; hd128-bf16 has 24 groups (no tail)."""
+    from layer_speculative_decoding_amd import api
+    B, P, m = 3, 190, 6
+    shape, tol, om, gm, gkv, okv, prompts = _setup(name, B, P + m, cap=P + m + 4)
+    say(f"verify split keys {name} B={B} P={P} m={m}")
+    w = ws(api.spec_workspace_bytes(gm, B, max(P, m), 1))
+    api.spec_verify_forward(gm, gkv, B, i32(prompts[:, :P]), i32([0] * B), P, P - 1, None, w)
+    for b in range(B):
+        forward(om, okv, b, prompts[b, :P], range(P), logits=None)
+    vt = prompts[:, P:P + m].copy()
+    logits = torch.zeros(B, m, shape.vocab, device="cuda")
+    st = np.array([P, P - 3, P - 7], dtype=np.int32)
+    api.spec_verify_forward(gm, gkv, B, i32(vt), i32(st), m, int(st.max()) + m - 1, logits, w)
+    torch.cuda.synchronize()
+    zg = logits.cpu().numpy()
+    for b in range(B):
+        zo = forward(om, okv, b, vt[b], range(st[b], st[b] + m), logits="all")
+        err = rel_linf(zg[b], zo)
+        say(f"  b={b} start {st[b]} logits rel {err:.2e}")
+        assert err < tol
+        srt = np.sort(zo, axis=1)
+        ok = (srt[:, -1] - srt[:, -2]) >= exclusion(zg[b], zo, 0.0)
+        np.testing.assert_array_equal(np.argmax(zg[b], 1)[ok], np.argmax(zo, 1)[ok])
+
+
 PLANS = {
     "c1-draft-f32": [[[0], [1]], [[0, 1]]],
     "gqa-bias-f32": [[[0], [1, 2], [3]], [[0, 1, 2, 3]]],
