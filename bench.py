@@ -136,7 +136,7 @@ def pmc_mfma_summary(csv_path, command):
     print()
     print("The run covers the llama-1b-8b workload: three prompt prefills (base 511 rows, draft 512 rows:"
           " k_gemm_tile), then four rounds of draft steps (k_gemv, one row), verify and calibration (k_gemm_mfma,"
-          " 6 rows) and attention (k_attn, float32 matrix instructions).  Flops are what the matrix cores"
+          " 6 rows) and attention (k_attn: bf16 matrix instructions on the bf16 caches, operands in three bf16 pieces).  Flops are what the matrix cores"
           " executed (padding rows included); the bf16 peak is 2500 TFLOP/s, the float32 one 157.3.")
     print()
     top, ft = max(fam.items(), key=lambda kv: kv[1]["ns"])

@@ -219,8 +219,11 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
     int kmax = last_row >= 0 ? pos0 + last_row : -1;
     if (kmax >= p.capacity) kmax = p.capacity - 1;
     const int total = kmax + 1;
+    // split ranges are whole rounds of the four waves (16-key blocks, or
+    // 32-key chunks on the bfloat16 path)
+    constexpr int SPAN = kBf ? CK * kWaves : kSpan;
     int per = (total + p.splits - 1) / p.splits;
-    per = ((per + kSpan - 1) / kSpan) * kSpan;
+    per = ((per + SPAN - 1) / SPAN) * SPAN;
     const int ks = sp * per;
     const int ke = min(total, ks + per);
 
@@ -605,14 +608,17 @@ int attention_split_max() { return kSplitMax; }
 // kTargetWG workgroups, each split at least one round of the four waves.
 // Calls with more than 64 rows (prompt prefills) have many query blocks and
 // never split (the split partials are sized for 64 rows).
-int attention_splits(int n_group, int batch, int hq, int hkv, int mseq, int max_pos) {
+int attention_splits(int dtype, int hd, int n_group, int batch, int hq, int hkv, int mseq, int max_pos) {
     constexpr int kTargetWG = 512;
+    // keys per round of a workgroup: 32-key chunks per wave on the bfloat16
+    // path (bf16 cache, head_dim a multiple of 32), 16-key blocks otherwise
+    const int span = (dtype != 0 && hd % 32 == 0) ? 2 * kSpan : kSpan;
     if ((long)batch * mseq > 64) return 1;
     const int G = hq / hkv;
     const int QB = 16 * qv_blocks(G, mseq) / G;
     const int nqb = (mseq + QB - 1) / QB;
     const long base = (long)nqb * n_group * hkv * batch;
-    const int rounds = (max_pos + 1 + kSpan - 1) / kSpan;
+    const int rounds = (max_pos + 1 + span - 1) / span;
     long sp = (kTargetWG + base - 1) / base;
     if (sp > rounds) sp = rounds;
     if (sp > kSplitMax) sp = kSplitMax;

@@ -329,7 +329,7 @@ hipError_t run_stage(Fwd &f, int l0, int n, int mlp_mode, float *cos_out = nullp
     ap.kc = f.kv->k; ap.vc = f.kv->v; ap.layer0 = l0; ap.n_group = n; ap.batch = f.batch;
     ap.hq = d.n_q_heads; ap.hkv = d.n_kv_heads; ap.hd = d.head_dim; ap.capacity = f.kv->capacity;
     ap.rows = f.rows; ap.max_pos = f.max_pos;
-    ap.splits = attention_splits(n, f.batch, d.n_q_heads, d.n_kv_heads, f.mseq, f.max_pos);
+    ap.splits = attention_splits(d.dtype, d.head_dim, n, f.batch, d.n_q_heads, d.n_kv_heads, f.mseq, f.max_pos);
     ap.o = o; ap.o_sel_stride = (int64_t)R * qd;
     ap.part_acc = at<float>(f.ws, f.c.pacc); ap.part_ml = at<float>(f.ws, f.c.pml); ap.Mtot = R;
     {

@@ -169,7 +169,7 @@ struct AttnParams {
     int Mtot;
 };
 hipError_t launch_attention(int dtype, const AttnParams &p, hipStream_t s);
-int attention_splits(int n_group, int batch, int hq, int hkv, int mseq, int max_pos);
+int attention_splits(int dtype, int hd, int n_group, int batch, int hq, int hkv, int mseq, int max_pos);
 int attention_split_max();
 int attention_max_group();   // largest n_q_heads / n_kv_heads
 
