@@ -26,8 +26,11 @@
  *    beyond the KV capacity are treated as invalid rows (no KV write).
  *  - Floating point: weights and KV are float32 (SPEC_F32) or bfloat16
  *    (SPEC_BF16).  Activations, norms, RoPE, softmax and accumulation are
- *    float32.  On the bf16 path every input vector of a matrix product is
- *    rounded to bfloat16 (nearest, ties to even) and K/V are stored as bf16.
+ *    float32.  On the bf16 path every input vector of a weight product is
+ *    rounded to bfloat16 (nearest, ties to even) and K/V are stored as bf16;
+ *    attention keeps q and the softmax probabilities at float32 precision
+ *    against the bf16 K/V (on the bf16 matrix cores each is split into three
+ *    bf16 pieces whose sum carries the float32 value).
  *  - Random numbers: Philox4x64-10 (Salmon et al., SC'11), key = (seed, b),
  *    counter = (v >> 2, position of the token being decided, 0, purpose),
  *    word v & 3, u = ((word >> 41) + 0.5) * 2^-23.  Purposes: 0 draft
