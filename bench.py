@@ -51,22 +51,26 @@ def stored_traffic(kernel):
     or None if there is none for it or the kernels changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
-            kv = dict(line.strip().split(": ", 1) for line in f if line.startswith(("kernel: ", "traffic_bytes_per_launch: ", "source_sha256: ")))
+            lines = [line.strip() for line in f]
     except OSError:
         return None
-    if kv.get("kernel") != kernel or kv.get("source_sha256") != kernel_source_hash():
+    sha = [ln.split(": ", 1)[1] for ln in lines if ln.startswith("source_sha256: ")]
+    if not sha or sha[0] != kernel_source_hash():
         return None
-    return int(kv["traffic_bytes_per_launch"])
+    for i, ln in enumerate(lines[:-1]):
+        if ln == f"kernel: {kernel}" and lines[i + 1].startswith("traffic_bytes_per_launch: "):
+            return int(lines[i + 1].split(": ", 1)[1])
+    return None
 
 
-def pmc_summary(fetch_csv, write_csv, kernel, command):
+def pmc_summary(fetch_csv, write_csv, kernels, command):
     """Markdown summary of two counter runs (FETCH_SIZE, WRITE_SIZE; KiB per
     dispatch) of `bench.py --pmc-probe`: each counter is scaled by what it
     reads for the probe's device copy of PROBE_COPY_BYTES, then averaged over
-    the dispatches of `kernel`."""
+    the dispatches of each kernel in `kernels`."""
     import csv
 
-    def load(path, counter):
+    def load(path, counter, kernel):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
         rows.sort(key=lambda r: int(r["Dispatch_Id"]))
         copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]][-1]
@@ -74,27 +78,33 @@ def pmc_summary(fetch_csv, write_csv, kernel, command):
         vals = [float(r["Counter_Value"]) for r in rows if kernel + "(" in r["Kernel_Name"]]
         return copy, factor, vals
 
-    fc, ff, fv = load(fetch_csv, "FETCH_SIZE")
-    wc, wf, wv = load(write_csv, "WRITE_SIZE")
-    fetch = sum(fv) / len(fv) * ff * 1024
-    write = sum(wv) / len(wv) * wf * 1024
-    print(f"# HBM traffic of {kernel} (hardware counters)")
+    print(f"# HBM traffic of {', '.join(kernels)} (hardware counters)")
     print()
     print("Commands (from the repository root, TMPDIR=/tmp):")
     print()
     for c in command:
         print(f"    {c}")
     print()
+    fc, ff, _ = load(fetch_csv, "FETCH_SIZE", kernels[0])
+    wc, wf, _ = load(write_csv, "WRITE_SIZE", kernels[0])
     print(f"Calibration: the probe's device copy of {PROBE_COPY_BYTES} bytes reads FETCH_SIZE {fc:.1f} KiB and "
           f"WRITE_SIZE {wc:.1f} KiB, so the counters are scaled by {ff:.4f} (fetch) and {wf:.4f} (write).")
     print()
-    print(f"| counter | dispatches | raw avg KiB | scaled avg bytes |")
-    print(f"|---|---|---|---|")
-    print(f"| FETCH_SIZE | {len(fv)} | {sum(fv) / len(fv):.1f} | {fetch:.0f} |")
-    print(f"| WRITE_SIZE | {len(wv)} | {sum(wv) / len(wv):.1f} | {write:.0f} |")
+    print(f"| kernel | counter | dispatches | raw avg KiB | scaled avg bytes |")
+    print(f"|---|---|---|---|---|")
+    totals = []
+    for kernel in kernels:
+        _, _, fv = load(fetch_csv, "FETCH_SIZE", kernel)
+        _, _, wv = load(write_csv, "WRITE_SIZE", kernel)
+        fetch = sum(fv) / len(fv) * ff * 1024
+        write = sum(wv) / len(wv) * wf * 1024
+        print(f"| {kernel} | FETCH_SIZE | {len(fv)} | {sum(fv) / len(fv):.1f} | {fetch:.0f} |")
+        print(f"| {kernel} | WRITE_SIZE | {len(wv)} | {sum(wv) / len(wv):.1f} | {write:.0f} |")
+        totals.append((kernel, int(round(fetch + write))))
     print()
-    print(f"kernel: {kernel}")
-    print(f"traffic_bytes_per_launch: {int(round(fetch + write))}")
+    for kernel, t in totals:
+        print(f"kernel: {kernel}")
+        print(f"traffic_bytes_per_launch: {t}")
     print(f"source_sha256: {kernel_source_hash()}")
 
 
@@ -255,8 +265,8 @@ def main():
                          "acceptance and tokens/s")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run a few rounds and one device copy of known size, for hardware-counter runs")
-    ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL"),
-                    help="print the traffic summary of two counter runs of --pmc-probe")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="FETCH_CSV WRITE_CSV KERNEL",
+                    help="print the traffic summary of two counter runs of --pmc-probe for one or more kernels")
     ap.add_argument("--pmc-mfma-summary", metavar="CSV",
                     help="print the matrix-core utilisation summary of a counter run of --pmc-probe")
     ap.add_argument("--rocprof-summary", nargs=2, metavar=("STATS_CSV", "TRACE_CSV"),
@@ -279,8 +289,11 @@ def main():
             f"python bench.py --pmc-mfma-summary {args.pmc_mfma_summary} > profiles/mfma_util.md"])
         return
     if args.pmc_summary:
-        f, w, kname = args.pmc_summary
-        pmc_summary(f, w, kname, [
+        if len(args.pmc_summary) < 3:
+            ap.error("--pmc-summary needs FETCH_CSV WRITE_CSV KERNEL [KERNEL ...]")
+        f, w, knames = args.pmc_summary[0], args.pmc_summary[1], args.pmc_summary[2:]
+        kname = "' '".join(knames)
+        pmc_summary(f, w, knames, [
             f"timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d {odir(f)} -o run "
             "-- python bench.py --warmup 1 --pmc-probe",
             f"timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d {odir(w)} -o run "

@@ -88,8 +88,8 @@ __global__ __launch_bounds__(64 * KS * (epi_is_pair(EPI) ? 2 : 1)) void k_gemm_m
 #pragma unroll
         for (int r = 0; r < 4; ++r) { best_v[t][r] = -INFINITY; best_i[t][r] = 0x7FFFFFFF; }
 
-    for (int u = blockIdx.x; u < p.n_units; u += gridDim.x) {
-        int r0b, r1b;
+    // first weight rows of unit u's two blocks
+    auto unit_blocks = [&](int u, int &r0b, int &r1b) {
         if (kPair) {
             const int bb = u / bph, jb = u - bb * bph;
             r0b = bb * p.pair_block + jb * 16;
@@ -98,6 +98,18 @@ __global__ __launch_bounds__(64 * KS * (epi_is_pair(EPI) ? 2 : 1)) void k_gemm_m
             r0b = u * 16;
             r1b = r0b;
         }
+    };
+    // The weight tile in flight lives outside the unit loop, and a workgroup
+    // that takes several units (sampling products) requests its next unit's
+    // first tile before the current unit's reduction.  In this form the
+    // paired products compile to about 124 VGPRs, so two 8-wave workgroups
+    // share a CU (measured: 8B gate/up at 6 rows 47.1 -> 43.2 us against the
+    // loop-local form at 136 VGPRs, one workgroup per CU).
+    uint4 wv[NL];
+    bool have_first = false;   // wv already holds this unit's first tile
+    for (int u = blockIdx.x; u < p.n_units; u += gridDim.x) {
+        int r0b, r1b;
+        unit_blocks(u, r0b, r1b);
         const int sel = r0b / p.rows_per_sel;
         const int rb = blk ? r1b : r0b;         // this wave's block
         const uint16_t *W = reinterpret_cast<const uint16_t *>(p.W) + (int64_t)rb * K;
@@ -113,14 +125,15 @@ __global__ __launch_bounds__(64 * KS * (epi_is_pair(EPI) ? 2 : 1)) void k_gemm_m
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        uint4 wv[NL];
-        auto load = [&](int tt) {
+        auto load_from = [&](const uint16_t *Wr, int tt) {
             const int k = tt * kTK + lcol;
 #pragma unroll
             for (int i = 0; i < NL; ++i)
-                wv[i] = k < K ? ld16_stream(W + (int64_t)(2 * i + lrow) * K + k) : make_uint4(0, 0, 0, 0);
+                wv[i] = k < K ? ld16_stream(Wr + (int64_t)(2 * i + lrow) * K + k) : make_uint4(0, 0, 0, 0);
         };
-        if (t0 < t1) load(t0);
+        auto load = [&](int tt) { load_from(W, tt); };
+        if (t0 < t1 && !have_first) load(t0);
+        have_first = false;
         for (int tt = t0; tt < t1; ++tt) {
 #pragma unroll
             for (int i = 0; i < NL; ++i) *reinterpret_cast<uint4 *>(&tile[(2 * i + lrow) * kLD + lcol]) = wv[i];
@@ -144,6 +157,12 @@ __global__ __launch_bounds__(64 * KS * (epi_is_pair(EPI) ? 2 : 1)) void k_gemm_m
                                                                           0, 0, 0);
                 }
             }
+        }
+        if (u + (int)gridDim.x < p.n_units && t0 < t1) {
+            int n0, n1;
+            unit_blocks(u + gridDim.x, n0, n1);
+            load_from(reinterpret_cast<const uint16_t *>(p.W) + (int64_t)(blk ? n1 : n0) * K, t0);
+            have_first = true;
         }
         // fixed-order sum of the K parts of each block by wave 0; C layout:
         // lane l, register r holds C[4 * (l / 16) + r][l % 16] = (activation
@@ -252,6 +271,11 @@ int gemm_mfma_max_rows() { return 32; }
 
 // One unit per workgroup, except sampling products, which keep a fixed grid
 // (their arg-max partials are per workgroup).
+// One unit per workgroup (measured against one or two persistent workgroups
+// per CU that take several units each with the next unit's first tile
+// requested early: 8B gate/up at 6 rows 43.2 vs 45.0-45.4 us), except
+// sampling products, which keep a fixed grid (their arg-max partials are per
+// workgroup).
 int gemm_mfma_grid(const GemvParams &p) {
     const int n = p.n_units < 1 ? 1 : p.n_units;
     return p.epi == EPI_LOGITS && n > kLogitGrid ? kLogitGrid : n;

@@ -424,6 +424,12 @@ int gemv_grid(const GemvParams &p, int ks) {
     return g < cap ? (g < 1 ? 1 : g) : cap;
 }
 
+int gemv_operand_mode(int dtype, const GemvParams &p) {
+    if (p.xmode != X_NORM) return XM_PLAIN;
+    const bool st = dtype ? gemv_staged<uint16_t>(p) : gemv_staged<float>(p);
+    return st ? XM_STAGED : XM_DIRECT;
+}
+
 hipError_t launch_gemv(int dtype, const GemvParams &p, int grid, int ks, hipStream_t s) {
     if (ks != 1 && ks != 2 && ks != 4) return hipErrorInvalidValue;
     return dtype ? launch_t<uint16_t>(p, grid, ks, s) : launch_t<float>(p, grid, ks, s);

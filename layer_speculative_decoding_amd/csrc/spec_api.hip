@@ -95,10 +95,10 @@ struct ProfScope {
     }
 };
 
-std::string gemv_name(int dtype, int M, int epi) {
-    const int mr = M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : 8));
+std::string gemv_name(int dtype, const GemvParams &p) {
+    const int mr = p.M <= 1 ? 1 : (p.M <= 2 ? 2 : (p.M <= 4 ? 4 : 8));
     return std::string("k_gemv<") + (dtype ? "unsigned short" : "float") + ", " + std::to_string(mr) + ", " +
-           std::to_string(epi) + ">";
+           std::to_string(p.epi) + ", " + std::to_string(gemv_operand_mode(dtype, p)) + ">";
 }
 
 std::string mfma_name(int M, int epi, int ks) {
@@ -261,7 +261,7 @@ hipError_t product(const Fwd &f, GemvParams p, int *parts_out = nullptr) {
         p.M = (Mtot - m0) < mr ? (Mtot - m0) : mr;
         ProfScope ps(f.s);
         hipError_t e = launch_gemv(m->d.dtype, p, grid, ks, f.s);
-        ps.done(gemv_name(m->d.dtype, p.M, p.epi), wbytes + (double)p.M * p.K * (p.xmode == X_NORM ? 4 : m->xs),
+        ps.done(gemv_name(m->d.dtype, p), wbytes + (double)p.M * p.K * (p.xmode == X_NORM ? 4 : m->xs),
                 2.0 * p.M * rows * (double)p.K);
         if (e != hipSuccess) return e;
     }

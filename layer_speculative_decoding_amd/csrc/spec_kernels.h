@@ -103,6 +103,9 @@ hipError_t launch_gemv(int dtype, const GemvParams &p, int grid, int ks, hipStre
 int gemv_max_rows();
 int gemv_splits(const GemvParams &p, int elem_bytes);
 int gemv_grid(const GemvParams &p, int ks);
+// Operand mode of the GEMV instance a launch uses (0 plain rows, 1 normalised
+// rows staged in LDS, 2 normalised per step): the last template argument.
+int gemv_operand_mode(int dtype, const GemvParams &p);
 // MFMA skinny GEMM (bf16), M <= 32 per launch, K a multiple of 32.  Units:
 // pairs of 16-row blocks for the paired epilogues (QKV RoPE, SiLU; n_units =
 // rows / 32, pair_block a multiple of 32), single 16-row blocks otherwise
