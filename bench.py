@@ -258,6 +258,9 @@ def main():
     ap.add_argument("--no-vanilla", action="store_true")
     ap.add_argument("--group-size", type=int, default=0,
                     help="layer-parallel set size N of the default plan (0: the workload's own)")
+    ap.add_argument("--plan", default="",
+                    help="explicit layer-parallel plan as comma-separated stage offsets (0, ..., n_layers), "
+                         "for ablations of the plan reading; overrides --group-size")
     ap.add_argument("--no-calibration", action="store_true",
                     help="ablation: keep the fuzzy KV of accepted drafts, run only the emitted token precisely")
     ap.add_argument("--n1-compare", action="store_true",
@@ -325,6 +328,10 @@ def main():
     log(f"  weights ready in {time.time() - t0:.1f}s")
     N = args.group_size or cfg.group_size
     offs = api.spec_default_group_plan(cfg.draft.n_layers, N)
+    if args.plan:
+        offs = [int(x) for x in args.plan.split(",")]
+        if offs[0] != 0 or offs[-1] != cfg.draft.n_layers or any(b <= a for a, b in zip(offs, offs[1:])):
+            ap.error(f"--plan must be increasing stage offsets from 0 to {cfg.draft.n_layers}")
     seq_offs = list(range(cfg.draft.n_layers + 1))      # every layer its own stage (N = 1)
     P = cfg.prompt_len
     rounds_cap = W + K + 4
