@@ -261,6 +261,9 @@ def main():
     ap.add_argument("--plan", default="",
                     help="explicit layer-parallel plan as comma-separated stage offsets (0, ..., n_layers), "
                          "for ablations of the plan reading; overrides --group-size")
+    ap.add_argument("--separate-calibration", action="store_true",
+                    help="ablation: the other reading of the calibration (all k drafts from fuzzy steps, then a "
+                         "precise pass over the committed fuzzy tokens)")
     ap.add_argument("--no-calibration", action="store_true",
                     help="ablation: keep the fuzzy KV of accepted drafts, run only the emitted token precisely")
     ap.add_argument("--n1-compare", action="store_true",
@@ -339,7 +342,7 @@ def main():
     prompts = make_prompts(cfg.draft.vocab, P, cfg.batch, cfg.prompt_seed)
     inv_t = 0.0 if args.temperature == 0 else 1.0 / args.temperature
     dec = SpecDecoder(cfg.draft, dw, cfg.base, bw, cfg.batch, cap, k, offs, P, inv_t, cfg.sample_seed,
-                      calibrate=not args.no_calibration)
+                      calibrate=not args.no_calibration, separate=args.separate_calibration)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
     e0, e1 = ev(), ev()
@@ -403,7 +406,10 @@ def main():
     ms = {key: float(np.mean([a.elapsed_time(b) for a, b in v])) for key, v in ph.items()}
     acc_rate = (tokens - K * cfg.batch) / (K * cfg.batch * k)
     ctx = P + (W + K // 2) * (1 + acc_rate * k)
-    d_step_ms = ms["draft"] / max(k - 1, 1)
+    # draft steps per round: k-1 (the calibration yields d_1), k with the
+    # separate-pass calibration
+    n_dsteps = k if args.separate_calibration else max(k - 1, 1)
+    d_step_ms = ms["draft"] / n_dsteps
     d_bytes = draft_step_bytes(cfg.draft, ctx)
     v_bytes = verify_bytes(cfg.base, ctx)
     d_gbs = d_bytes / (d_step_ms * 1e-3) / 1e9
@@ -451,7 +457,7 @@ def main():
             dec.draft_phase()
             b_.record()
             torch.cuda.synchronize()
-            t_plan[key].append(a_.elapsed_time(b_) / max(k - 1, 1))
+            t_plan[key].append(a_.elapsed_time(b_) / n_dsteps)
     dec.plan = offs
     step_n, step_seq = float(np.median(t_plan["n"])), float(np.median(t_plan["seq"]))
     log(f"  draft step: plan {step_n * 1e3:.0f} us, sequential (N = 1) {step_seq * 1e3:.0f} us -> drafting "
@@ -509,7 +515,7 @@ def main():
     n1 = None
     if args.n1_compare:
         d1 = SpecDecoder(cfg.draft, dw, cfg.base, bw, cfg.batch, cap, k, seq_offs, P, inv_t, cfg.sample_seed,
-                         calibrate=not args.no_calibration)
+                         calibrate=not args.no_calibration, separate=args.separate_calibration)
         d1.prefill(prompts)
         for _ in range(W):
             d1.step(big)

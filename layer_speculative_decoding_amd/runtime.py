@@ -38,7 +38,8 @@ class RoundRecord:
 class SpecDecoder:
     def __init__(self, draft_shape, draft_w, base_shape, base_w, batch: int, capacity: int, k: int,
                  plan_offsets, prompt_len: int, inv_temp: float, seed: int,
-                 mlp_mode: int = SPEC_MLP_SEQUENTIAL, device="cuda", calibrate: bool = True):
+                 mlp_mode: int = SPEC_MLP_SEQUENTIAL, device="cuda", calibrate: bool = True,
+                 separate: bool = False):
         if k < 1:
             raise ValueError("k must be >= 1")
         self.dev = torch.device(device)
@@ -54,6 +55,13 @@ class SpecDecoder:
         # entries of accepted drafts stay, and only the emitted token's own
         # forward (which yields the next d_1) runs precisely
         self.calibrate = calibrate
+        # separate=True is the other reading of the calibration (ablation):
+        # all k drafts come from fuzzy steps starting at the pending token,
+        # and after the acceptance a precise pass rewrites the draft KV of
+        # [x_t, d_1..d_a] at t..t+a; the emitted token is the next pending one
+        self.separate = separate
+        if separate and not calibrate:
+            raise ValueError("separate calibration needs calibrate=True")
         self.inv_temp = float(np.float32(inv_temp))
         self.seed = int(seed)
         self.dkv = api.KVCache(draft_shape, batch, capacity, device)
@@ -70,6 +78,9 @@ class SpecDecoder:
         self.p_logits = torch.zeros(batch, k + 1, self.V, dtype=torch.float32, device=self.dev)
         self.n_acc = torch.zeros(batch, **i32)
         self.commit = torch.zeros(batch, k + 1, **i32)
+        self.xt = torch.zeros(batch, **i32)                    # pending token of the round
+        self.caltok = torch.zeros(batch, k + 1, **i32)         # [x_t, d_1..d_k] (separate calibration)
+        self.dummy_tok = torch.zeros(batch, **i32)
         # per-round integer table: [0:k] positions t+j for j = 0..k-1 ([B] each),
         # [k] calibration start t+1, [k+1] calibration count a+1
         self.tab = torch.zeros(k + 2, batch, **i32)
@@ -89,8 +100,14 @@ class SpecDecoder:
         if P > 1:
             pre = toks[:, :P - 1].contiguous()
             api.spec_verify_forward(self.base, self.bkv, B, pre, zero, P - 1, P - 2, None, self.ws)
-        api.spec_calibrate_kv(self.draft, self.dkv, B, toks, zero, None, P, P - 1, self.inv_temp, self.seed,
-                              self.q_logits[:, 0], self.k * self.V, self.vtok[:, 1], self.k + 1, self.ws)
+        if self.separate:
+            # the last prompt token is drafted from with a fuzzy step
+            if P > 1:
+                api.spec_calibrate_kv(self.draft, self.dkv, B, toks[:, :P - 1].contiguous(), zero, None, P - 1,
+                                      P - 2, self.inv_temp, self.seed, None, 0, self.dummy_tok, 1, self.ws)
+        else:
+            api.spec_calibrate_kv(self.draft, self.dkv, B, toks, zero, None, P, P - 1, self.inv_temp, self.seed,
+                                  self.q_logits[:, 0], self.k * self.V, self.vtok[:, 1], self.k + 1, self.ws)
         self.vtok[:, 0].copy_(toks[:, P - 1])
         self.t = [P - 1] * B
         self.out = [[] for _ in range(B)]
@@ -105,7 +122,7 @@ class SpecDecoder:
 
     def draft_phase(self):
         k, B = self.k, self.B
-        for j in range(1, k):
+        for j in range(0 if self.separate else 1, k):
             api.spec_draft_group_step(
                 self.draft, self.dkv, self.plan, self.mlp_mode, B, self.vtok[:, j], k + 1, self.tab[j],
                 max(self.t) + j, self.inv_temp, self.seed, self.q_logits[:, j], k * self.V,
@@ -138,6 +155,8 @@ class SpecDecoder:
         self.verify_phase()
         if marks:
             marks[2].record()
+        if self.separate:
+            self.xt.copy_(self.vtok[:, 0])
         if self.record:
             tok_before = self.vtok.to("cpu").numpy().copy()
             ql = self.q_logits.cpu().numpy().copy()
@@ -170,6 +189,8 @@ class SpecDecoder:
             if len(self.out[b]) >= new_tokens:
                 continue
             th[k + 1, b] = a[b] + 1
+            if self.separate:
+                th[k, b] = self.t[b]       # [x_t, d_1..d_a] at t..t+a
             self.t[b] += int(a[b]) + 1
             if not self.calibrate:
                 th[k, b] = self.t[b]
@@ -185,10 +206,17 @@ class SpecDecoder:
         rows = max(1, max(int(th[k + 1, b]) for b in range(B)))
         # without calibration the one row is the emitted token y, which the
         # accept step left in vtok[:, 0]
-        toks = self.commit if self.calibrate else self.vtok
-        api.spec_calibrate_kv(self.draft, self.dkv, B, toks, self.tab[k], self.tab[k + 1], rows,
-                              max(self.t), self.inv_temp, self.seed, self.q_logits[:, 0], k * self.V,
-                              self.vtok[:, 1], k + 1, self.ws, tokens_stride=k + 1)
+        if self.separate:
+            self.caltok[:, 0].copy_(self.xt)
+            self.caltok[:, 1:].copy_(self.vtok[:, 1:])
+            api.spec_calibrate_kv(self.draft, self.dkv, B, self.caltok, self.tab[k], self.tab[k + 1], rows,
+                                  max(self.t), self.inv_temp, self.seed, None, 0, self.dummy_tok, 1, self.ws,
+                                  tokens_stride=k + 1)
+        else:
+            toks = self.commit if self.calibrate else self.vtok
+            api.spec_calibrate_kv(self.draft, self.dkv, B, toks, self.tab[k], self.tab[k + 1], rows,
+                                  max(self.t), self.inv_temp, self.seed, self.q_logits[:, 0], k * self.V,
+                                  self.vtok[:, 1], k + 1, self.ws, tokens_stride=k + 1)
         if marks:
             marks[4].record()
         return True

@@ -14,6 +14,13 @@ Readings adopted where the pages are silent:
     gives q_1 and d_1 of the next round, so a round has k-1 fuzzy steps;
   * exactly `new_tokens` tokens are produced; the last round is truncated.
 
+separate=True is the other reading of what calibration covers (an ablation):
+the draft prefills prompt[0:P-1] like the base, every round drafts all k
+tokens with fuzzy steps starting from the pending token x_t, and after the
+acceptance a separate precise pass rewrites the draft KV of the tokens that
+were drafted fuzzily and committed, [x_t, d_1..d_a] at positions t..t+a; the
+emitted token y is the next round's pending token.
+
 A `hook(kind, key, value, margin)` may replace any decision (kinds 'draft',
 'accept', 'y'); lock-step parity tests use it to adopt the GPU's choice where
 the oracle's decision margin is below the exclusion threshold.
@@ -37,7 +44,7 @@ def spec_generate(draft: OracleModel, base: OracleModel, prompt, k: int, sets,
                   new_tokens: int, inv_temp: float, seed: int, b: int = 0,
                   capacity: Optional[int] = None, mlp_mode: int = MLP_SEQUENTIAL,
                   calibrate: bool = True, hook: Optional[Callable] = None,
-                  ftype=np.float64, caches=None):
+                  ftype=np.float64, caches=None, separate: bool = False):
     """Speculative decoding of one sequence.  Returns (tokens, rounds) where
     rounds is a list of dicts (t, drafts, a, y, q_logits, p_logits)."""
     hook = hook or _id_hook
@@ -51,13 +58,21 @@ def spec_generate(draft: OracleModel, base: OracleModel, prompt, k: int, sets,
         dkv, bkv = caches
     if P > 1:
         forward(base, bkv, b, prompt[:-1], range(P - 1), logits=None)
-    zq = forward(draft, dkv, b, prompt, range(P), logits="last")
+    if separate:
+        if P > 1:
+            forward(draft, dkv, b, prompt[:-1], range(P - 1), logits=None)
+        zq = None
+    else:
+        zq = forward(draft, dkv, b, prompt, range(P), logits="last")
     t = P - 1
     seq = list(prompt)
     rounds = []
     r = 0
     while len(seq) - P < new_tokens:
         drafts: List[int] = []
+        xt = seq[-1]
+        if separate:
+            zq = fuzzy_step(draft, dkv, b, xt, t, sets, mlp_mode)
         qlog = [zq]
         d, mg = sample_from_logits(zq, inv_temp, seed, b, t + 1, philox.DRAFT)
         drafts.append(hook("draft", (r, 1), d, mg))
@@ -66,7 +81,7 @@ def spec_generate(draft: OracleModel, base: OracleModel, prompt, k: int, sets,
             qlog.append(z)
             d, mg = sample_from_logits(z, inv_temp, seed, b, t + j + 1, philox.DRAFT)
             drafts.append(hook("draft", (r, j + 1), d, mg))
-        plog = forward(base, bkv, b, [seq[-1]] + drafts, range(t, t + k + 1), logits="all")
+        plog = forward(base, bkv, b, [xt] + drafts, range(t, t + k + 1), logits="all")
         a_or, y, info = accept_resample(plog, np.stack(qlog), drafts, t, inv_temp, seed, b)
         acc_m = [m for (kind, _, m) in info["margins"] if kind in ("accept", "argmax")]
         a = hook("accept", (r,), a_or, min(acc_m) if acc_m else np.inf)
@@ -81,7 +96,9 @@ def spec_generate(draft: OracleModel, base: OracleModel, prompt, k: int, sets,
         seq += emitted[:room]
         if len(seq) - P >= new_tokens:
             break
-        if calibrate:
+        if separate:
+            forward(draft, dkv, b, [xt] + drafts[:a], range(t, t + a + 1), logits=None)
+        elif calibrate:
             zq = forward(draft, dkv, b, emitted, range(t + 1, t + a + 2), logits="last")
         else:   # ablation: keep fuzzy KV, run only the emitted token precisely
             zq = forward(draft, dkv, b, [y], [t + a + 1], logits="last")

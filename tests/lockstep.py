@@ -17,7 +17,8 @@ from oracle.decode import spec_generate
 from gpu_common import MARGIN
 
 
-def lockstep(dec, om_draft, om_base, prompts, k, sets, new_tokens, inv_temp, seed, mlp_mode, tol, calibrate=True):
+def lockstep(dec, om_draft, om_base, prompts, k, sets, new_tokens, inv_temp, seed, mlp_mode, tol, calibrate=True,
+             separate=False):
     B = prompts.shape[0]
     dec.record = True
     dec.records = []
@@ -40,7 +41,8 @@ def lockstep(dec, om_draft, om_base, prompts, k, sets, new_tokens, inv_temp, see
             return g
 
         toks, rounds = spec_generate(om_draft, om_base, prompts[b], k, sets, new_tokens, inv_temp, seed, b=b,
-                                     capacity=dec.cap, mlp_mode=mlp_mode, calibrate=calibrate, hook=hook)
+                                     capacity=dec.cap, mlp_mode=mlp_mode, calibrate=calibrate, hook=hook,
+                                     separate=separate)
         assert toks == gpu_out[b], (b, toks[:20], gpu_out[b][:20])
         dz = []
         for r, rd in enumerate(rounds):

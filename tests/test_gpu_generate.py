@@ -96,6 +96,29 @@ def test_no_calibration_ablation_lockstep(dtype, inv_temp):
 
 
 @pytest.mark.parametrize("dtype", [0, BF16])
+@pytest.mark.parametrize("inv_temp", [0.0, 1.0])
+def test_separate_calibration_lockstep(dtype, inv_temp):
+    """The separate-pass reading of the calibration: all k drafts from fuzzy
+    steps, then a precise pass over [x_t, d_1..d_a] at t..t+a; GPU and
+    oracle run the same loop in lock step."""
+    from layer_speculative_decoding_amd.runtime import SpecDecoder
+    sh, dw, bw = _near_copy_pair(dtype)
+    say(f"separate-calibration lockstep dtype={dtype} invT={inv_temp}")
+    sets = default_group_plan(sh.n_layers, 2)
+    B, P, k, new = 3, 12, 4, 24
+    prompts = make_prompts(sh.vocab, P, B, lambda b: 133 + b)
+    dec = SpecDecoder(sh, to_dev(dw), sh, to_dev(bw), B, P + new + k + 2, k, plan_offsets(sets), P, inv_temp,
+                      616, MLP_SEQUENTIAL, separate=True)
+    tol = TOL_F32 if dtype == 0 else TOL_BF16
+    st = lockstep(dec, OracleModel.from_torch(sh, dw), OracleModel.from_torch(sh, bw), prompts, k, sets, new,
+                  dec.inv_temp, 616, MLP_SEQUENTIAL, tol, separate=True)
+    acc = sum(int(a) for r in dec.records for a in r.n_acc)
+    say(f"  checked {st['checked']} excluded {st['excluded']} max rel err {st['err']:.2e}; accepted {acc}")
+    assert acc > 0
+    assert st["excluded"] <= max(3, st["checked"] // 3)
+
+
+@pytest.mark.parametrize("dtype", [0, BF16])
 def test_greedy_speculative_equals_vanilla_on_gpu(dtype):
     """Lossless greedy decoding on the GPU.  float32: identical outputs.  bf16:
     verification (k+1 rows, matrix-core kernel) and vanilla decoding (one row)

@@ -128,6 +128,46 @@ def test_greedy_speculative_equals_vanilla(k, N):
     assert sum(r["a"] for r in rounds) > 0
 
 
+@pytest.mark.parametrize("k,N", [(1, 2), (3, 2), (4, 3), (5, 4)])
+def test_greedy_speculative_equals_vanilla_separate_calibration(k, N):
+    """The separate-pass reading of the calibration (all k drafts from fuzzy
+    steps, the committed fuzzy tokens rewritten afterwards) changes only the
+    drafts, so greedy output is still the base's greedy output."""
+    ds, dw, bs, bw = tiny_pair(V=24, base_layers=5, draft_noise=0.01)
+    d, b = OracleModel.from_torch(ds, dw), OracleModel.from_torch(bs, bw)
+    prompt = [2, 7, 1, 8, 2, 8]
+    sets = default_group_plan(5, N)
+    spec, rounds = spec_generate(d, b, prompt, k, sets, 20, 0.0, 0, separate=True)
+    assert spec == vanilla_generate(b, prompt, 20, 0.0, 0)
+    assert sum(r["a"] for r in rounds) > 0
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_separate_calibration_restores_precise_kv(dtype):
+    """Separate-pass reading: the draft prefills P-1 tokens, and each
+    calibration rewrites [x_t, d_1..d_a] at t..t+a, so after the last one the
+    draft KV up to the pending position equals a sequential prefill."""
+    ds, dw, bs, bw = tiny_pair(V=32, dtype=dtype, draft_layers=5, draft_noise=None)
+    d, b = OracleModel.from_torch(ds, dw), OracleModel.from_torch(bs, bw)
+    prompt = [3, 1, 4, 1, 5, 9]
+    sets = default_group_plan(5, 3)
+    cap = 64
+    dkv, bkv = KVCache(ds, 1, cap), KVCache(bs, 1, cap)
+    toks, rounds = spec_generate(d, b, prompt, 3, sets, 12, 1.0, 5, caches=(dkv, bkv), capacity=cap,
+                                 separate=True)
+    assert len(rounds) > 1
+    seq = prompt + toks
+    last_cal = len(prompt) - 1 + sum(r["a"] + 1 for r in rounds[:-1])
+    assert last_cal == rounds[-1]["t"]
+    ref = _prefill_model(d, seq[:last_cal], cap)
+    np.testing.assert_allclose(dkv.k[:, :, :, :last_cal], ref.k[:, :, :, :last_cal], rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(dkv.v[:, :, :, :last_cal], ref.v[:, :, :, :last_cal], rtol=1e-9, atol=1e-12)
+    # the pending token's own entry is fuzzy (a set member's attention input
+    # is the set's input, not the running state): it differs from the prefill
+    ref2 = _prefill_model(d, seq[:last_cal + 1], cap)
+    assert not np.allclose(dkv.k[:, :, :, last_cal], ref2.k[:, :, :, last_cal], rtol=1e-6, atol=1e-9)
+
+
 @pytest.mark.parametrize("inv_temp", [0.0, 1.0])
 def test_self_draft_accepts_everything(inv_temp):
     """Draft identical to the base and a sequential plan: p = q at every step, so
