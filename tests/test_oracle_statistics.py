@@ -6,12 +6,14 @@ import numpy as np
 import pytest
 from scipy import stats
 
+from oracle import model as oracle_model
 from oracle import philox, sampling
 from oracle.decode import spec_generate
 from oracle.model import KVCache, OracleModel, forward
 from oracle.plan import default_group_plan
 from oracle.sampling import accept_law, accept_resample, accept_resample_batch, sample_from_logits, softmax
 from helpers import tiny_pair
+from synth import make_weights, tiny_shape
 
 P_MIN = 1e-4      # reject the null below this p-value
 
@@ -123,3 +125,65 @@ def test_round_loop_preserves_base_joint_law():
         acc += rounds[0]["a"]
     assert 0.2 * n < acc < 1.8 * n          # both accept and reject paths are exercised
     assert _chi2_p(counts.ravel(), joint.ravel()) > P_MIN
+
+
+def _expected_overlap(V, sd_p, sd_q, n, seed):
+    """E[sum_v min(p_v, q_v)] for p = softmax(z_p), q = softmax(z_q) with
+    independent logit vectors of i.i.d. N(0, sd^2) entries (Monte Carlo)."""
+    rng = np.random.default_rng(seed)
+    tot = 0.0
+    for _ in range(n // 2000):
+        zp = rng.normal(size=(2000, V)) * sd_p
+        zq = rng.normal(size=(2000, V)) * sd_q
+        p = np.exp(zp - zp.max(1, keepdims=True))
+        q = np.exp(zq - zq.max(1, keepdims=True))
+        tot += np.minimum(p / p.sum(1, keepdims=True), q / q.sum(1, keepdims=True)).sum()
+    return tot / n
+
+
+def _observed_acceptance(inv_temp, sw, V, dq, dp, k, n_pairs=6, new_tokens=120):
+    """Per-draft acceptance of the round loop on independent random-init
+    pairs: accepted drafts / tested drafts (a round tests min(a + 1, k))."""
+    acc = tested = 0
+    for s in range(n_pairs):
+        ds = tiny_shape(4, dq, 4, 2, 8, 64, V)
+        bs = tiny_shape(3, dp, 4, 2, 16, 128, V)
+        d = OracleModel.from_torch(ds, make_weights(ds, 50 + 2 * s, std=sw))
+        b = OracleModel.from_torch(bs, make_weights(bs, 51 + 2 * s, std=sw))
+        prompt = np.random.default_rng(s).integers(0, V, size=8).tolist()
+        _, rounds = spec_generate(d, b, prompt, k, default_group_plan(4, 2), new_tokens, inv_temp, 900 + s)
+        for r in rounds:
+            acc += r["a"]
+            tested += min(r["a"] + 1, len(r["drafts"]))
+    return acc / tested, tested
+
+
+def _check_random_init_acceptance(T):
+    V, sw, k, dq, dp = 256, 0.15, 4, 32, 64
+    # unit gains: the final RMSNorm leaves a hidden state of squared norm d,
+    # so with an independent N(0, sw^2) lm head the logits are i.i.d.
+    # N(0, sw^2 d) given the state, independently for draft and base
+    alpha = _expected_overlap(V, sw * np.sqrt(dp) / T, sw * np.sqrt(dq) / T, 40_000, 1)
+    obs, n = _observed_acceptance(1.0 / T, sw, V, dq, dp, k)
+    return alpha, obs, n
+
+
+@pytest.mark.parametrize("T", [1.0, 0.7])
+def test_random_init_acceptance_matches_closed_form(T):
+    """Acceptance on random-init pairs is fixed by the weights' law: a draft
+    d ~ q is accepted with probability sum_v min(p_v, q_v) (the accept rule
+    the pages cite), whose expectation over i.i.d. Gaussian logits is
+    computable.  The layer-parallel draft changes q's hidden state, not its
+    law, so the same value holds for any plan."""
+    alpha, obs, n = _check_random_init_acceptance(T)
+    se = np.sqrt(alpha * (1 - alpha) / n)
+    assert abs(obs - alpha) < 4 * se + 0.02, (alpha, obs, n)
+
+
+def test_random_init_acceptance_detects_a_planted_mistake(monkeypatch):
+    """Power check: a head that skips the final RMSNorm (logit scale no
+    longer sw * sqrt(d)) must fail the same comparison."""
+    monkeypatch.setattr(oracle_model, "final_logits", lambda m, h: oracle_model.linear(h, m.w["lm_head"]))
+    alpha, obs, n = _check_random_init_acceptance(1.0)
+    se = np.sqrt(alpha * (1 - alpha) / n)
+    assert abs(obs - alpha) > 4 * se + 0.02, (alpha, obs, n)
