@@ -314,3 +314,76 @@ def test_attention_input_cosine_matches_oracle(name):
             assert err < (1e-5 if tol == TOL_F32 else 1e-2)
             for s in sets:                              # the first member reads exactly h0
                 assert abs(cg[b, s[0]] - 1.0) < 1e-5
+
+
+@pytest.mark.parametrize("name", ["gqa-bias-f32", "hd64-bias-bf16", "hd128-bf16"])
+def test_kv_filled_to_capacity(name):
+    """Every forward entry point at the last KV slot: a verify whose rows of
+    sequence 0 end at position capacity - 1 (several key splits, the last
+    one ragged: the capacity, 301, is no multiple of a key block or chunk),
+    a layer-parallel draft step at that position, and a ragged calibration
+    ending there.  The oracle takes the same calls, so the whole KV cache is
+    compared at the end."""
+    from layer_speculative_decoding_amd import api
+    B, m, cap = 2, 6, 301
+    P = cap - m
+    shape, tol, om, gm, gkv, okv, prompts = _setup(name, B, cap + 1, cap=cap)
+    sets = PLANS[name][0]
+    offs = plan_offsets(sets)
+    G = max(len(s) for s in sets)
+    say(f"capacity edge {name} cap={cap} plan={offs}")
+    w = ws(max(api.spec_workspace_bytes(gm, B, P, 1), api.spec_workspace_bytes(gm, B, 1, G)))
+
+    api.spec_verify_forward(gm, gkv, B, i32(prompts[:, :P]), i32([0] * B), P, P - 1, None, w)
+    for b in range(B):
+        forward(om, okv, b, prompts[b, :P], range(P), logits=None)
+
+    # verify: rows P .. cap - 1 (sequence 0) and P - 2 .. cap - 3 (sequence 1)
+    vt = prompts[:, P:P + m].copy()
+    st = np.array([P, P - 2], dtype=np.int32)
+    logits = torch.zeros(B, m, shape.vocab, device="cuda")
+    api.spec_verify_forward(gm, gkv, B, i32(vt), i32(st), m, cap - 1, logits, w)
+    torch.cuda.synchronize()
+    zg = logits.cpu().numpy()
+    for b in range(B):
+        zo = forward(om, okv, b, vt[b], range(st[b], st[b] + m), logits="all")
+        err = rel_linf(zg[b], zo)
+        say(f"  verify b={b} start {st[b]} logits rel {err:.2e}")
+        assert err < tol
+
+    # draft step writing fuzzy K/V at the last slot of both sequences
+    cur = prompts[:, cap].copy()
+    pos = np.array([cap - 1, cap - 1], dtype=np.int32)
+    dl = torch.zeros(B, shape.vocab, device="cuda")
+    out = torch.zeros(B, dtype=torch.int32, device="cuda")
+    api.spec_draft_group_step(gm, gkv, offs, MLP_SEQUENTIAL, B, i32(cur), 1, i32(pos), cap - 1, 1.0, 77,
+                              dl, shape.vocab, out, 1, w)
+    torch.cuda.synchronize()
+    zg, tg = dl.cpu().numpy(), out.cpu().numpy()
+    for b in range(B):
+        zo = fuzzy_step(om, okv, b, int(cur[b]), int(pos[b]), sets, MLP_SEQUENTIAL)
+        err = rel_linf(zg[b], zo)
+        say(f"  draft step b={b} logits rel {err:.2e}")
+        assert err < tol
+        t_or, mg = sample_from_logits(zo, 1.0, 77, b, int(pos[b]) + 1, philox.DRAFT)
+        if mg >= exclusion(zg[b], zo, 1.0):
+            assert tg[b] == t_or
+
+    # ragged calibration: sequence 0 rewrites the last m slots, sequence 1
+    # m - 2 slots ending two before the last
+    ct = prompts[:, P - 1:P - 1 + m].copy()
+    cs = np.array([cap - m, cap - m - 2], dtype=np.int32)
+    cn = np.array([m, m - 2], dtype=np.int32)
+    ll = torch.zeros(B, shape.vocab, device="cuda")
+    tok = torch.zeros(B, dtype=torch.int32, device="cuda")
+    api.spec_calibrate_kv(gm, gkv, B, i32(ct), i32(cs), i32(cn), m, cap - 1, 0.0, 0, ll, shape.vocab, tok, 1, w)
+    torch.cuda.synchronize()
+    zg = ll.cpu().numpy()
+    for b in range(B):
+        zo = forward(om, okv, b, ct[b, :cn[b]], range(cs[b], cs[b] + cn[b]), logits="last")
+        err = rel_linf(zg[b], zo)
+        say(f"  calibrate b={b} rows {cs[b]}..{cs[b] + cn[b] - 1} last logits rel {err:.2e}")
+        assert err < tol
+    ek, ev = _kv_rel(gkv, okv, cap)
+    say(f"  KV rel over all {cap} slots: k {ek:.2e} v {ev:.2e}")
+    assert ek < tol and ev < tol
