@@ -87,6 +87,7 @@ CASES = [
     ("llama-1b-8b", "draft", 512, 1, None),
     ("llama-1b-8b", "base", 512, 1, None),
     ("llama-1b-8b-n4", "draft", 2048, 1, None),
+    ("llama-1b-8b-n4", "base", 2048, 1, None),
     ("qwen-0.5b-7b", "draft", 1024, 1, None),
     ("qwen-0.5b-7b", "base", 1024, 1, None),
     ("llama-8b-70b", "draft", 8192, 4, 8),
@@ -182,6 +183,8 @@ PREFILL_CASES = [
     # (config, which model, prompt rows per sequence, batch, layers of the model to keep)
     ("llama-1b-8b", "draft", 512, 1, None),
     ("llama-1b-8b", "base", 511, 1, None),
+    ("llama-1b-8b-n4", "draft", 2048, 1, None),
+    ("llama-1b-8b-n4", "base", 2047, 1, 8),
     ("qwen-0.5b-7b", "draft", 1024, 1, None),
     ("qwen-0.5b-7b", "base", 1023, 1, 8),
     ("llama-8b-70b", "base", 256, 4, 2),
@@ -254,7 +257,7 @@ def test_fullsize_prompt_prefill(cfg_name, which, P, batch, layers):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("cfg_name", ["llama-1b-8b", "qwen-0.5b-7b", "llama-8b-70b"])
+@pytest.mark.parametrize("cfg_name", ["llama-1b-8b", "llama-1b-8b-n4", "qwen-0.5b-7b", "llama-8b-70b"])
 def test_fullsize_accept_resample(cfg_name):
     """accept / resample at the workload's vocabulary, batch and k, on logits
     whose draft and base rows are close (so both branches occur)."""
