@@ -87,7 +87,7 @@ CASES = [
     ("llama-1b-8b", "draft", 512, 1, None),
     ("llama-1b-8b", "base", 512, 1, None),
     ("llama-1b-8b-n4", "draft", 2048, 1, None),
-    ("llama-1b-8b-n4", "base", 2048, 1, None),
+    ("llama-1b-8b-n4", "base", 2048, 1, 8),
     ("qwen-0.5b-7b", "draft", 1024, 1, None),
     ("qwen-0.5b-7b", "base", 1024, 1, None),
     ("llama-8b-70b", "draft", 8192, 4, 8),
