@@ -115,7 +115,7 @@ def test_round_loop_preserves_base_joint_law():
         c2 = KVCache(bs, 1, 16)
         z2 = forward(b, c2, 0, prompt + [x1], range(4), logits="last")
         joint[x1] = p1[x1] * softmax(z2)
-    sets = default_group_plan(3, 2)
+    sets = [[0], [1, 2]]      # a real layer-parallel set (default grouping of 3 layers: singletons)
     n = 2500
     counts = np.zeros((V, V), dtype=np.int64)
     acc = 0
@@ -187,3 +187,109 @@ def test_random_init_acceptance_detects_a_planted_mistake(monkeypatch):
     alpha, obs, n = _check_random_init_acceptance(1.0)
     se = np.sqrt(alpha * (1 - alpha) / n)
     assert abs(obs - alpha) > 4 * se + 0.02, (alpha, obs, n)
+
+
+# a 4-layer draft plan with a real layer-parallel set (the default grouping of
+# 4 layers in sets of 2 has only singletons: layers 1 and 2 fall in different
+# aligned pairs)
+FUZZY4 = [[0], [1, 2], [3]]
+
+
+def _round_law(d, b, prompt, k, sets, inv_t, separate):
+    """Exact law of the tokens one round emits, E = (d_1..d_a, y), over every
+    draft path: spec_generate runs the round with the drafts forced through its
+    hook and returns the draft and base distributions it computed for that
+    path; the accept rule composes them (accept d_j with probability
+    min(1, p_j(d_j) / q_j(d_j)), at the first rejection y ~ max(0, p_j - q_j)
+    normalised, after k acceptances y ~ p_{k+1})."""
+    import itertools
+    V = b.shape.vocab
+    law = {}
+    for path in itertools.product(range(V), repeat=k):
+        hook = lambda kind, key, value, margin: path[key[1] - 1] if kind == "draft" else value
+        _, rounds = spec_generate(d, b, prompt, k, sets, 1, inv_t, 5, hook=hook, separate=separate)
+        q = [softmax(z * inv_t) for z in rounds[0]["q_logits"]]
+        p = [softmax(z * inv_t) for z in rounds[0]["p_logits"]]
+        w = np.prod([q[j][path[j]] for j in range(k)])          # probability of drafting this path
+        for a in range(k + 1):
+            acc = np.prod([min(1.0, p[j][path[j]] / q[j][path[j]]) for j in range(a)])
+            if a < k:
+                stop = 1.0 - min(1.0, p[a][path[a]] / q[a][path[a]])
+                res = np.maximum(p[a] - q[a], 0.0)
+                ylaw = res / res.sum() if res.sum() > 0 else p[a]
+            else:
+                stop, ylaw = 1.0, p[k]
+            for y in range(V):
+                e = tuple(path[:a]) + (y,)
+                law[e] = law.get(e, 0.0) + w * acc * stop * ylaw[y]
+    return law
+
+
+@pytest.mark.parametrize("separate", [False, True])
+@pytest.mark.parametrize("inv_t", [1.0, 1.0 / 0.7])
+def test_round_law_exact_enumeration(separate, inv_t):
+    """Losslessness of one round, exactly: the first k + 1 tokens, with the
+    round's emitted tokens completed by the base's own law where the round
+    stops early, follow the base model's autoregressive joint law (float64,
+    every draft path enumerated).  The rule is lossless for any draft
+    distribution, so this pins the round itself: which draft and base
+    distributions meet in each decision, at which positions, across the
+    prompt seam and both readings of the calibration pass."""
+    import itertools
+    V, k = 4, 3
+    ds, dw, bs, bw = tiny_pair(V=V, draft_layers=4, base_layers=3, d=16, hq=2, hkv=1, hd=8, ffn=32)
+    d, b = OracleModel.from_torch(ds, dw), OracleModel.from_torch(bs, bw)
+    prompt = [1, 3, 0, 2]
+    law = _round_law(d, b, prompt, k, FUZZY4, inv_t, separate)
+    assert abs(sum(law.values()) - 1.0) < 1e-12
+
+    cond = {}      # base law of the next token after prompt + prefix, by separate precise forwards
+
+    def base_next(prefix):
+        if prefix not in cond:
+            seq = prompt + list(prefix)
+            z = forward(b, KVCache(bs, 1, 16), 0, seq, range(len(seq)), logits="last")
+            cond[prefix] = softmax(z * inv_t)
+        return cond[prefix]
+
+    worst = 0.0
+    for s in itertools.product(range(V), repeat=k + 1):
+        target = np.prod([base_next(s[:i])[s[i]] for i in range(k + 1)])
+        got = 0.0
+        for i in range(1, k + 2):
+            pe = law.get(s[:i], 0.0)
+            if pe:
+                got += pe * np.prod([base_next(s[:j])[s[j]] for j in range(i, k + 1)])
+        worst = max(worst, abs(got - target))
+    assert worst < 1e-12, worst
+
+
+def test_round_law_detects_a_planted_mistake(monkeypatch):
+    """Power check: a verify pass that places the drafts one position late
+    (an off-by-one in the round's positions) breaks the exact equality."""
+    import itertools
+    import oracle.decode as odec
+    real = odec.forward
+
+    def shifted(m, kv, bb, toks, pos, logits="all"):
+        if logits == "all" and m is base_model[0]:
+            pos = [p + 1 for p in pos]
+        return real(m, kv, bb, toks, pos, logits=logits)
+    base_model = [None]
+    monkeypatch.setattr(odec, "forward", shifted)
+    V, k = 4, 2
+    ds, dw, bs, bw = tiny_pair(V=V, draft_layers=4, base_layers=3, d=16, hq=2, hkv=1, hd=8, ffn=32)
+    d, b = OracleModel.from_torch(ds, dw), OracleModel.from_torch(bs, bw)
+    base_model[0] = b
+    prompt = [1, 3, 0, 2]
+    law = _round_law(d, b, prompt, k, FUZZY4, 1.0, False)
+    worst = 0.0
+    for s in itertools.product(range(V), repeat=k + 1):
+        pn = []
+        for i in range(k + 1):
+            seq = prompt + list(s[:i])
+            pn.append(softmax(forward(b, KVCache(bs, 1, 16), 0, seq, range(len(seq)), logits="last")))
+        target = np.prod([pn[i][s[i]] for i in range(k + 1)])
+        got = sum(law.get(s[:i], 0.0) * np.prod([pn[j][s[j]] for j in range(i, k + 1)]) for i in range(1, k + 2))
+        worst = max(worst, abs(got - target))
+    assert worst > 1e-6, worst
