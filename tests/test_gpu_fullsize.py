@@ -183,8 +183,8 @@ PREFILL_CASES = [
     # (config, which model, prompt rows per sequence, batch, layers of the model to keep)
     ("llama-1b-8b", "draft", 512, 1, None),
     ("llama-1b-8b", "base", 511, 1, None),
-    ("llama-1b-8b-n4", "draft", 2048, 1, None),
-    ("llama-1b-8b-n4", "base", 2047, 1, 8),
+    ("llama-1b-8b-n4", "draft", 2048, 1, 4),
+    ("llama-1b-8b-n4", "base", 2047, 1, 2),
     ("qwen-0.5b-7b", "draft", 1024, 1, None),
     ("qwen-0.5b-7b", "base", 1023, 1, 8),
     ("llama-8b-70b", "base", 256, 4, 2),
