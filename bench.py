@@ -162,11 +162,16 @@ def pmc_mfma_summary(csv_path, command):
               f"{f32:.2f} | {busy:.1%} |")
 
 
-def rocprof_summary(stats_csv, trace_csv, command):
-    """Markdown summary of a `rocprofv3 --kernel-trace --stats` run of the
-    default workload: the per-kernel statistics, then the kernels of one
-    steady-state round split into its phases (a round runs calibration, the
-    draft steps, verify, accept; every calibration and draft step ends with
+def profile_name(cfg):
+    """File name of a workload's kernel-statistics summary under profiles/."""
+    return f"kernel_stats_{cfg.name}_k{cfg.k}_N{cfg.group_size}" + (f"_B{cfg.batch}" if cfg.batch > 1 else "") + ".md"
+
+
+def rocprof_summary(stats_csv, trace_csv, command, cfg):
+    """Markdown summary of a `rocprofv3 --kernel-trace --stats` run of a
+    workload: the per-kernel statistics, then the kernels of one steady-state
+    round split into its phases (a round runs calibration, the draft steps,
+    verify, accept; every calibration and draft step ends with
     k_sample_reduce, accept starts with k_acc_stats)."""
     import collections
     import csv
@@ -176,12 +181,18 @@ def rocprof_summary(stats_csv, trace_csv, command):
         return n.split("(spec::")[0].split("(float const")[0][:70]
 
     rows = list(csv.DictReader(open(stats_csv)))
-    print("# rocprofv3 kernel statistics: llama-1b-8b workload (bench.py default)")
+    def shape(sh):
+        return (f"{sh.n_layers}-layer d{sh.d_model} ({sh.n_q_heads} q / {sh.n_kv_heads} kv heads of {sh.head_dim}, "
+                f"ffn {sh.d_ffn}{', QKV bias' if sh.qkv_bias else ''})")
+
+    print(f"# rocprofv3 kernel statistics: {cfg.name} workload")
     print()
-    print("Workload: Llama-3.2-1B-shaped draft -> Llama-3-8B-shaped base, bf16, vocab 128256, 512-token prompt, "
-          "k = 5, layer-parallel set size N = 2, batch 1, greedy; three prompt prefills (k_gemm_tile: base 511 "
-          "rows, draft 512 rows), 2 warm-up + 10 timed + 5 instrumented rounds, and the weight generation "
-          "(the at::native kernels).  Template arguments: k_gemm_mfma<row tiles, epilogue, waves per block>, "
+    print(f"Workload: draft {shape(cfg.draft)} -> base {shape(cfg.base)}, "
+          f"{'bf16' if cfg.base.dtype == 1 else 'float32'}, vocab {cfg.base.vocab}, {cfg.prompt_len}-token prompt, "
+          f"k = {cfg.k}, layer-parallel set size N = {cfg.group_size}, batch {cfg.batch}, greedy; the prompt "
+          "prefills (k_gemm_tile), the warm-up, timed and instrumented rounds of the command below, and the "
+          "weight generation (the at::native kernels).  Template arguments: k_gemm_mfma<row tiles, epilogue, "
+          "waves per block>, "
           "k_gemv<type, rows, epilogue, operand mode>, k_gemm_tile<epilogue, 32-row weight blocks, K split>; "
           "epilogues 0 store, 1 QKV RoPE + KV append, 2 SiLU gate, 3 residual add, 4 logits + arg-max, "
           "5 attention-output routing.")
@@ -206,8 +217,10 @@ def rocprof_summary(stats_csv, trace_csv, command):
     idx = [i for i, r in enumerate(ks) if r[0] == "k_acc_stats"]
     seg = ks[idx[-2]:idx[-1]]
     sr = [i for i, r in enumerate(seg) if r[0] == "k_sample_reduce"]
-    phases = {"calibration (a + 1 rows: 1 at acceptance 0)": seg[3:sr[0] + 1],
-              "one draft step (1 row)": seg[sr[0] + 1:sr[1] + 1], "verify (k + 1 = 6 rows)": seg[sr[-1] + 1:]}
+    per = f" per sequence, {cfg.batch} sequences" if cfg.batch > 1 else ""
+    phases = {f"calibration (a + 1 rows{per}: 1 at acceptance 0)": seg[3:sr[0] + 1],
+              f"one draft step (1 row{per})": seg[sr[0] + 1:sr[1] + 1],
+              f"verify (k + 1 = {cfg.k + 1} rows{per})": seg[sr[-1] + 1:]}
     print()
     print("One steady-state round from run_kernel_trace.csv (the last instrumented round; busy = sum of kernel "
           "durations, which excludes the profiler's own dispatch gaps):")
@@ -277,15 +290,25 @@ def main():
                     help="print the matrix-core utilisation summary of a counter run of --pmc-probe")
     ap.add_argument("--rocprof-summary", nargs=2, metavar=("STATS_CSV", "TRACE_CSV"),
                     help="print the kernel statistics and one round's phases of a kernel-trace run")
+    ap.add_argument("--rocprof-timeout", type=int, default=300,
+                    help="the time limit of the summarised profiler run, as quoted in the summary")
     args = ap.parse_args()
     # the profiler's output directory of a summarised run: where its CSV is
     odir = lambda path: os.path.dirname(path) or "."
     if args.rocprof_summary:
+        # describes the profiled run: the same --config / --steps / --warmup
+        from synth import get_config as _cfg
         st, tr = args.rocprof_summary
+        cfg = _cfg(args.config)
+        run = (f"--config {args.config} " if args.config != "llama-1b-8b" else "") + \
+            f"--steps {args.steps} --warmup {args.warmup}"
         rocprof_summary(st, tr, [
-            f"timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d {odir(st)} -o run "
-            "-- python bench.py --steps 10 --warmup 2 --no-cpu-baseline --no-vanilla",
-            f"python bench.py --rocprof-summary {st} {tr} > profiles/kernel_stats_llama-1b-8b_k5_N2.md"])
+            f"timeout -k 10 {args.rocprof_timeout} rocprofv3 --kernel-trace --stats --output-format csv "
+            f"-d {odir(st)} -o run "
+            f"-- python bench.py {run} --no-cpu-baseline --no-vanilla",
+            f"python bench.py {run}" + (f" --rocprof-timeout {args.rocprof_timeout}" if args.rocprof_timeout != 300
+                                        else "") + f" --rocprof-summary {st} {tr} > profiles/{profile_name(cfg)}"],
+                        cfg)
         return
     if args.pmc_mfma_summary:
         pmc_mfma_summary(args.pmc_mfma_summary, [
