@@ -52,8 +52,10 @@ class SpecDecoder:
         self.G = max(self.plan[i + 1] - self.plan[i] for i in range(len(self.plan) - 1))
         self.mlp_mode = mlp_mode
         # calibrate=False is the ablation without KV calibration: the fuzzy
-        # entries of accepted drafts stay, and only the emitted token's own
-        # forward (which yields the next d_1) runs precisely
+        # entries of accepted drafts stay, and only the emitted tokens that
+        # have no draft entry yet run precisely (y, and d_k when every draft
+        # was accepted, since no fuzzy step feeds the last draft); that pass
+        # also yields the next d_1
         self.calibrate = calibrate
         # separate=True is the other reading of the calibration (ablation):
         # all k drafts come from fuzzy steps starting at the pending token,
@@ -80,6 +82,7 @@ class SpecDecoder:
         self.commit = torch.zeros(batch, k + 1, **i32)
         self.xt = torch.zeros(batch, **i32)                    # pending token of the round
         self.caltok = torch.zeros(batch, k + 1, **i32)         # [x_t, d_1..d_k] (separate calibration)
+        self.nocal_host = torch.zeros(batch, k + 1, dtype=torch.int32).pin_memory()
         self.dummy_tok = torch.zeros(batch, **i32)
         # per-round integer table: [0:k] positions t+j for j = 0..k-1 ([B] each),
         # [k] calibration start t+1, [k+1] calibration count a+1
@@ -193,8 +196,12 @@ class SpecDecoder:
                 th[k, b] = self.t[b]       # [x_t, d_1..d_a] at t..t+a
             self.t[b] += int(a[b]) + 1
             if not self.calibrate:
-                th[k, b] = self.t[b]
-                th[k + 1, b] = 1
+                # accepted drafts d_1..d_j0 keep their fuzzy entries
+                j0 = min(int(a[b]), k - 1)
+                th[k, b] = self.t[b] - int(a[b]) + j0
+                th[k + 1, b] = int(a[b]) + 1 - j0
+                for i, x in enumerate(emitted[j0:]):
+                    self.nocal_host[b, i] = x
             more = True
         if not more:
             if marks:
@@ -204,8 +211,8 @@ class SpecDecoder:
         # the calibration covers exactly the emitted tokens: its row bound is
         # the longest a + 1 of the round (token rows keep their k + 1 stride)
         rows = max(1, max(int(th[k + 1, b]) for b in range(B)))
-        # without calibration the one row is the emitted token y, which the
-        # accept step left in vtok[:, 0]
+        if not self.calibrate:
+            self.caltok.copy_(self.nocal_host, non_blocking=True)
         if self.separate:
             self.caltok[:, 0].copy_(self.xt)
             self.caltok[:, 1:].copy_(self.vtok[:, 1:])
@@ -213,7 +220,7 @@ class SpecDecoder:
                                   max(self.t), self.inv_temp, self.seed, None, 0, self.dummy_tok, 1, self.ws,
                                   tokens_stride=k + 1)
         else:
-            toks = self.commit if self.calibrate else self.vtok
+            toks = self.commit if self.calibrate else self.caltok
             api.spec_calibrate_kv(self.draft, self.dkv, B, toks, self.tab[k], self.tab[k + 1], rows,
                                   max(self.t), self.inv_temp, self.seed, self.q_logits[:, 0], k * self.V,
                                   self.vtok[:, 1], k + 1, self.ws, tokens_stride=k + 1)

@@ -100,8 +100,13 @@ def spec_generate(draft: OracleModel, base: OracleModel, prompt, k: int, sets,
             forward(draft, dkv, b, [xt] + drafts[:a], range(t, t + a + 1), logits=None)
         elif calibrate:
             zq = forward(draft, dkv, b, emitted, range(t + 1, t + a + 2), logits="last")
-        else:   # ablation: keep fuzzy KV, run only the emitted token precisely
-            zq = forward(draft, dkv, b, [y], [t + a + 1], logits="last")
+        else:
+            # ablation: accepted drafts keep the fuzzy entries their steps
+            # wrote; the tokens that have no draft entry yet run precisely:
+            # y, and d_k too when every draft was accepted (no fuzzy step
+            # feeds the last draft)
+            j0 = min(a, k - 1)
+            zq = forward(draft, dkv, b, emitted[j0:], range(t + 1 + j0, t + a + 2), logits="last")
         t = t + a + 1
         r += 1
     return seq[P:], rounds
