@@ -25,12 +25,14 @@
  *  - Token ids outside [0, vocab) are clamped on the device; positions at or
  *    beyond the KV capacity are treated as invalid rows (no KV write).
  *  - Floating point: weights and KV are float32 (SPEC_F32) or bfloat16
- *    (SPEC_BF16).  Activations, norms, RoPE, softmax and accumulation are
- *    float32.  On the bf16 path every input vector of a weight product is
- *    rounded to bfloat16 (nearest, ties to even) and K/V are stored as bf16;
- *    attention keeps q and the softmax probabilities at float32 precision
- *    against the bf16 K/V (on the bf16 matrix cores each is split into three
- *    bf16 pieces whose sum carries the float32 value).
+ *    (SPEC_BF16; K/V rounded to nearest, ties to even, when written).
+ *    Activations, norms, RoPE, softmax and accumulation are float32 on both
+ *    paths.  A bf16 weight product over two or more activation rows runs on
+ *    the bf16 matrix cores with each float32 activation split into two bf16
+ *    pieces hi + lo (together within 2^-16 of its value); over one row it
+ *    runs as float32 FMAs.  Attention keeps q and the softmax probabilities
+ *    at float32 precision against the bf16 K/V (three bf16 pieces on the
+ *    matrix cores).
  *  - Random numbers: Philox4x64-10 (Salmon et al., SC'11), key = (seed, b),
  *    counter = (v >> 2, position of the token being decided, 0, purpose),
  *    word v & 3, u = ((word >> 41) + 0.5) * 2^-23.  Purposes: 0 draft

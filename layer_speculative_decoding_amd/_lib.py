@@ -11,7 +11,9 @@ import ctypes as C
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libspec.so")
+# SPEC_LIB_PATH selects another build of the same library (the host-sanitizer
+# test loads an ASan/UBSan build this way)
+LIB_PATH = os.environ.get("SPEC_LIB_PATH") or os.path.join(HERE, "libspec.so")
 
 SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_MLP_SEQUENTIAL, SPEC_MLP_PARALLEL = 0, 1

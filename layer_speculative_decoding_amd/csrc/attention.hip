@@ -474,7 +474,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
     __syncthreads();
     if (wave != 0) return;
 
-    T *obase = reinterpret_cast<T *>(p.o) + (int64_t)gi * p.o_sel_stride;
+    float *obase = reinterpret_cast<float *>(p.o) + (int64_t)gi * p.o_sel_stride;
     const int64_t stride_sp = (int64_t)p.n_group * p.Mtot * p.hq;
 #pragma unroll
     for (int nb = 0; nb < NQB; ++nb) {
@@ -507,7 +507,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
                 const bool ok = L > 0.f;   // rows without a valid position have no keys
 #pragma unroll
                 for (int j = 0; j < DV; ++j) ov[j] = ok ? ov[j] / L : 0.f;
-                store_span<T, DV>(obase + ((int64_t)row * p.hq + head) * HD + DV * c, ov);
+                store_span<float, DV>(obase + ((int64_t)row * p.hq + head) * HD + DV * c, ov);
             } else {
                 // several key splits: publish (max, sum, unnormalised output)
                 const int64_t pr = (int64_t)sp * stride_sp + ((int64_t)gi * p.Mtot + row) * p.hq + head;
@@ -543,7 +543,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnParams p) {
     const float den = wave_sum(w * l);
     const int gi = (int)(item / ((int64_t)p.Mtot * p.hq));
     const int64_t rh = item - (int64_t)gi * p.Mtot * p.hq;       // row * hq + head
-    T *o = reinterpret_cast<T *>(p.o) + (int64_t)gi * p.o_sel_stride + rh * HD;
+    float *o = reinterpret_cast<float *>(p.o) + (int64_t)gi * p.o_sel_stride + rh * HD;
     for (int d = lane; d < HD; d += 64) {
         float num = 0.f;
         int s2 = 0;
@@ -558,7 +558,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnParams p) {
             for (int u = 0; u < 4; ++u) num = fmaf(ww[u], a[u], num);
         }
         for (; s2 < p.splits; ++s2) num = fmaf(__shfl(w, s2, 64), p.part_acc[(item + s2 * stride_sp) * HD + d], num);
-        o[d] = Store<T>::from_f32(den > 0.f ? num / den : 0.f);
+        o[d] = den > 0.f ? num / den : 0.f;
     }
 }
 

@@ -2,7 +2,7 @@
 // GEMV and MFMA skinny GEMM).
 //
 //  * X_NORM operands: RMSNorm is folded into the consumer.  Activation row m
-//    is round(gain[k] * h[k] * inv_rms); whoever last wrote h (the embedding,
+//    is gain[k] * h[k] * inv_rms (float32); whoever last wrote h (the embedding,
 //    or a residual-add epilogue below) left per-block partial sums of squares,
 //    and every consuming block sums a row's partials in block order, so no
 //    separate normalisation launch and no cross-block synchronisation exist.
@@ -127,8 +127,8 @@ __device__ __forceinline__ void epi_pair(const GemvParams &p, int u, int r0, int
             c[j + hd / 2] = S::from_f32(y1);
         }
     } else if constexpr (EPI == EPI_SILU_MUL) {
-        T *a = reinterpret_cast<T *>(p.act) + (int64_t)gm * p.act_ld + u;
-        *a = S::from_f32(silu(y0) * y1);
+        float *a = reinterpret_cast<float *>(p.act) + (int64_t)gm * p.act_ld + u;
+        *a = silu(y0) * y1;
     }
 }
 

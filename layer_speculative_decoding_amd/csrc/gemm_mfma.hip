@@ -2,9 +2,10 @@
 // verification rows, the calibration rows, several sequences' draft rows),
 // with the same fused epilogues as the VALU GEMV.
 //
-// Y[m][n] = sum_k X[m][k] W[n][k] with v_mfma_f32_16x16x32_bf16: the
-// activations are the A operand (16 rows, zero padded), a 16-row block of W
-// is the B operand.  At these row counts the product is bound by HBM
+// Y[m][n] = sum_k X[m][k] W[n][k] with v_mfma_f32_16x16x32_bf16: the float32
+// activations are the A operand (16 rows, zero padded) as two bfloat16 pieces
+// hi + lo, so each 32-element step is two matrix instructions; a 16-row block
+// of W is the B operand.  At these row counts the product is bound by HBM
 // bandwidth (a few flops per weight byte), so the kernel is organised around
 // the weight stream:
 //
@@ -61,7 +62,8 @@ __device__ __forceinline__ void group16_argmax(float &v, int &i) {
 // 16-row blocks (2 for the paired epilogues, else 1); the workgroup runs KS
 // waves per block, wave w streaming block w / KS over K part w % KS.
 template <int MT, int EPI, int KS>
-__global__ __launch_bounds__(64 * KS * (epi_is_pair(EPI) ? 2 : 1)) void k_gemm_mfma(GemvParams p, int ups) {
+__global__ __launch_bounds__(64 * KS * (epi_is_pair(EPI) ? 2 : 1), (MT == 1 && epi_is_pair(EPI)) ? 4 : 1)
+void k_gemm_mfma(GemvParams p, int ups) {
     constexpr bool kPair = epi_is_pair(EPI);
     constexpr int NB = kPair ? 2 : 1;       // 16-row blocks per unit
     constexpr int NW = NB * KS;             // waves per workgroup
@@ -113,9 +115,9 @@ __global__ __launch_bounds__(64 * KS * (epi_is_pair(EPI) ? 2 : 1)) void k_gemm_m
         const int sel = r0b / p.rows_per_sel;
         const int rb = blk ? r1b : r0b;         // this wave's block
         const uint16_t *W = reinterpret_cast<const uint16_t *>(p.W) + (int64_t)rb * K;
-        const uint16_t *xb = reinterpret_cast<const uint16_t *>(p.X) + (int64_t)sel * p.x_sel_stride;
+        const float *xb = reinterpret_cast<const float *>(p.X) + (int64_t)sel * p.x_sel_stride;
         bool xok[MT];
-        const uint16_t *xr[MT];
+        const float *xr[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
             xok[t] = t * 16 + li < p.M;
@@ -137,26 +139,45 @@ __global__ __launch_bounds__(64 * KS * (epi_is_pair(EPI) ? 2 : 1)) void k_gemm_m
         for (int tt = t0; tt < t1; ++tt) {
 #pragma unroll
             for (int i = 0; i < NL; ++i) *reinterpret_cast<uint4 *>(&tile[(2 * i + lrow) * kLD + lcol]) = wv[i];
-            // the tile's activation operands are requested before the next
-            // tile's weights, so the matrix cores wait only for them
+            // the first half of the tile's activation operands is requested
+            // before the next tile's weights, so the matrix cores wait only
+            // for them; the second half (float32 rows, L2 hits) follows the
+            // first half's matrix instructions, which keeps the activation
+            // registers at half a tile
             const int nsteps = min(kTK, K - tt * kTK) >> 5;     // 32-element MFMA steps in this tile
-            uint4 xv[kTK / 32][MT];
+            constexpr int HS = kTK / 64;                        // steps per half tile
+            uint4 xv[HS][MT][2];
+            auto load_x = [&](int h) {
 #pragma unroll
-            for (int s2 = 0; s2 < kTK / 32; ++s2)
+                for (int s2 = 0; s2 < HS; ++s2)
 #pragma unroll
-                for (int t = 0; t < MT; ++t)
-                    xv[s2][t] = (xok[t] && s2 < nsteps) ? ld16(xr[t] + tt * kTK + 32 * s2) : make_uint4(0, 0, 0, 0);
-            if (tt + 1 < t1) load(tt + 1);
+                    for (int t = 0; t < MT; ++t) {
+                        const bool ok = xok[t] && h * HS + s2 < nsteps;
+                        const float *xp = xr[t] + tt * kTK + 32 * (h * HS + s2);
+                        xv[s2][t][0] = ok ? ld16(xp) : make_uint4(0, 0, 0, 0);
+                        xv[s2][t][1] = ok ? ld16(xp + 4) : make_uint4(0, 0, 0, 0);
+                    }
+            };
+            auto mma = [&](int h) {
 #pragma unroll
-            for (int s2 = 0; s2 < kTK / 32; ++s2) {
-                if (s2 < nsteps) {
-                    const uint4 wt = *reinterpret_cast<const uint4 *>(&tile[li * kLD + 32 * s2 + 8 * lg]);
+                for (int s2 = 0; s2 < HS; ++s2) {
+                    if (h * HS + s2 < nsteps) {
+                        const uint4 wt = *reinterpret_cast<const uint4 *>(&tile[li * kLD + 32 * (h * HS + s2) + 8 * lg]);
 #pragma unroll
-                    for (int t = 0; t < MT; ++t)
-                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xv[s2][t]), as_bf16x8(wt), acc[t],
-                                                                          0, 0, 0);
+                        for (int t = 0; t < MT; ++t) {
+                            uint4 xh, xl;
+                            split2_bf16(xv[s2][t][0], xv[s2][t][1], xh, xl);
+                            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xh), as_bf16x8(wt), acc[t], 0, 0, 0);
+                            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xl), as_bf16x8(wt), acc[t], 0, 0, 0);
+                        }
+                    }
                 }
-            }
+            };
+            load_x(0);
+            if (tt + 1 < t1) load(tt + 1);
+            mma(0);
+            load_x(1);
+            mma(1);
         }
         if (u + (int)gridDim.x < p.n_units && t0 < t1) {
             int n0, n1;

@@ -14,12 +14,16 @@
 //    epilogues a unit is the (RoPE partner, or gate / up) row pair, so both
 //    rows of a pair end up in the same lane's accumulators; for the other
 //    products a unit's rows are simply n0 + i and n0 + NH + i;
+//  * the float32 activations enter the matrix cores as two bfloat16 pieces
+//    hi + lo (split when the step's rows are written to LDS), so every
+//    fragment pair takes two matrix instructions and the products carry the
+//    activations to within 2^-16 of their magnitude;
 //  * K advances in 64-element steps through one LDS stage (rows padded by 16
 //    bytes, so the fragment reads of a wave spread over all banks); each
-//    lane moves 16 bytes per row (128 contiguous bytes per row per 8 lanes),
-//    the weights two (128-row tiles) or three (64-row) steps ahead of the
-//    matrix instructions (HBM latency),
-//    the activations one step ahead (they stay in L2);
+//    lane moves 16 bytes of weights per row (128 contiguous bytes per row per
+//    8 lanes) and 32 bytes of activations, the weights two (128-row tiles) or
+//    three (64-row) steps ahead of the matrix instructions (HBM latency), the
+//    activations one step ahead (they stay in L2);
 //  * the 64-row weight tile is chosen when 128-row tiles would leave CUs
 //    without a workgroup, and when even those are too few, K is split: each
 //    K slice stores its float32 accumulators, and a second kernel adds the
@@ -142,10 +146,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(GemvParams p, TileArgs ta)
     constexpr int RPP = 32;                      // rows per load pass (8 lanes x 16 bytes per row)
     constexpr int LA = kBM / RPP, LB = BN / RPP; // load passes per step
     // weight steps in flight: three for 64-row tiles (their per-step bytes are
-    // half, and four workgroups share a CU), two for 128-row tiles (whose
+    // half, and three workgroups share a CU), two for 128-row tiles (whose
     // register budget has no room for a third)
     constexpr int DIST = WNB == 2 ? 3 : 2;
-    __shared__ __align__(16) uint16_t lds[(kBM + BN) * kLDK];
+    // activation hi pieces, lo pieces, weights
+    __shared__ __align__(16) uint16_t lds[(2 * kBM + BN) * kLDK];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;
@@ -159,7 +164,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(GemvParams p, TileArgs ta)
     const int nk = SPLIT ? min(ta.kc, K / kBK - kbeg) : K / kBK;
 
     // operands as a uniform base plus 32-bit per-lane byte offsets
-    const char *Xb = reinterpret_cast<const char *>(reinterpret_cast<const uint16_t *>(p.X) +
+    const char *Xb = reinterpret_cast<const char *>(reinterpret_cast<const float *>(p.X) +
                                                     (int64_t)q.sel * p.x_sel_stride + (int64_t)p.m0 * K +
                                                     (int64_t)kbeg * kBK);
     const char *Wb = reinterpret_cast<const char *>(reinterpret_cast<const uint16_t *>(p.W) + (int64_t)kbeg * kBK);
@@ -172,7 +177,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(GemvParams p, TileArgs ta)
     for (int i = 0; i < LA; ++i) {
         const int m = q.m0 + lr + RPP * i;
         va[i] = m < p.M;
-        oa[i] = ((uint32_t)(va[i] ? m : 0) * (uint32_t)K + (uint32_t)lc) * 2u;
+        oa[i] = ((uint32_t)(va[i] ? m : 0) * (uint32_t)K + (uint32_t)lc) * 4u;
     }
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
@@ -188,21 +193,29 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(GemvParams p, TileArgs ta)
     }
     // weights DIST steps ahead (HBM latency), activations one step ahead
     // (they are re-read from L2 by every weight tile)
-    uint4 ra[LA], rb[DIST][LB];
+    uint4 ra[LA][2], rb[DIST][LB];
     auto load_w = [&](int k0, uint4 (&xb)[LB]) {
 #pragma unroll
         for (int i = 0; i < LB; ++i) xb[i] = ld16(Wb + (uint64_t)(ob[i] + (uint32_t)k0 * 2u));
     };
     auto load_x = [&](int k0) {
 #pragma unroll
-        for (int i = 0; i < LA; ++i)
-            ra[i] = va[i] ? ld16(Xb + (uint64_t)(oa[i] + (uint32_t)k0 * 2u)) : make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < LA; ++i) {
+            const char *x = Xb + (uint64_t)(oa[i] + (uint32_t)k0 * 4u);
+            ra[i][0] = va[i] ? ld16(x) : make_uint4(0, 0, 0, 0);
+            ra[i][1] = va[i] ? ld16(x + 16) : make_uint4(0, 0, 0, 0);
+        }
     };
-    auto stash = [&](const uint4 (&xa)[LA], const uint4 (&xb)[LB]) {
+    auto stash = [&](const uint4 (&xa)[LA][2], const uint4 (&xb)[LB]) {
 #pragma unroll
-        for (int i = 0; i < LA; ++i) *reinterpret_cast<uint4 *>(&lds[(lr + RPP * i) * kLDK + lc]) = xa[i];
+        for (int i = 0; i < LA; ++i) {
+            uint4 hi, lo;
+            split2_bf16(xa[i][0], xa[i][1], hi, lo);
+            *reinterpret_cast<uint4 *>(&lds[(lr + RPP * i) * kLDK + lc]) = hi;
+            *reinterpret_cast<uint4 *>(&lds[(kBM + lr + RPP * i) * kLDK + lc]) = lo;
+        }
 #pragma unroll
-        for (int i = 0; i < LB; ++i) *reinterpret_cast<uint4 *>(&lds[(kBM + lr + RPP * i) * kLDK + lc]) = xb[i];
+        for (int i = 0; i < LB; ++i) *reinterpret_cast<uint4 *>(&lds[(2 * kBM + lr + RPP * i) * kLDK + lc]) = xb[i];
     };
 
     f32x4 acc[kWMB][WNB];
@@ -214,24 +227,28 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(GemvParams p, TileArgs ta)
     // LDS rows of this lane's fragments: activation block a, weight block c
     // (member c / HB, unit block c % HB of this wave column)
     const int arow = (64 * wm + li) * kLDK + 8 * lg;
-    const int brow = (kBM + (NH / 2) * wn + li) * kLDK + 8 * lg;
+    const int brow = (2 * kBM + (NH / 2) * wn + li) * kLDK + 8 * lg;
     auto compute = [&]() {
 #pragma unroll
         for (int ks = 0; ks < kBK / 32; ++ks) {
-            uint4 av[kWMB], bv[WNB];
-#pragma unroll
-            for (int a = 0; a < kWMB; ++a)
-                av[a] = *reinterpret_cast<const uint4 *>(&lds[arow + 16 * a * kLDK + 32 * ks]);
+            uint4 bv[WNB];
 #pragma unroll
             for (int c = 0; c < WNB; ++c)
                 bv[c] = *reinterpret_cast<const uint4 *>(
                     &lds[brow + ((c / HB) * NH + 16 * (c % HB)) * kLDK + 32 * ks]);
 #pragma unroll
-            for (int a = 0; a < kWMB; ++a)
+            for (int h = 0; h < 2; ++h) {
+                uint4 av[kWMB];
 #pragma unroll
-                for (int c = 0; c < WNB; ++c)
-                    acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(av[a]), as_bf8(bv[c]), acc[a][c],
-                                                                        0, 0, 0);
+                for (int a = 0; a < kWMB; ++a)
+                    av[a] = *reinterpret_cast<const uint4 *>(&lds[arow + (h * kBM + 16 * a) * kLDK + 32 * ks]);
+#pragma unroll
+                for (int a = 0; a < kWMB; ++a)
+#pragma unroll
+                    for (int c = 0; c < WNB; ++c)
+                        acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(av[a]), as_bf8(bv[c]),
+                                                                            acc[a][c], 0, 0, 0);
+            }
         }
     };
 
@@ -356,12 +373,12 @@ Pick pick(const GemvParams &p, size_t part_bytes) {
         if (fits(p, 128) && (int64_t)gm * (rows / 128) >= 256) return {128, 1};
         if (!fits(p, 64)) return {0, 1};
         k.bn = 64;
-        // fewer than 384 tiles: slices so that at most 1024 workgroups run
-        // (four per CU resident at once: no tail round), each over >= 2 K
+        // fewer than 384 tiles: slices so that at most 768 workgroups run
+        // (three per CU resident at once: no tail round), each over >= 2 K
         // steps (more tiles run better unsplit: the slices' float32 partials
         // cost a write and a read each)
         const int64_t T = (int64_t)gm * (rows / 64);
-        k.ks = T >= 384 ? 1 : (int)(1024 / T);
+        k.ks = T >= 384 ? 1 : (int)(768 / T);
     }
     k.ks = k.ks < 1 ? 1 : (k.ks > kMaxSplit ? kMaxSplit : k.ks);
     if (k.ks > nk / 2) k.ks = nk / 2 < 1 ? 1 : nk / 2;

@@ -32,10 +32,12 @@ constexpr int kUnroll = 4;
 // Normalised operands: every wave forms the rows' 1/rms from the residual
 // writers' partials (summed in partial order, so all waves agree bit for
 // bit).  When the normalised rows of all set members fit in kStageBytes of
-// LDS, the workgroup writes them there once (rounded to the activation type)
-// and the units read them from LDS; the first chunk of weights is requested
-// before, so the staging overlaps the weight stream.  Otherwise each step
-// normalises its own operands.
+// LDS, the workgroup writes them there once (float32) and the units read them
+// from LDS; the first chunk of weights is requested before, so the staging
+// overlaps the weight stream.  Otherwise each step normalises its own
+// operands.  Activations are float32 on both paths (only weights and the KV
+// cache are bfloat16 on the bfloat16 path), so the products are float32 dot
+// products of the stored weights.
 constexpr int kStageBytes = 32768;
 
 enum : int { XM_PLAIN = 0, XM_STAGED = 1, XM_DIRECT = 2 };
@@ -47,7 +49,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, int KS) {
     constexpr bool staged = XM == XM_STAGED;
     constexpr int E = S::kPer16;
     constexpr bool kPair = epi_is_pair(EPI);
-    __shared__ __align__(16) T xs[staged ? kStageBytes / sizeof(T) : 8];
+    __shared__ __align__(16) float xs[staged ? kStageBytes / 4 : 4];
     __shared__ float red[kWaves][kMaxRows][2];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, int KS) {
                         if constexpr (E == 8) x_norm8(p, sel, hrow[m], k, inv[m], f);
                         else x_norm4(p, sel, hrow[m], k, inv[m], f);
 #pragma unroll
-                        for (int e = 0; e < E; ++e) xs[(sel * MR + m) * K + k + e] = S::from_f32(f[e]);
+                        for (int e = 0; e < E; ++e) xs[(sel * MR + m) * K + k + e] = f[e];
                     }
                 }
             __syncthreads();
@@ -135,8 +137,8 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, int KS) {
             unit_rows(u, r0, r1, sel);
             const T *w0 = reinterpret_cast<const T *>(p.W) + (int64_t)r0 * K;
             const T *w1 = reinterpret_cast<const T *>(p.W) + (int64_t)r1 * K;
-            const T *xp = reinterpret_cast<const T *>(p.X) + (int64_t)sel * p.x_sel_stride + (int64_t)p.m0 * K;
-            const T *xl = xs + (int64_t)sel * MR * K;
+            const float *xp = reinterpret_cast<const float *>(p.X) + (int64_t)sel * p.x_sel_stride + (int64_t)p.m0 * K;
+            const float *xl = xs + (int64_t)sel * MR * K;
             float a0[MR], a1[MR];
 #pragma unroll
             for (int m = 0; m < MR; ++m) { a0[m] = 0.f; a1[m] = 0.f; }
@@ -154,14 +156,16 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, int KS) {
                         for (int e = 0; e < E; ++e) xo[q][m][e] = 0.f;
                         if (m >= p.M || k >= ke) continue;
                         if constexpr (!kNorm) {
-                            S::unpack(ld16(xp + (int64_t)m * K + k), xo[q][m]);
+#pragma unroll
+                            for (int e = 0; e < E; e += 4)
+                                Store<float>::unpack(ld16(xp + (int64_t)m * K + k + e), xo[q][m] + e);
                         } else if constexpr (staged) {
-                            S::unpack(*reinterpret_cast<const uint4 *>(xl + m * K + k), xo[q][m]);
+#pragma unroll
+                            for (int e = 0; e < E; e += 4)
+                                Store<float>::unpack(*reinterpret_cast<const uint4 *>(xl + m * K + k + e), xo[q][m] + e);
                         } else {
                             if constexpr (E == 8) x_norm8(p, sel, hrow[m], k, inv[m], xo[q][m]);
                             else x_norm4(p, sel, hrow[m], k, inv[m], xo[q][m]);
-#pragma unroll
-                            for (int e = 0; e < E; ++e) xo[q][m][e] = S::round(xo[q][m][e]);
                         }
                     }
                 }
@@ -260,18 +264,17 @@ void launch_tex(const GemvParams &p, int grid, int ks, hipStream_t s) {
     else hipLaunchKernelGGL((k_gemv<T, 8, EPI, XM>), g, b, 0, s, p, ks);
 }
 
-// normalised operands go through LDS when every set member's rows fit
-template <typename T>
+// normalised (float32) operands go through LDS when every set member's rows fit
 bool gemv_staged(const GemvParams &p) {
     const int mr = p.M <= 1 ? 1 : (p.M <= 2 ? 2 : (p.M <= 4 ? 4 : 8));
     const int64_t n_sel = (int64_t)p.n_units * 2 / p.rows_per_sel;
-    return n_sel * mr * p.K * (int64_t)sizeof(T) <= kStageBytes;
+    return n_sel * mr * p.K * 4 <= kStageBytes;
 }
 
 template <typename T, int EPI>
 void launch_ten(const GemvParams &p, int grid, int ks, bool norm, hipStream_t s) {
     if (!norm) launch_tex<T, EPI, XM_PLAIN>(p, grid, ks, s);
-    else if (gemv_staged<T>(p)) launch_tex<T, EPI, XM_STAGED>(p, grid, ks, s);
+    else if (gemv_staged(p)) launch_tex<T, EPI, XM_STAGED>(p, grid, ks, s);
     else launch_tex<T, EPI, XM_DIRECT>(p, grid, ks, s);
 }
 
@@ -307,8 +310,8 @@ hipError_t launch_t(const GemvParams &p, int grid, int ks, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------ norm
-// Normalised activations for the matrix-core products:
-// xn[sel][m][k] = round(gain_sel[k] * (xh[hrow][k] + xadd[sel][hrow][k]) / rms(hrow)),
+// Normalised float32 activations for the matrix-core products:
+// xn[sel][m][k] = gain_sel[k] * (xh[hrow][k] + xadd[sel][hrow][k]) / rms(hrow),
 // rms from the row's sum-of-squares partials (summed in block order by every
 // wave, so all blocks agree bit for bit).  Grid (K / 2048, M, n_sel).  The
 // row's values and gains are requested before the partials, so the two
@@ -341,9 +344,9 @@ __global__ __launch_bounds__(256) void k_norm_rows(GemvParams p, void *xn) {
     }
     const float f[8] = {h0.x * inv * g0.x, h0.y * inv * g0.y, h0.z * inv * g0.z, h0.w * inv * g0.w,
                         h1.x * inv * g1.x, h1.y * inv * g1.y, h1.z * inv * g1.z, h1.w * inv * g1.w};
-    T *o = reinterpret_cast<T *>(xn) + ((int64_t)sel * p.Mtot + p.m0 + m) * p.K + k;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = Store<T>::from_f32(f[e]);
+    float4 *o = reinterpret_cast<float4 *>(reinterpret_cast<float *>(xn) + ((int64_t)sel * p.Mtot + p.m0 + m) * p.K + k);
+    o[0] = make_float4(f[0], f[1], f[2], f[3]);
+    o[1] = make_float4(f[4], f[5], f[6], f[7]);
 }
 
 // ------------------------------------------------------------------ sampling
@@ -428,9 +431,9 @@ int gemv_grid(const GemvParams &p, int ks) {
 }
 
 int gemv_operand_mode(int dtype, const GemvParams &p) {
+    (void)dtype;
     if (p.xmode != X_NORM) return XM_PLAIN;
-    const bool st = dtype ? gemv_staged<uint16_t>(p) : gemv_staged<float>(p);
-    return st ? XM_STAGED : XM_DIRECT;
+    return gemv_staged(p) ? XM_STAGED : XM_DIRECT;
 }
 
 hipError_t launch_gemv(int dtype, const GemvParams &p, int grid, int ks, hipStream_t s) {

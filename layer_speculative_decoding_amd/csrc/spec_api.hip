@@ -21,7 +21,7 @@ struct spec_model {
     spec_weights w;
     int D;      // (hq + 2 hkv) * hd
     int qd;     // hq * hd
-    int xs;     // activation element size (4 f32, 2 bf16)
+    int xs;     // weight and KV element size (4 f32, 2 bf16); activations are float32
 };
 
 namespace {
@@ -126,10 +126,10 @@ Carve carve(const spec_model *m, int batch, int max_m, int G) {
     c.h = take(R * d * 4);
     c.h0 = take(R * d * 4);
     c.abuf = take((size_t)G * R * d * 4);
-    c.xn = take((size_t)G * R * d * xs);
+    c.xn = take((size_t)G * R * d * 4);
     c.q = take((size_t)G * R * hq * hd * 4);
-    c.o = take((size_t)G * R * hq * hd * xs);
-    c.act = take(R * (size_t)m->d.d_ffn * xs);
+    c.o = take((size_t)G * R * hq * hd * 4);
+    c.act = take(R * (size_t)m->d.d_ffn * 4);
     c.pacc = take((size_t)attention_split_max() * G * prow * hq * hd * 4);
     c.pml = take((size_t)attention_split_max() * G * prow * hq * 2 * 4);
     c.pval = take((size_t)batch * kPartialsMax * 4);
@@ -207,7 +207,7 @@ hipError_t product(const Fwd &f, GemvParams p, int *parts_out = nullptr) {
     if (m->d.dtype == SPEC_BF16 && Mtot >= tiled_min_rows() && gemm_tiled_supported(t)) {
         // more than 16 rows: one tiled launch over every row
         if (parts_out) *parts_out = gemm_tiled_parts(t);
-        double xbytes = (double)Mtot * p.K * m->xs;
+        double xbytes = (double)Mtot * p.K * 4;
         if (p.xmode == X_NORM) {
             const int n_sel = rows / p.rows_per_sel;
             void *xn = at<char>(f.ws, f.c.xn);
@@ -233,7 +233,7 @@ hipError_t product(const Fwd &f, GemvParams p, int *parts_out = nullptr) {
             q.m0 = m0;
             q.M = (Mtot - m0) < mr ? (Mtot - m0) : mr;
             GemvParams r = q;
-            double xbytes = (double)q.M * p.K * m->xs;
+            double xbytes = (double)q.M * p.K * 4;
             if (p.xmode == X_NORM) {
                 // normalise once into xn, then stream the weights against it
                 const int n_sel = rows / p.rows_per_sel;
@@ -261,7 +261,7 @@ hipError_t product(const Fwd &f, GemvParams p, int *parts_out = nullptr) {
         p.M = (Mtot - m0) < mr ? (Mtot - m0) : mr;
         ProfScope ps(f.s);
         hipError_t e = launch_gemv(m->d.dtype, p, grid, ks, f.s);
-        ps.done(gemv_name(m->d.dtype, p), wbytes + (double)p.M * p.K * (p.xmode == X_NORM ? 4 : m->xs),
+        ps.done(gemv_name(m->d.dtype, p), wbytes + (double)p.M * p.K * 4,
                 2.0 * p.M * rows * (double)p.K);
         if (e != hipSuccess) return e;
     }

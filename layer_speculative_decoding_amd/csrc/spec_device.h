@@ -43,6 +43,27 @@ template <> struct Store<uint16_t> {
 };
 
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+// Activation buffers are float32 on both paths.  A bfloat16 matrix-core
+// product takes a float32 operand as two bfloat16 pieces hi + lo (hi the
+// float32 value with its low 16 bits dropped, lo the remainder rounded to
+// nearest): the pair carries the value to within 2^-16 of its magnitude, and
+// each piece times a bfloat16 weight is exact in float32, so two products
+// replace one float32 product at that precision.
+__device__ __forceinline__ void split2_bf16(const uint4 &a, const uint4 &b, uint4 &hi, uint4 &lo) {
+    const uint32_t x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t x0 = x[2 * i] & 0xFFFF0000u, x1 = x[2 * i + 1] & 0xFFFF0000u;
+        h[i] = (x0 >> 16) | x1;
+        const uint16_t l0 = f32_to_bf16(__uint_as_float(x[2 * i]) - __uint_as_float(x0));
+        const uint16_t l1 = f32_to_bf16(__uint_as_float(x[2 * i + 1]) - __uint_as_float(x1));
+        l[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    }
+    hi = make_uint4(h[0], h[1], h[2], h[3]);
+    lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // Streaming (non-temporal) 16-byte load for data read once per step.
 __device__ __forceinline__ uint4 ld16_stream(const void *p) {

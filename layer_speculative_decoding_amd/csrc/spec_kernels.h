@@ -22,7 +22,7 @@ struct RowMap {
 enum GemvEpi : int {
     EPI_STORE = 0,      // out[m * out_ld + sel * out_sel_stride + row_in_sel] = y
     EPI_QKV_ROPE = 1,   // RoPE on q/k pairs; q -> q_out, k/v -> KV cache
-    EPI_SILU_MUL = 2,   // act[m * act_ld + unit] = round(silu(gate) * up)
+    EPI_SILU_MUL = 2,   // act[m * act_ld + unit] = silu(gate) * up (float32)
     EPI_RESID_ADD = 3,  // h[m][row] += y (+ add2[m][row]); row-norm partials of h
     EPI_LOGITS = 4,     // store (if out) + per-block Gumbel / greedy arg-max partials
     EPI_ATTN_OUT = 5,   // sequential MLPs: sel 0 -> h += y (+ partials), sel > 0 -> abuf
@@ -32,8 +32,8 @@ enum GemvEpi : int {
 
 // How a product reads its activations.
 enum XMode : int {
-    X_PLAIN = 0,   // X[sel * x_sel_stride + m * K + k] (activation dtype)
-    X_NORM = 1,    // round(gain_sel[k] * (xh[hrow][k] + xadd[sel][hrow][k]) / rms(hrow))
+    X_PLAIN = 0,   // X[sel * x_sel_stride + m * K + k] (float32)
+    X_NORM = 1,    // gain_sel[k] * (xh[hrow][k] + xadd[sel][hrow][k]) / rms(hrow)
 };
 
 struct GemvParams {
@@ -96,7 +96,9 @@ struct GemvParams {
     int32_t *part_idx;
 };
 
-// dtype: 0 float32, 1 bfloat16 (weights and activation buffers share it).
+// dtype: 0 float32, 1 bfloat16: the weights and the KV cache.  Activation
+// buffers (normalised rows, attention outputs, SiLU products) are float32 on
+// both paths.
 // VALU GEMV: units are row pairs, M <= gemv_max_rows() per launch; ks waves
 // (1, 2 or 4) split each unit's K.
 hipError_t launch_gemv(int dtype, const GemvParams &p, int grid, int ks, hipStream_t s);
@@ -126,8 +128,8 @@ int gemm_tiled_min_rows();
 int gemm_tiled_parts(const GemvParams &p);
 size_t gemm_tiled_part_bytes();
 std::string gemm_tiled_name(const GemvParams &p, size_t part_bytes);   // kernel instance, for measurement
-// X_NORM operands written once as activation-dtype rows xn[sel][m][K] for
-// rows m0 .. m0 + M - 1 (the matrix-core products then read them plainly).
+// X_NORM operands written once as float32 rows xn[sel][m][K] for rows
+// m0 .. m0 + M - 1 (the matrix-core products then read them plainly).
 hipError_t launch_norm_rows(int dtype, const GemvParams &p, int n_sel, void *xn, hipStream_t s);
 bool gemm_mfma_supported(const GemvParams &p);
 int gemm_mfma_max_rows();
@@ -165,7 +167,7 @@ struct AttnParams {
     RowMap rows;
     int max_pos;           // host bound of positions in this call
     int splits;
-    void *o;               // [g][Mtot][hq*hd] activation dtype
+    void *o;               // [g][Mtot][hq*hd] float32
     int64_t o_sel_stride;
     float *part_acc;       // [splits][g][Mtot][hq][hd]
     float *part_ml;        // [splits][g][Mtot][hq][2]

@@ -25,8 +25,9 @@ order: h = h + a_i; h = h + MLP_i(h).  The "parallel MLP" variant: h = h0 +
 sum_i (a_i + MLP_i(h0 + a_i)).  Both equal the sequential layer for a set of
 size 1.
 
-bf16 path: weights and KV are bfloat16 values; every matrix-product input is
-rounded to bfloat16 (see oracle.numerics); everything else is float64 here.
+bf16 path: weights and the KV cache hold bfloat16 values (the weights are
+given as such; K and V are rounded to bfloat16 when they are written, see
+oracle.numerics); every activation is float64 here.
 """
 from __future__ import annotations
 
@@ -81,7 +82,12 @@ class KVCache:
 # ----------------------------------------------------------------- primitives
 def linear(x, W):
     """x W^T for x [n][in], W [out][in] (computed as (W x^T)^T so that NumPy
-    hands the row-major weight to BLAS as is)."""
+    hands the row-major weight to BLAS as is).  The product is formed in the
+    weights' precision: float64 for the default float64 model; float32 for a
+    model whose weights are held as float32 (workload-size models whose
+    float64 copy would not fit), whose residual stream stays float64."""
+    if W.dtype == np.float32 and x.dtype != np.float32:
+        x = x.astype(np.float32)
     return (W @ x.T).T
 
 
@@ -132,7 +138,7 @@ def attn_part(m: OracleModel, cache: KVCache, l: int, b: int, h_in, positions):
     """
     sh, w = m.shape, m.w
     hq, hkv, hd = sh.n_q_heads, sh.n_kv_heads, sh.head_dim
-    x = m.rnd(rmsnorm(h_in, w["attn_norm"][l], sh.rms_eps))
+    x = rmsnorm(h_in, w["attn_norm"][l], sh.rms_eps)
     qkv = linear(x, w["wqkv"][l])
     if w.get("bqkv") is not None:
         qkv = qkv + w["bqkv"][l]
@@ -146,16 +152,16 @@ def attn_part(m: OracleModel, cache: KVCache, l: int, b: int, h_in, positions):
         cache.k[l, b, :, p] = m.rnd(k[r])
         cache.v[l, b, :, p] = m.rnd(v[r])
     o = attention(q, cache.k[l, b], cache.v[l, b], positions, hkv)
-    o = m.rnd(o.reshape(n, hq * hd))
+    o = o.reshape(n, hq * hd)
     return linear(o, w["wo"][l])
 
 
 def mlp_part(m: OracleModel, l: int, h_in):
     sh, w = m.shape, m.w
     f = sh.d_ffn
-    y = m.rnd(rmsnorm(h_in, w["ffn_norm"][l], sh.rms_eps))
+    y = rmsnorm(h_in, w["ffn_norm"][l], sh.rms_eps)
     gu = linear(y, w["w_gate_up"][l])
-    act = m.rnd(silu(gu[:, :f]) * gu[:, f:])
+    act = silu(gu[:, :f]) * gu[:, f:]
     return linear(act, w["w_down"][l])
 
 
@@ -164,7 +170,7 @@ def embed(m: OracleModel, tokens):
 
 
 def final_logits(m: OracleModel, h):
-    x = m.rnd(rmsnorm(h, m.w["final_norm"], m.shape.rms_eps))
+    x = rmsnorm(h, m.w["final_norm"], m.shape.rms_eps)
     return linear(x, m.w["lm_head"])
 
 

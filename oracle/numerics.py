@@ -1,10 +1,10 @@
 """bfloat16 rounding for the oracle's mirror of the bf16 path.
 
-On the bf16 path the weights and the KV cache are bfloat16, and every input
-vector of a matrix product is rounded to bfloat16 (round to nearest, ties to
-even) before the product; all other arithmetic stays in float32 on the GPU and
-in float64 here.  This module is the oracle's own implementation of that
-rounding.  (The pages fix no precision; this is the build's reading.)
+On the bf16 path the weights and the KV cache are bfloat16: K and V are
+rounded to bfloat16 (round to nearest, ties to even) when they are written to
+the cache.  Activations are not rounded (float32 on the GPU, float64 here).
+This module is the oracle's own implementation of that rounding.  (The pages
+fix no precision; this is the build's reading.)
 """
 from __future__ import annotations
 

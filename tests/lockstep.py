@@ -10,7 +10,10 @@ sequence (scores are z / T plus identical Gumbel noise):
   draft / greedy / bonus arg-max:   2 * s * dz      (s = 1/T, or 1 greedy)
   accept test |u - p/q|, residual:  8 * s * dz      (p/q and log(p - q) move
                                                      by at most ~4 s dz)
-never below MARGIN."""
+never below MARGIN.  The stats separate the excluded decisions into those
+below MARGIN (the fixed rule: within 1e-3 of a tie or threshold) and those in
+the band between MARGIN and the error-derived bound ('band'), and count how
+many excluded decisions the GPU took differently ('flipped')."""
 import numpy as np
 
 from oracle.decode import spec_generate
@@ -25,7 +28,7 @@ def lockstep(dec, om_draft, om_base, prompts, k, sets, new_tokens, inv_temp, see
     gpu_out = dec.generate(prompts, new_tokens)
     recs = dec.records
     s = 1.0 if inv_temp == 0.0 else inv_temp
-    stats = {"checked": 0, "excluded": 0, "err": 0.0}
+    stats = {"checked": 0, "excluded": 0, "band": 0, "flipped": 0, "err": 0.0, "rounds": len(recs)}
     for b in range(B):
         log = []
 
@@ -64,4 +67,6 @@ def lockstep(dec, om_draft, om_base, prompts, k, sets, new_tokens, inv_temp, see
                 stats["checked"] += 1
             else:
                 stats["excluded"] += 1
+                stats["band"] += margin >= MARGIN
+                stats["flipped"] += g != value
     return stats
