@@ -212,8 +212,16 @@ def rocprof_summary(stats_csv, trace_csv, command, cfg):
               f"{float(r['TotalDurationNs']) / 1e6:.2f} | {float(r['Percentage']):.1f} |")
     tr = list(csv.DictReader(open(trace_csv)))
     tr.sort(key=lambda r: int(r["Start_Timestamp"]))
-    ks = [(short(r["Kernel_Name"]), int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
-           int(r["Grid_Size_X"]) // max(int(r["Workgroup_Size_X"]), 1), int(r["Workgroup_Size_X"])) for r in tr]
+    def dims(r, key):
+        return [int(r.get(f"{key}_{a}", 1) or 1) for a in "XYZ"]
+
+    def grid(r):
+        # workgroups per dimension x threads per workgroup, e.g. (1, 16, 5) x 256
+        g, w = dims(r, "Grid_Size"), dims(r, "Workgroup_Size")
+        wg = tuple(gi // max(wi, 1) for gi, wi in zip(g, w))
+        blk = w[0] * w[1] * w[2]
+        return (f"{wg[0]}" if wg[1:] == (1, 1) else f"({wg[0]}, {wg[1]}, {wg[2]})"), blk
+    ks = [(short(r["Kernel_Name"]), int(r["Start_Timestamp"]), int(r["End_Timestamp"])) + grid(r) for r in tr]
     idx = [i for i, r in enumerate(ks) if r[0] == "k_acc_stats"]
     seg = ks[idx[-2]:idx[-1]]
     sr = [i for i, r in enumerate(seg) if r[0] == "k_sample_reduce"]
@@ -229,7 +237,7 @@ def rocprof_summary(stats_csv, trace_csv, command, cfg):
         print()
         print(f"**{name}**: {len(st)} kernels, busy {busy:.1f} us")
         print()
-        print("| kernel | grid x block | launches | total us | avg us |")
+        print("| kernel | workgroups x threads | launches | total us | avg us |")
         print("|---|---|---|---|---|")
         agg = collections.defaultdict(lambda: [0, 0.0])
         for r in st:
@@ -535,6 +543,75 @@ def main():
     log(f"  draft steps + verify: back to back {ser_ms:.3f} ms, on two streams {ovl_ms:.3f} ms")
     del ws2
 
+    # the draft step at a fixed context P + 64 (comparable across acceptance
+    # rates): the round's k-1 steps at positions P+64 .. (their KV writes land
+    # beyond the committed positions and are rewritten before they are read)
+    t_keep = list(dec.t)
+    dec.t = [P + 64] * cfg.batch
+    dec._upload_positions()
+    t_fix = []
+    for _ in range(5):
+        a_, b_ = ev(), ev()
+        a_.record()
+        dec.draft_phase()
+        b_.record()
+        torch.cuda.synchronize()
+        t_fix.append(a_.elapsed_time(b_) / n_dsteps)
+    step_fix = float(np.median(t_fix))
+    fix_bytes = draft_step_bytes(cfg.draft, P + 64)
+    log(f"  draft step at context {P + 64}: {step_fix * 1e3:.0f} us, "
+        f"{fix_bytes / (step_fix * 1e-3) / 1e9:.0f} GB/s")
+    # calibration cost per row count (a + 1 = 1 .. k + 1 emitted tokens), at
+    # the same positions, for the projections below
+    cal_ms = []
+    ntok = torch.zeros(cfg.batch, dtype=torch.int32, device=dev)
+    start = torch.full((cfg.batch,), P + 64, dtype=torch.int32, device=dev)
+    for m_ in range(1, k + 2):
+        ntok.fill_(m_)
+        tt = []
+        for _ in range(5):
+            a_, b_ = ev(), ev()
+            a_.record()
+            api.spec_calibrate_kv(dec.draft, dec.dkv, cfg.batch, dec.commit, start, ntok, k + 1, P + 64 + m_ - 1,
+                                  dec.inv_temp, dec.seed, dec.q_logits[:, 0], k * dec.V, dec.vtok[:, 1], k + 1,
+                                  dec.ws, tokens_stride=k + 1)
+            b_.record()
+            torch.cuda.synchronize()
+            tt.append(a_.elapsed_time(b_))
+        cal_ms.append(float(np.median(tt)))
+    dec.t = t_keep
+    log("  calibration by rows: " + ", ".join(f"{i + 1}: {c * 1e3:.0f} us" for i, c in enumerate(cal_ms)))
+
+    # tokens/s at acceptance rates alpha per draft (E[a] under a truncated
+    # geometric law, Leviathan et al.): the measured phases with the
+    # calibration cost of a + 1 rows, the same kernels and shapes
+    base_ms = ms["draft"] + ms["verify"] + ms["accept"]
+
+    def projected(alpha):
+        pa = [alpha ** j * (1 - alpha) for j in range(k)] + [alpha ** k]
+        tok = sum(p_ * (j + 1) for j, p_ in enumerate(pa))
+        rnd = base_ms + sum(p_ * cal_ms[j] for j, p_ in enumerate(pa))
+        return round(cfg.batch * tok / (rnd * 1e-3), 2)
+    proj = {"0.5": projected(0.5), "0.8": projected(0.8)}
+    log(f"  projected tokens/s at acceptance 0.5: {proj['0.5']}, at 0.8: {proj['0.8']}")
+
+    # copy ceiling measured on this GPU: a 2 GiB device-to-device copy (bytes
+    # read + bytes written over its time)
+    src = torch.empty(1 << 30, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    tc = []
+    for _ in range(5):
+        a_, b_ = ev(), ev()
+        a_.record()
+        dst.copy_(src)
+        b_.record()
+        torch.cuda.synchronize()
+        tc.append(a_.elapsed_time(b_))
+    copy_gbs = 2 * src.numel() * 2 / (float(np.median(tc)) * 1e-3) / 1e9
+    del src, dst
+    log(f"  device copy ceiling: {copy_gbs:.0f} GB/s")
+
     n1 = None
     if args.n1_compare:
         d1 = SpecDecoder(cfg.draft, dw, cfg.base, bw, cfg.batch, cap, k, seq_offs, P, inv_t, cfg.sample_seed,
@@ -606,9 +683,17 @@ def main():
                      "launches": dom_n, "avg_launch_us": round(dom_ms / dom_n * 1e3, 2),
                      "bytes_per_launch": int(dom_bytes / dom_n)},
         "roofline_draft_step": {"bound": "hbm", "achieved": round(d_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                "frac": round(d_gbs / HBM_PEAK_GBS, 4), "bytes_per_step": int(d_bytes)},
+                                "frac": round(d_gbs / HBM_PEAK_GBS, 4), "frac_of_copy_ceiling": round(d_gbs / copy_gbs, 4),
+                                "bytes_per_step": int(d_bytes)},
+        "draft_step_at_fixed_context": {"context": P + 64, "us": round(step_fix * 1e3, 1),
+                                        "gbs": round(fix_bytes / (step_fix * 1e-3) / 1e9, 1),
+                                        "frac": round(fix_bytes / (step_fix * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "roofline_verify": {"bound": "hbm", "achieved": round(v_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                            "frac": round(v_gbs / HBM_PEAK_GBS, 4), "bytes_per_step": int(v_bytes)},
+                            "frac": round(v_gbs / HBM_PEAK_GBS, 4), "frac_of_copy_ceiling": round(v_gbs / copy_gbs, 4),
+                            "bytes_per_step": int(v_bytes)},
+        "copy_ceiling_gbs": round(copy_gbs, 1),
+        "calibrate_us_by_rows": [round(c * 1e3, 1) for c in cal_ms],
+        "projected_tokens_per_s": proj,
         "kernels": {name: {"launches": n, "avg_us": round(t / n * 1e3, 2),
                            "gbs": round(by / (t * 1e-3) / 1e9, 1)} for name, (n, t, by, _) in prof.items()},
         "mfma_decode": {"bound": "mfma", "achieved": round(mf_tfs, 2), "peak": MFMA_BF16_PEAK_TFS,

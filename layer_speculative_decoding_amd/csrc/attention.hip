@@ -108,6 +108,23 @@ __device__ __forceinline__ void store_span(T *p, const float *v) {
     for (int i = 0; i < N; ++i) p[i] = Store<T>::from_f32(v[i]);
 }
 
+// N output elements of (layer gi, row, q head) from dim d0: float32 rows, or
+// the packed operand of the O product's matrix-core kernel (bf16 hi pieces
+// at row `row`, lo pieces at row + o_packed / 2)
+template <int N>
+__device__ __forceinline__ void store_out(const AttnParams &p, int gi, int row, int head, int d0, const float *v) {
+    if (p.o_packed) {
+        uint16_t *o = reinterpret_cast<uint16_t *>(p.o) + (int64_t)gi * p.o_sel_stride;
+        uint16_t *hp = o + ((int64_t)row * p.hq + head) * p.hd + d0;
+        uint16_t *lp = o + ((int64_t)(row + p.o_packed / 2) * p.hq + head) * p.hd + d0;
+#pragma unroll
+        for (int i = 0; i < N; ++i) split2_one(v[i], hp[i], lp[i]);
+    } else {
+        float *o = reinterpret_cast<float *>(p.o) + (int64_t)gi * p.o_sel_stride;
+        store_span<float, N>(o + ((int64_t)row * p.hq + head) * p.hd + d0, v);
+    }
+}
+
 // N consecutive cache elements kept as loaded (bf16 pairs stay packed until
 // used, which halves the registers a K or V slice needs).
 template <typename T, int N> struct Raw;
@@ -474,7 +491,6 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
     __syncthreads();
     if (wave != 0) return;
 
-    float *obase = reinterpret_cast<float *>(p.o) + (int64_t)gi * p.o_sel_stride;
     const int64_t stride_sp = (int64_t)p.n_group * p.Mtot * p.hq;
 #pragma unroll
     for (int nb = 0; nb < NQB; ++nb) {
@@ -507,7 +523,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
                 const bool ok = L > 0.f;   // rows without a valid position have no keys
 #pragma unroll
                 for (int j = 0; j < DV; ++j) ov[j] = ok ? ov[j] / L : 0.f;
-                store_span<float, DV>(obase + ((int64_t)row * p.hq + head) * HD + DV * c, ov);
+                store_out<DV>(p, gi, row, head, DV * c, ov);
             } else {
                 // several key splits: publish (max, sum, unnormalised output)
                 const int64_t pr = (int64_t)sp * stride_sp + ((int64_t)gi * p.Mtot + row) * p.hq + head;
@@ -543,7 +559,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnParams p) {
     const float den = wave_sum(w * l);
     const int gi = (int)(item / ((int64_t)p.Mtot * p.hq));
     const int64_t rh = item - (int64_t)gi * p.Mtot * p.hq;       // row * hq + head
-    float *o = reinterpret_cast<float *>(p.o) + (int64_t)gi * p.o_sel_stride + rh * HD;
+    const int row = (int)(rh / p.hq), head = (int)(rh - (int64_t)row * p.hq);
     for (int d = lane; d < HD; d += 64) {
         float num = 0.f;
         int s2 = 0;
@@ -558,7 +574,8 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnParams p) {
             for (int u = 0; u < 4; ++u) num = fmaf(ww[u], a[u], num);
         }
         for (; s2 < p.splits; ++s2) num = fmaf(__shfl(w, s2, 64), p.part_acc[(item + s2 * stride_sp) * HD + d], num);
-        o[d] = den > 0.f ? num / den : 0.f;
+        const float v = den > 0.f ? num / den : 0.f;
+        store_out<1>(p, gi, row, head, d, &v);
     }
 }
 

@@ -127,8 +127,17 @@ __device__ __forceinline__ void epi_pair(const GemvParams &p, int u, int r0, int
             c[j + hd / 2] = S::from_f32(y1);
         }
     } else if constexpr (EPI == EPI_SILU_MUL) {
-        float *a = reinterpret_cast<float *>(p.act) + (int64_t)gm * p.act_ld + u;
-        *a = silu(y0) * y1;
+        const float a = silu(y0) * y1;
+        if (p.act_packed) {
+            // packed operand rows of the down product's matrix-core kernel
+            uint16_t hi, lo;
+            split2_one(a, hi, lo);
+            uint16_t *a16 = reinterpret_cast<uint16_t *>(p.act);
+            a16[(int64_t)gm * p.act_ld + u] = hi;
+            a16[(int64_t)(gm + p.act_packed / 2) * p.act_ld + u] = lo;
+        } else {
+            reinterpret_cast<float *>(p.act)[(int64_t)gm * p.act_ld + u] = a;
+        }
     }
 }
 

@@ -1,11 +1,17 @@
-// Skinny bf16 GEMM on the matrix cores for 2..32 activation rows (the k+1
+// Skinny bf16 GEMM on the matrix cores for 2..16 activation rows (the k+1
 // verification rows, the calibration rows, several sequences' draft rows),
 // with the same fused epilogues as the VALU GEMV.
 //
-// Y[m][n] = sum_k X[m][k] W[n][k] with v_mfma_f32_16x16x32_bf16: the float32
-// activations are the A operand (16 rows, zero padded) as two bfloat16 pieces
-// hi + lo, so each 32-element step is two matrix instructions; a 16-row block
-// of W is the B operand.  At these row counts the product is bound by HBM
+// Y[m][n] = sum_k X[m][k] W[n][k] with v_mfma_f32_16x16x32_bf16: the
+// activations are the A operand, a 16-row block of W the B operand.  The
+// float32 activation rows arrive as bf16 pieces packed into the operand's
+// rows by their producer (the normalisation pass, the attention output, the
+// SiLU epilogue): with M <= 8 rows, row m holds hi(x_m) and row m + 8 holds
+// lo(x_m) in one 16-row tile; with M <= 16, tile 0 holds the hi rows and
+// tile 1 the lo rows.  hi + lo is within 2^-16 of x, each piece times a bf16
+// weight is exact in float32, so the two halves of the result add up to the
+// float32 product at that precision; up to 8 rows this costs no matrix
+// instruction more than bf16 activations would.  At these row counts the product is bound by HBM
 // bandwidth (a few flops per weight byte), so the kernel is organised around
 // the weight stream:
 //
@@ -58,12 +64,11 @@ __device__ __forceinline__ void group16_argmax(float &v, int &i) {
     }
 }
 
-// MT: 16-row activation tiles (1: M <= 16, 2: M <= 32).  A unit has NB
+// MT: 16-row operand tiles (1: M <= 8, 2: M <= 16).  A unit has NB
 // 16-row blocks (2 for the paired epilogues, else 1); the workgroup runs KS
 // waves per block, wave w streaming block w / KS over K part w % KS.
 template <int MT, int EPI, int KS>
-__global__ __launch_bounds__(64 * KS * (epi_is_pair(EPI) ? 2 : 1), (MT == 1 && epi_is_pair(EPI)) ? 4 : 1)
-void k_gemm_mfma(GemvParams p, int ups) {
+__global__ __launch_bounds__(64 * KS * (epi_is_pair(EPI) ? 2 : 1)) void k_gemm_mfma(GemvParams p, int ups) {
     constexpr bool kPair = epi_is_pair(EPI);
     constexpr int NB = kPair ? 2 : 1;       // 16-row blocks per unit
     constexpr int NW = NB * KS;             // waves per workgroup
@@ -115,13 +120,14 @@ void k_gemm_mfma(GemvParams p, int ups) {
         const int sel = r0b / p.rows_per_sel;
         const int rb = blk ? r1b : r0b;         // this wave's block
         const uint16_t *W = reinterpret_cast<const uint16_t *>(p.W) + (int64_t)rb * K;
-        const float *xb = reinterpret_cast<const float *>(p.X) + (int64_t)sel * p.x_sel_stride;
+        const uint16_t *xb = reinterpret_cast<const uint16_t *>(p.X) + (int64_t)sel * p.x_sel_stride;
         bool xok[MT];
-        const float *xr[MT];
+        const uint16_t *xr[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-            xok[t] = t * 16 + li < p.M;
-            xr[t] = xb + (int64_t)(p.m0 + t * 16 + li) * K + 8 * lg;
+            // operand row t * 16 + li carries a piece of call row (t * 16 + li) % (8 * MT)
+            xok[t] = (t * 16 + li) % (8 * MT) < p.M;
+            xr[t] = xb + (int64_t)(t * 16 + li) * K + 8 * lg;
         }
         f32x4 acc[MT];
 #pragma unroll
@@ -139,45 +145,26 @@ void k_gemm_mfma(GemvParams p, int ups) {
         for (int tt = t0; tt < t1; ++tt) {
 #pragma unroll
             for (int i = 0; i < NL; ++i) *reinterpret_cast<uint4 *>(&tile[(2 * i + lrow) * kLD + lcol]) = wv[i];
-            // the first half of the tile's activation operands is requested
-            // before the next tile's weights, so the matrix cores wait only
-            // for them; the second half (float32 rows, L2 hits) follows the
-            // first half's matrix instructions, which keeps the activation
-            // registers at half a tile
+            // the tile's activation operands are requested before the next
+            // tile's weights, so the matrix cores wait only for them
             const int nsteps = min(kTK, K - tt * kTK) >> 5;     // 32-element MFMA steps in this tile
-            constexpr int HS = kTK / 64;                        // steps per half tile
-            uint4 xv[HS][MT][2];
-            auto load_x = [&](int h) {
+            uint4 xv[kTK / 32][MT];
 #pragma unroll
-                for (int s2 = 0; s2 < HS; ++s2)
+            for (int s2 = 0; s2 < kTK / 32; ++s2)
 #pragma unroll
-                    for (int t = 0; t < MT; ++t) {
-                        const bool ok = xok[t] && h * HS + s2 < nsteps;
-                        const float *xp = xr[t] + tt * kTK + 32 * (h * HS + s2);
-                        xv[s2][t][0] = ok ? ld16(xp) : make_uint4(0, 0, 0, 0);
-                        xv[s2][t][1] = ok ? ld16(xp + 4) : make_uint4(0, 0, 0, 0);
-                    }
-            };
-            auto mma = [&](int h) {
-#pragma unroll
-                for (int s2 = 0; s2 < HS; ++s2) {
-                    if (h * HS + s2 < nsteps) {
-                        const uint4 wt = *reinterpret_cast<const uint4 *>(&tile[li * kLD + 32 * (h * HS + s2) + 8 * lg]);
-#pragma unroll
-                        for (int t = 0; t < MT; ++t) {
-                            uint4 xh, xl;
-                            split2_bf16(xv[s2][t][0], xv[s2][t][1], xh, xl);
-                            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xh), as_bf16x8(wt), acc[t], 0, 0, 0);
-                            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xl), as_bf16x8(wt), acc[t], 0, 0, 0);
-                        }
-                    }
-                }
-            };
-            load_x(0);
+                for (int t = 0; t < MT; ++t)
+                    xv[s2][t] = (xok[t] && s2 < nsteps) ? ld16(xr[t] + tt * kTK + 32 * s2) : make_uint4(0, 0, 0, 0);
             if (tt + 1 < t1) load(tt + 1);
-            mma(0);
-            load_x(1);
-            mma(1);
+#pragma unroll
+            for (int s2 = 0; s2 < kTK / 32; ++s2) {
+                if (s2 < nsteps) {
+                    const uint4 wt = *reinterpret_cast<const uint4 *>(&tile[li * kLD + 32 * s2 + 8 * lg]);
+#pragma unroll
+                    for (int t = 0; t < MT; ++t)
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xv[s2][t]), as_bf16x8(wt), acc[t],
+                                                                          0, 0, 0);
+                }
+            }
         }
         if (u + (int)gridDim.x < p.n_units && t0 < t1) {
             int n0, n1;
@@ -214,8 +201,20 @@ void k_gemm_mfma(GemvParams p, int ups) {
             __syncthreads();
         }
         if (wave != 0) continue;
+        // hi and lo halves of each output: rows m and m + 8 of one tile sit in
+        // lane groups g and g + 2 (lanes l and l ^ 32); with two tiles they
+        // sit in the same lane and register of tiles 0 and 1
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
+        for (int j = 0; j < NB; ++j) {
+            if constexpr (MT == 1) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) res[j][0][r] += __shfl_xor(res[j][0][r], 32, kWave);
+            } else {
+                res[j][0] += res[j][1];
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < 1; ++t) {
             float ssv[4] = {0.f, 0.f, 0.f, 0.f};
             // one activation row at a time (keeps the epilogue's registers
             // out of the streaming loop's budget)
@@ -247,7 +246,7 @@ void k_gemm_mfma(GemvParams p, int ups) {
     if constexpr (EPI == EPI_LOGITS) {
         if (wave != 0) return;
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
+        for (int t = 0; t < 1; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float v = best_v[t][r];
@@ -288,7 +287,7 @@ hipError_t launch_mt(const GemvParams &p, dim3 g, int ks, int ups, hipStream_t s
 
 }  // namespace
 
-int gemm_mfma_max_rows() { return 32; }
+int gemm_mfma_max_rows() { return 16; }
 
 // One unit per workgroup, except sampling products, which keep a fixed grid
 // (their arg-max partials are per workgroup).
@@ -315,17 +314,21 @@ int gemm_mfma_splits(const GemvParams &p) {
 }
 
 bool gemm_mfma_supported(const GemvParams &p) {
-    if (p.K % 32 != 0 || p.M < 1 || p.M > 32 || p.rows_per_sel % 16 != 0) return false;
+    if (p.K % 32 != 0 || p.M < 1 || p.M > 16 || p.rows_per_sel % 16 != 0) return false;
     if (epi_is_pair(p.epi)) return p.pair_block % 32 == 0;
     return true;
 }
+
+int gemm_mfma_packed_rows(int M) { return M <= 8 ? 16 : 32; }
 
 hipError_t launch_gemm_mfma(const GemvParams &p, int grid, int ks, hipStream_t s) {
     if ((ks != 4 && ks != 8) || (epi_is_pair(p.epi) && ks != 4)) return hipErrorInvalidValue;
     // partial index of a residual writer: the unit within its set member
     const int ups = p.rows_per_sel / 16;
     if (epi_has_ss(p.epi) && p.n_norm_sel > 0 && grid != p.n_units) return hipErrorInvalidValue;
-    if (p.M <= 16) return launch_mt<1>(p, dim3(grid), ks, ups, s);
+    // every row of the call in one launch, operand packed as gemm_mfma_packed_rows says
+    if (p.m0 != 0 || p.M > 16) return hipErrorInvalidValue;
+    if (p.M <= 8) return launch_mt<1>(p, dim3(grid), ks, ups, s);
     return launch_mt<2>(p, dim3(grid), ks, ups, s);
 }
 

@@ -317,7 +317,7 @@ hipError_t launch_t(const GemvParams &p, int grid, int ks, hipStream_t s) {
 // row's values and gains are requested before the partials, so the two
 // memory round trips overlap (same arithmetic as x_norm8).
 template <typename T>
-__global__ __launch_bounds__(256) void k_norm_rows(GemvParams p, void *xn) {
+__global__ __launch_bounds__(256) void k_norm_rows(GemvParams p, void *xn, int packed) {
     const int m = blockIdx.y, sel = blockIdx.z;
     const int hrow = x_row(p, p.m0 + m);
     const int k = (blockIdx.x * 256 + threadIdx.x) * 8;
@@ -344,6 +344,19 @@ __global__ __launch_bounds__(256) void k_norm_rows(GemvParams p, void *xn) {
     }
     const float f[8] = {h0.x * inv * g0.x, h0.y * inv * g0.y, h0.z * inv * g0.z, h0.w * inv * g0.w,
                         h1.x * inv * g1.x, h1.y * inv * g1.y, h1.z * inv * g1.z, h1.w * inv * g1.w};
+    if (packed) {
+        // packed operand rows of the skinny matrix-core kernel (m0 = 0)
+        uint16_t hs[8], ls[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) split2_one(f[e], hs[e], ls[e]);
+        uint4 hv, lv;
+        __builtin_memcpy(&hv, hs, 16);
+        __builtin_memcpy(&lv, ls, 16);
+        uint16_t *o = reinterpret_cast<uint16_t *>(xn) + ((int64_t)sel * packed + m) * p.K + k;
+        *reinterpret_cast<uint4 *>(o) = hv;
+        *reinterpret_cast<uint4 *>(o + (int64_t)(packed / 2) * p.K) = lv;
+        return;
+    }
     float4 *o = reinterpret_cast<float4 *>(reinterpret_cast<float *>(xn) + ((int64_t)sel * p.Mtot + p.m0 + m) * p.K + k);
     o[0] = make_float4(f[0], f[1], f[2], f[3]);
     o[1] = make_float4(f[4], f[5], f[6], f[7]);
@@ -441,10 +454,11 @@ hipError_t launch_gemv(int dtype, const GemvParams &p, int grid, int ks, hipStre
     return dtype ? launch_t<uint16_t>(p, grid, ks, s) : launch_t<float>(p, grid, ks, s);
 }
 
-hipError_t launch_norm_rows(int dtype, const GemvParams &p, int n_sel, void *xn, hipStream_t s) {
+hipError_t launch_norm_rows(int dtype, const GemvParams &p, int n_sel, void *xn, int packed, hipStream_t s) {
+    if (packed && (p.m0 != 0 || 2 * p.M > packed || p.K % 8)) return hipErrorInvalidValue;
     dim3 grid((p.K + 2047) / 2048, p.M, n_sel);
-    if (dtype) hipLaunchKernelGGL(k_norm_rows<uint16_t>, grid, dim3(256), 0, s, p, xn);
-    else hipLaunchKernelGGL(k_norm_rows<float>, grid, dim3(256), 0, s, p, xn);
+    if (dtype) hipLaunchKernelGGL(k_norm_rows<uint16_t>, grid, dim3(256), 0, s, p, xn, packed);
+    else hipLaunchKernelGGL(k_norm_rows<float>, grid, dim3(256), 0, s, p, xn, packed);
     return hipGetLastError();
 }
 

@@ -102,9 +102,11 @@ std::string gemv_name(int dtype, const GemvParams &p) {
 }
 
 std::string mfma_name(int M, int epi, int ks) {
-    return std::string("k_gemm_mfma<") + (M <= 16 ? "1" : "2") + ", " + std::to_string(epi) + ", " +
+    return std::string("k_gemm_mfma<") + (M <= 8 ? "1" : "2") + ", " + std::to_string(epi) + ", " +
            std::to_string(ks) + ">";
 }
+
+constexpr bool epi_is_pair_host(int epi) { return epi == EPI_QKV_ROPE || epi == EPI_SILU_MUL; }
 
 // Workspace layout for R activation rows and sets of at most G layers.
 struct Carve {
@@ -126,10 +128,12 @@ Carve carve(const spec_model *m, int batch, int max_m, int G) {
     c.h = take(R * d * 4);
     c.h0 = take(R * d * 4);
     c.abuf = take((size_t)G * R * d * 4);
-    c.xn = take((size_t)G * R * d * 4);
+    // activation operands: float32 rows, or up to 32 packed bf16 rows
+    const size_t arow = R * 4 > 64 ? R * 4 : 64;
+    c.xn = take((size_t)G * d * arow);
     c.q = take((size_t)G * R * hq * hd * 4);
-    c.o = take((size_t)G * R * hq * hd * 4);
-    c.act = take(R * (size_t)m->d.d_ffn * 4);
+    c.o = take((size_t)G * hq * hd * arow);
+    c.act = take((size_t)m->d.d_ffn * arow);
     c.pacc = take((size_t)attention_split_max() * G * prow * hq * hd * 4);
     c.pml = take((size_t)attention_split_max() * G * prow * hq * 2 * 4);
     c.pval = take((size_t)batch * kPartialsMax * 4);
@@ -183,9 +187,45 @@ int tiled_min_rows() {
     return v;
 }
 
-// Weight-streaming product over the call's p.Mtot activation rows, chunked by
-// the kernel's row limit.  *parts_out: the sum-of-squares or sampling
-// partials each output row now has.
+// Which kernel serves a product over p.Mtot rows: the VALU GEMV (one row,
+// the float32 path, shapes the matrix-core kernels do not take), the skinny
+// matrix-core kernel (2..16 rows, one launch, packed bf16 hi/lo operand rows)
+// or the tiled matrix-core GEMM (17 rows and more, float32 operand rows).
+enum ProdPath { PP_VALU, PP_MFMA, PP_TILED };
+
+GemvParams mfma_params(const GemvParams &p) {
+    const bool pair = epi_is_pair_host(p.epi);
+    GemvParams q = p;
+    q.n_units = pair ? p.n_units * 2 / 32 : p.n_units * 2 / 16;   // 16-row blocks (pairs of them when paired)
+    q.m0 = 0;
+    q.M = p.Mtot;
+    return q;
+}
+
+ProdPath product_path(const spec_model *m, const GemvParams &p) {
+    if (m->d.dtype != SPEC_BF16) return PP_VALU;
+    const int Mtot = p.Mtot;
+    GemvParams t = p;
+    t.m0 = 0;
+    t.M = Mtot;
+    if (Mtot >= tiled_min_rows() && gemm_tiled_supported(t)) return PP_TILED;
+    const int rows = p.n_units * 2;
+    if (Mtot >= mfma_min_rows() && Mtot <= gemm_mfma_max_rows() && rows % (epi_is_pair_host(p.epi) ? 32 : 16) == 0 &&
+        gemm_mfma_supported(mfma_params(p)))
+        return PP_MFMA;
+    return PP_VALU;
+}
+
+// Rows of the packed operand a producer writes for this product (0: float32
+// rows).
+int packed_rows(const spec_model *m, const GemvParams &consumer) {
+    return product_path(m, consumer) == PP_MFMA ? gemm_mfma_packed_rows(consumer.Mtot) : 0;
+}
+
+// Weight-streaming product over the call's p.Mtot activation rows.  A plain
+// (X_PLAIN) operand must already be in the form product_path gives (packed
+// rows for the skinny matrix-core kernel, x_sel_stride in its elements).
+// *parts_out: the sum-of-squares or sampling partials each output row now has.
 hipError_t product(const Fwd &f, GemvParams p, int *parts_out = nullptr) {
     const spec_model *m = f.m;
     const int Mtot = p.Mtot;
@@ -193,25 +233,19 @@ hipError_t product(const Fwd &f, GemvParams p, int *parts_out = nullptr) {
     p.ss_sel_stride = f.c.ss_sel_stride;
     p.part_val = at<float>(f.ws, f.c.pval);
     p.part_idx = at<int32_t>(f.ws, f.c.pidx);
-    const bool pair = p.epi == EPI_QKV_ROPE || p.epi == EPI_SILU_MUL;
     const int rows = p.n_units * 2;
-    GemvParams q = p;
-    q.n_units = pair ? rows / 32 : rows / 16;   // 16-row blocks (pairs of them for paired epilogues)
-    q.M = Mtot < 32 ? Mtot : 32;
-    const bool mfma = m->d.dtype == SPEC_BF16 && Mtot >= mfma_min_rows() && rows % (pair ? 32 : 16) == 0 &&
-                      gemm_mfma_supported(q);
     const double wbytes = (double)rows * p.K * m->xs;   // every weight row once
-    GemvParams t = p;
-    t.m0 = 0;
-    t.M = Mtot;
-    if (m->d.dtype == SPEC_BF16 && Mtot >= tiled_min_rows() && gemm_tiled_supported(t)) {
-        // more than 16 rows: one tiled launch over every row
+    const ProdPath path = product_path(m, p);
+    if (path == PP_TILED) {
+        GemvParams t = p;
+        t.m0 = 0;
+        t.M = Mtot;
         if (parts_out) *parts_out = gemm_tiled_parts(t);
         double xbytes = (double)Mtot * p.K * 4;
         if (p.xmode == X_NORM) {
             const int n_sel = rows / p.rows_per_sel;
             void *xn = at<char>(f.ws, f.c.xn);
-            hipError_t e = launch_norm_rows(m->d.dtype, t, n_sel, xn, f.s);
+            hipError_t e = launch_norm_rows(m->d.dtype, t, n_sel, xn, 0, f.s);
             if (e != hipSuccess) return e;
             t.xmode = X_PLAIN;
             t.X = xn;
@@ -224,33 +258,28 @@ hipError_t product(const Fwd &f, GemvParams p, int *parts_out = nullptr) {
         ps.done(gemm_tiled_name(t, f.c.tpart_bytes), wbytes + xbytes, 2.0 * Mtot * rows * (double)p.K);
         return e;
     }
-    if (mfma) {
+    if (path == PP_MFMA) {
+        GemvParams q = mfma_params(p);
         const int grid = gemm_mfma_grid(q);
         const int ks = gemm_mfma_splits(q);
         if (parts_out) *parts_out = (p.epi == EPI_LOGITS) ? grid : p.rows_per_sel / 16;
-        const int mr = gemm_mfma_max_rows();
-        for (int m0 = 0; m0 < Mtot; m0 += mr) {
-            q.m0 = m0;
-            q.M = (Mtot - m0) < mr ? (Mtot - m0) : mr;
-            GemvParams r = q;
-            double xbytes = (double)q.M * p.K * 4;
-            if (p.xmode == X_NORM) {
-                // normalise once into xn, then stream the weights against it
-                const int n_sel = rows / p.rows_per_sel;
-                void *xn = at<char>(f.ws, f.c.xn);
-                hipError_t e = launch_norm_rows(m->d.dtype, q, n_sel, xn, f.s);
-                if (e != hipSuccess) return e;
-                r.xmode = X_PLAIN;
-                r.X = xn;   // rows (sel * Mtot + m0 + m); the kernel adds m0 * K
-                r.x_sel_stride = (int64_t)Mtot * p.K;
-                xbytes *= n_sel;
-            }
-            ProfScope ps(f.s);
-            hipError_t e = launch_gemm_mfma(r, grid, ks, f.s);
-            ps.done(mfma_name(q.M, p.epi, ks), wbytes + xbytes, 2.0 * q.M * rows * (double)p.K);
+        double xbytes = (double)Mtot * p.K * 4;
+        if (p.xmode == X_NORM) {
+            // normalise once into packed operand rows, then stream the weights
+            const int n_sel = rows / p.rows_per_sel;
+            const int pr = gemm_mfma_packed_rows(Mtot);
+            void *xn = at<char>(f.ws, f.c.xn);
+            hipError_t e = launch_norm_rows(m->d.dtype, q, n_sel, xn, pr, f.s);
             if (e != hipSuccess) return e;
+            q.xmode = X_PLAIN;
+            q.X = xn;
+            q.x_sel_stride = (int64_t)pr * p.K;
+            xbytes *= n_sel;
         }
-        return hipSuccess;
+        ProfScope ps(f.s);
+        hipError_t e = launch_gemm_mfma(q, grid, ks, f.s);
+        ps.done(mfma_name(Mtot, p.epi, ks), wbytes + xbytes, 2.0 * Mtot * rows * (double)p.K);
+        return e;
     }
     const int mr = gemv_max_rows();
     const int ks = gemv_splits(p, m->xs);
@@ -323,6 +352,14 @@ hipError_t run_stage(Fwd &f, int l0, int n, int mlp_mode, float *cos_out = nullp
     gp.rows = f.rows;
     if ((e = product(f, gp)) != hipSuccess) return e;
 
+    // the O product's operand format decides how the attention writes o
+    GemvParams go{};
+    go.Mtot = R; go.d = dm; go.eps = d.rms_eps;
+    go.W = layer_ptr(m->w.wo, l0, (size_t)dm * qd, xs);
+    go.K = qd; go.n_units = n * dm / 2; go.pair_block = 2; go.rows_per_sel = dm;
+    go.xmode = X_PLAIN; go.epi = EPI_ATTN_OUT;
+    const int o_packed = packed_rows(m, go);
+
     // 2. grouped attention
     AttnParams ap{};
     ap.q = q; ap.q_sel_stride = (int64_t)R * qd;
@@ -330,7 +367,7 @@ hipError_t run_stage(Fwd &f, int l0, int n, int mlp_mode, float *cos_out = nullp
     ap.hq = d.n_q_heads; ap.hkv = d.n_kv_heads; ap.hd = d.head_dim; ap.capacity = f.kv->capacity;
     ap.rows = f.rows; ap.max_pos = f.max_pos;
     ap.splits = attention_splits(d.dtype, d.head_dim, n, f.batch, d.n_q_heads, d.n_kv_heads, f.mseq, f.max_pos);
-    ap.o = o; ap.o_sel_stride = (int64_t)R * qd;
+    ap.o = o; ap.o_packed = o_packed; ap.o_sel_stride = (int64_t)(o_packed ? o_packed : R) * qd;
     ap.part_acc = at<float>(f.ws, f.c.pacc); ap.part_ml = at<float>(f.ws, f.c.pml); ap.Mtot = R;
     {
         // K/V rows of every set member, every sequence, up to max_pos (a bound)
@@ -343,12 +380,9 @@ hipError_t run_stage(Fwd &f, int l0, int n, int mlp_mode, float *cos_out = nullp
 
     // 3. grouped O projection: a_0 goes into the residual (sequential MLPs),
     //    the others wait in abuf; partial sums give the MLP inputs' RMS
-    gp = GemvParams{};
-    gp.Mtot = R; gp.d = dm; gp.eps = d.rms_eps;
-    gp.W = layer_ptr(m->w.wo, l0, (size_t)dm * qd, xs);
-    gp.K = qd; gp.n_units = n * dm / 2; gp.pair_block = 2; gp.rows_per_sel = dm;
-    gp.xmode = X_PLAIN; gp.X = o; gp.x_sel_stride = (int64_t)R * qd;
-    gp.epi = EPI_ATTN_OUT; gp.h = h; gp.h0 = h0; gp.par_mlp = par ? 1 : 0;
+    gp = go;
+    gp.X = o; gp.x_sel_stride = ap.o_sel_stride;
+    gp.h = h; gp.h0 = h0; gp.par_mlp = par ? 1 : 0;
     gp.out = abuf; gp.out_sel_stride = (int64_t)R * dm;
     gp.n_norm_sel = par ? n : 1;
     if ((e = product(f, gp, &grid)) != hipSuccess) return e;
@@ -366,15 +400,18 @@ hipError_t run_stage(Fwd &f, int l0, int n, int mlp_mode, float *cos_out = nullp
         gp.xss = ss + (size_t)si * f.c.ss_sel_stride; gp.xnparts = f.nparts[si];
         if (par) { gp.xh = h0; gp.xadd = abuf + (size_t)i * R * dm; }
         else gp.xh = h;
-        gp.epi = EPI_SILU_MUL; gp.act = act; gp.act_ld = d.d_ffn;
+        // the down product's operand format decides how the SiLU writes act
+        GemvParams gd{};
+        gd.Mtot = R; gd.d = dm; gd.eps = d.rms_eps;
+        gd.W = layer_ptr(m->w.w_down, l, (size_t)dm * d.d_ffn, xs);
+        gd.K = d.d_ffn; gd.n_units = dm / 2; gd.pair_block = 2; gd.rows_per_sel = dm;
+        gd.xmode = X_PLAIN; gd.X = act; gd.epi = EPI_RESID_ADD;
+        gp.epi = EPI_SILU_MUL; gp.act = act; gp.act_ld = d.d_ffn; gp.act_packed = packed_rows(m, gd);
         if ((e = product(f, gp)) != hipSuccess) return e;
 
-        gp = GemvParams{};
-        gp.Mtot = R; gp.d = dm; gp.eps = d.rms_eps;
-        gp.W = layer_ptr(m->w.w_down, l, (size_t)dm * d.d_ffn, xs);
-        gp.K = d.d_ffn; gp.n_units = dm / 2; gp.pair_block = 2; gp.rows_per_sel = dm;
-        gp.xmode = X_PLAIN; gp.X = act;
-        gp.epi = EPI_RESID_ADD; gp.h = h;
+        gp = gd;
+        gp.x_sel_stride = 0;
+        gp.h = h;
         // sequential: h += m_i + a_{i+1} (the next member's attention output);
         // parallel: h += a_i + m_i
         gp.add2 = par ? abuf + (size_t)i * R * dm : (i + 1 < n ? abuf + (size_t)(i + 1) * R * dm : nullptr);

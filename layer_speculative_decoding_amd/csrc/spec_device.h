@@ -50,6 +50,11 @@ __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<
 // nearest): the pair carries the value to within 2^-16 of its magnitude, and
 // each piece times a bfloat16 weight is exact in float32, so two products
 // replace one float32 product at that precision.
+__device__ __forceinline__ void split2_one(float x, uint16_t &hi, uint16_t &lo) {
+    const uint32_t u = __float_as_uint(x);
+    hi = (uint16_t)(u >> 16);
+    lo = f32_to_bf16(x - __uint_as_float(u & 0xFFFF0000u));
+}
 __device__ __forceinline__ void split2_bf16(const uint4 &a, const uint4 &b, uint4 &hi, uint4 &lo) {
     const uint32_t x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     uint32_t h[4], l[4];

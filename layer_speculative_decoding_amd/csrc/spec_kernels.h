@@ -58,6 +58,8 @@ struct GemvParams {
     int64_t xgain_stride;
     const float *xss;     // X_NORM: sum-of-squares partials of residual row hrow at
     int xnparts;          //   xss[hrow * xnparts + 0 .. xnparts-1] (summed in order)
+    int act_packed;       // SILU_MUL: 0 -> float32 act rows; PR -> packed bf16
+                          //   operand rows (hi at row m, lo at row m + PR / 2)
     int xgather_mseq;     // > 0: activation row m reads residual row
     const int32_t *xgather_ntok;   //   m * mseq + ntok[m] - 1 (last valid row)
     const float *bias;    // [rows] or NULL
@@ -108,7 +110,10 @@ int gemv_grid(const GemvParams &p, int ks);
 // Operand mode of the GEMV instance a launch uses (0 plain rows, 1 normalised
 // rows staged in LDS, 2 normalised per step): the last template argument.
 int gemv_operand_mode(int dtype, const GemvParams &p);
-// MFMA skinny GEMM (bf16), M <= 32 per launch, K a multiple of 32.  Units:
+// MFMA skinny GEMM (bf16) over all M <= 16 rows of a call in one launch (m0
+// = 0), K a multiple of 32.  X is the packed operand: gemm_mfma_packed_rows(M)
+// bf16 rows per set member, hi(x_m) in row m and lo(x_m) in row m + PR / 2
+// (see split2_bf16; PR = 16 for M <= 8, else 32).  Units:
 // pairs of 16-row blocks for the paired epilogues (QKV RoPE, SiLU; n_units =
 // rows / 32, pair_block a multiple of 32), single 16-row blocks otherwise
 // (n_units = rows / 16).  ks waves per workgroup (4, 8 or 16).  Residual
@@ -130,9 +135,12 @@ size_t gemm_tiled_part_bytes();
 std::string gemm_tiled_name(const GemvParams &p, size_t part_bytes);   // kernel instance, for measurement
 // X_NORM operands written once as float32 rows xn[sel][m][K] for rows
 // m0 .. m0 + M - 1 (the matrix-core products then read them plainly).
-hipError_t launch_norm_rows(int dtype, const GemvParams &p, int n_sel, void *xn, hipStream_t s);
+// packed > 0: the packed operand of the skinny matrix-core kernel instead
+// (bf16 rows [sel][packed][K], hi of row m at m, lo at m + packed / 2).
+hipError_t launch_norm_rows(int dtype, const GemvParams &p, int n_sel, void *xn, int packed, hipStream_t s);
 bool gemm_mfma_supported(const GemvParams &p);
 int gemm_mfma_max_rows();
+int gemm_mfma_packed_rows(int M);
 int gemm_mfma_grid(const GemvParams &p);
 int gemm_mfma_splits(const GemvParams &p);
 
@@ -167,7 +175,10 @@ struct AttnParams {
     RowMap rows;
     int max_pos;           // host bound of positions in this call
     int splits;
-    void *o;               // [g][Mtot][hq*hd] float32
+    void *o;               // [g][Mtot][hq*hd] float32, or o_packed > 0: packed
+                           // bf16 operand rows [g][o_packed][hq*hd] (hi at row
+                           // m, lo at row m + o_packed / 2)
+    int o_packed;
     int64_t o_sel_stride;
     float *part_acc;       // [splits][g][Mtot][hq][hd]
     float *part_ml;        // [splits][g][Mtot][hq][2]
