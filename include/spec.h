@@ -163,6 +163,27 @@ spec_status spec_draft_group_step(const spec_model *draft, const spec_kv *kv,
                                   int32_t *token_out, int token_out_stride,
                                   void *workspace, size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the draft
+ * step of spec_draft_group_step, same arguments and results, with the
+ * workspace taken from a scratch array of SPEC_SCRATCH_BYTES that the library
+ * holds in every GPU's memory from the first such call on that GPU until the
+ * process ends.  The call allocates nothing and launches the same kernels.
+ * Errors as for spec_draft_group_step; SPEC_ERR_WORKSPACE (nothing launched)
+ * if spec_workspace_bytes(draft, batch, 1, largest set of the plan) exceeds
+ * SPEC_SCRATCH_BYTES; SPEC_ERR_HIP if the scratch array's address cannot be
+ * obtained.  Every call on one GPU uses that GPU's one array, which keeps
+ * the last call's contents (the step needs no initial contents): calls that
+ * overlap on one GPU (several streams or host threads) race. */
+#define SPEC_SCRATCH_BYTES ((size_t)32 << 20)
+spec_status spec_draft_group_step_noalloc(const spec_model *draft, const spec_kv *kv,
+                                          const int32_t *plan_offsets, int n_stages, int flags,
+                                          int batch, const int32_t *tokens, int tokens_stride,
+                                          const int32_t *positions, int max_pos,
+                                          float inv_temperature, uint64_t seed,
+                                          float *logits_out, int64_t logits_stride,
+                                          int32_t *token_out, int token_out_stride, void *stream);
+
 /* Cosine-similarity diagnostic of the fuzzy inputs (review thread, the
  * discussion of Table 3: the similarity of the hidden states a layer-parallel
  * set feeds its attentions to the ones a sequential pass would feed, measured

@@ -26,7 +26,8 @@ EXPORTS = ("spec_model_create", "spec_model_destroy", "spec_check_pair", "spec_d
            "spec_workspace_bytes", "spec_draft_group_step", "spec_calibrate_kv", "spec_verify_forward",
            "spec_accept_workspace_bytes", "spec_accept_resample", "spec_status_string", "spec_last_error",
            "spec_version", "spec_profile_enable", "spec_profile_reset", "spec_profile_collect",
-           "spec_profile_entry", "spec_draft_attention_cosine")
+           "spec_profile_entry", "spec_draft_attention_cosine", "spec_draft_group_step_noalloc")
+SPEC_SCRATCH_BYTES = 32 << 20
 
 
 class SpecError(RuntimeError):
@@ -70,6 +71,8 @@ def load() -> C.CDLL:
         "spec_workspace_bytes": (sz, [vp, i32, i32, i32]),
         "spec_draft_group_step": (i32, [vp, C.POINTER(KV), C.POINTER(C.c_int32), i32, i32, i32, vp, i32, vp, i32,
                                         f32, u64, vp, i64, vp, i32, vp, sz, vp]),
+        "spec_draft_group_step_noalloc": (i32, [vp, C.POINTER(KV), C.POINTER(C.c_int32), i32, i32, i32, vp, i32, vp,
+                                                i32, f32, u64, vp, i64, vp, i32, vp]),
         "spec_calibrate_kv": (i32, [vp, C.POINTER(KV), i32, vp, i32, vp, vp, i32, i32, f32, u64, vp, i64, vp, i32, vp,
                                     sz, vp]),
         "spec_verify_forward": (i32, [vp, C.POINTER(KV), i32, vp, vp, i32, i32, vp, vp, sz, vp]),

@@ -106,6 +106,19 @@ def spec_draft_group_step(model: SpecModel, kv: KVCache, plan_offsets, flags: in
         logits_stride, _ptr(token_out), token_out_stride, _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
+def spec_draft_group_step_noalloc(model: SpecModel, kv: KVCache, plan_offsets, flags: int, batch: int,
+                                  tokens: torch.Tensor, tokens_stride: int, positions: torch.Tensor, max_pos: int,
+                                  inv_temperature: float, seed: int, logits_out: Optional[torch.Tensor],
+                                  logits_stride: int, token_out: torch.Tensor, token_out_stride: int, stream=None):
+    """spec_draft_group_step without a workspace argument: the library's
+    per-GPU scratch array serves instead (nothing is allocated)."""
+    plan = _plan_array(plan_offsets)
+    check(load().spec_draft_group_step_noalloc(
+        model.handle, C.byref(kv.c), plan, len(plan_offsets) - 1, flags, batch, _ptr(tokens), tokens_stride,
+        _ptr(positions), max_pos, C.c_float(inv_temperature), C.c_uint64(seed), _ptr(logits_out),
+        logits_stride, _ptr(token_out), token_out_stride, _stream(stream)))
+
+
 def spec_draft_attention_cosine(model: SpecModel, kv: KVCache, plan_offsets, batch: int, tokens: torch.Tensor,
                                 tokens_stride: int, positions: torch.Tensor, max_pos: int, cos_out: torch.Tensor,
                                 cos_stride: int, workspace: torch.Tensor, stream=None):

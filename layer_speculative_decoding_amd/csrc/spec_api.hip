@@ -462,6 +462,32 @@ spec_status check_model(const spec_model *m, const spec_kv *kv, int batch) {
     return SPEC_OK;
 }
 
+// Scratch array of the entry point that allocates nothing: one copy per GPU
+// (the code object is loaded on each device), its device address looked up
+// once per device with that device current.  Host code never passes the
+// array's name itself to a kernel (on the host it only stands for the
+// symbol), always the looked-up address.
+static __device__ __align__(256) unsigned char scratch[SPEC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+std::vector<void *> g_scratch_ptr;   // by device ordinal
+
+spec_status scratch_address(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (dev >= (int)g_scratch_ptr.size()) g_scratch_ptr.resize(dev + 1, nullptr);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(SPEC_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SPEC_OK;
+}
+
 spec_status check_ws(const spec_model *m, int batch, int max_m, int G, void *ws, size_t ws_bytes) {
     const size_t need = spec_workspace_bytes(m, batch, max_m, G);
     if (!ws || ws_bytes < need)
@@ -680,6 +706,28 @@ spec_status spec_draft_group_step(const spec_model *draft, const spec_kv *kv, co
                  token_out, token_out_stride);
     if (e != hipSuccess) return hip_fail(e, "draft head");
     return SPEC_OK;
+}
+
+spec_status spec_draft_group_step_noalloc(const spec_model *draft, const spec_kv *kv, const int32_t *plan_offsets,
+                                          int n_stages, int flags, int batch, const int32_t *tokens, int tokens_stride,
+                                          const int32_t *positions, int max_pos, float inv_temperature, uint64_t seed,
+                                          float *logits_out, int64_t logits_stride, int32_t *token_out,
+                                          int token_out_stride, void *stream) {
+    // the size check needs the plan's largest set; the full argument checks
+    // run again in spec_draft_group_step before anything is launched
+    spec_status st = check_model(draft, kv, batch);
+    if (st) return st;
+    int G = 1;
+    if ((st = check_plan(draft, plan_offsets, n_stages, flags, &G))) return st;
+    const size_t need = spec_workspace_bytes(draft, batch, 1, G);
+    if (need > SPEC_SCRATCH_BYTES)
+        return fail(SPEC_ERR_WORKSPACE, "draft step needs %zu bytes of workspace > scratch array %zu", need,
+                    (size_t)SPEC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if ((st = scratch_address(&ws))) return st;
+    return spec_draft_group_step(draft, kv, plan_offsets, n_stages, flags, batch, tokens, tokens_stride, positions,
+                                 max_pos, inv_temperature, seed, logits_out, logits_stride, token_out,
+                                 token_out_stride, ws, SPEC_SCRATCH_BYTES, stream);
 }
 
 static spec_status precise_forward(const spec_model *m, const spec_kv *kv, int batch, const int32_t *tokens,

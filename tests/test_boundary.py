@@ -151,3 +151,25 @@ def test_status_strings():
     lib = L.load()
     for code in _lib.STATUS:
         assert lib.spec_status_string(code)
+
+
+def test_noalloc_draft_step_rejects_before_touching_the_gpu():
+    """The entry point that allocates nothing rejects plans and shapes whose
+    workspace would not fit its scratch array, on the host, before any HIP
+    call (there is no GPU here)."""
+    lib = L.load()
+    big = _desc(n_layers=10, d_model=8192, n_q_heads=64, n_kv_heads=8, head_dim=128, d_ffn=28672, vocab=1024,
+                dtype=1)
+    _, h = _create(big, _fake_weights())
+    kv = _kv(cap=64, batch=8)
+    plan = [0, 1, 9, 10]                            # one set of 8 layers
+    need = lib.spec_workspace_bytes(h, 8, 1, 8)
+    assert need > _lib.SPEC_SCRATCH_BYTES
+    arr = (C.c_int32 * len(plan))(*plan)
+    st = lib.spec_draft_group_step_noalloc(h, C.byref(kv), arr, 3, 0, 8, 0x4000, 1, 0x5000, 3, 0.0, 0, None, 0,
+                                           0x7000, 1, None)
+    assert st == -6
+    assert b"scratch" in lib.spec_last_error()
+    bad = (C.c_int32 * 3)(0, 2, 9)                  # does not cover the last layer
+    assert lib.spec_draft_group_step_noalloc(h, C.byref(kv), bad, 2, 0, 8, 0x4000, 1, 0x5000, 3, 0.0, 0, None, 0,
+                                             0x7000, 1, None) == -4
