@@ -285,6 +285,9 @@ def main():
     ap.add_argument("--separate-calibration", action="store_true",
                     help="ablation: the other reading of the calibration (all k drafts from fuzzy steps, then a "
                          "precise pass over the committed fuzzy tokens)")
+    ap.add_argument("--mlp-parallel", action="store_true",
+                    help="the parallel reading of the set's MLPs (every MLP fed from the set input; the set's "
+                         "gate/up and down projections as one product each)")
     ap.add_argument("--no-calibration", action="store_true",
                     help="ablation: keep the fuzzy KV of accepted drafts, run only the emitted token precisely")
     ap.add_argument("--n1-compare", action="store_true",
@@ -372,8 +375,9 @@ def main():
     cap = P + rounds_cap * (k + 1) + k + 2
     prompts = make_prompts(cfg.draft.vocab, P, cfg.batch, cfg.prompt_seed)
     inv_t = 0.0 if args.temperature == 0 else 1.0 / args.temperature
+    mlp_mode = 1 if args.mlp_parallel else 0
     dec = SpecDecoder(cfg.draft, dw, cfg.base, bw, cfg.batch, cap, k, offs, P, inv_t, cfg.sample_seed,
-                      calibrate=not args.no_calibration, separate=args.separate_calibration)
+                      mlp_mode=mlp_mode, calibrate=not args.no_calibration, separate=args.separate_calibration)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
     e0, e1 = ev(), ev()
@@ -615,7 +619,7 @@ def main():
     n1 = None
     if args.n1_compare:
         d1 = SpecDecoder(cfg.draft, dw, cfg.base, bw, cfg.batch, cap, k, seq_offs, P, inv_t, cfg.sample_seed,
-                         calibrate=not args.no_calibration, separate=args.separate_calibration)
+                         mlp_mode=mlp_mode, calibrate=not args.no_calibration, separate=args.separate_calibration)
         d1.prefill(prompts)
         for _ in range(W):
             d1.step(big)
@@ -663,7 +667,8 @@ def main():
         "config": {"workload": f"{cfg.name}: draft {cfg.draft.n_layers}L d{cfg.draft.d_model} -> base "
                                f"{cfg.base.n_layers}L d{cfg.base.d_model}, V {cfg.draft.vocab}, P {P}, k {k}, "
                                f"N {N}, batch {cfg.batch}, T {args.temperature}"
-                               + (", no KV calibration" if args.no_calibration else ""),
+                               + (", no KV calibration" if args.no_calibration else "")
+                               + (", parallel MLPs" if args.mlp_parallel else ""),
                    "plan": offs, "global_batch": cfg.batch, "seq_len": P},
         "acceptance_rate": round(acc_rate, 4),
         "draft_step_us": round(d_step_ms * 1e3, 1),

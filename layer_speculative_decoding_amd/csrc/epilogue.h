@@ -36,9 +36,9 @@ __device__ __forceinline__ int x_row(const GemvParams &p, int gm) {
 // 1/rms of residual row hrow from its p.xnparts sum-of-squares partials.
 // Lane i adds partials i, i + 64, ... in that order (eight loads in flight),
 // then a fixed xor tree: every caller forms the same bits.  Whole wave.
-__device__ __forceinline__ float row_inv_rms(const GemvParams &p, int hrow) {
+__device__ __forceinline__ float row_inv_rms(const GemvParams &p, int hrow, int sel = 0) {
     const int lane = threadIdx.x & 63;
-    const float *src = p.xss + (int64_t)hrow * p.xnparts;
+    const float *src = p.xss + (int64_t)sel * p.xss_sel_stride + (int64_t)hrow * p.xnparts;
     const int n = p.xnparts;
     float s = 0.f;
     int i = lane;
@@ -127,17 +127,20 @@ __device__ __forceinline__ void epi_pair(const GemvParams &p, int u, int r0, int
             c[j + hd / 2] = S::from_f32(y1);
         }
     } else if constexpr (EPI == EPI_SILU_MUL) {
+        // column = gate row within its set member's [gate; up] block
+        const int64_t col = r0 - (int64_t)sel * p.rows_per_sel + (int64_t)sel * p.act_sel_stride;
         const float a = silu(y0) * y1;
         if (p.act_packed) {
             // packed operand rows of the down product's matrix-core kernel
             uint16_t hi, lo;
             split2_one(a, hi, lo);
             uint16_t *a16 = reinterpret_cast<uint16_t *>(p.act);
-            a16[(int64_t)gm * p.act_ld + u] = hi;
-            a16[(int64_t)(gm + p.act_packed / 2) * p.act_ld + u] = lo;
+            a16[(int64_t)gm * p.act_ld + col] = hi;
+            a16[(int64_t)(gm + p.act_packed / 2) * p.act_ld + col] = lo;
         } else {
-            reinterpret_cast<float *>(p.act)[(int64_t)gm * p.act_ld + u] = a;
+            reinterpret_cast<float *>(p.act)[(int64_t)gm * p.act_ld + col] = a;
         }
+        (void)u;
     }
 }
 
@@ -163,7 +166,10 @@ __device__ __forceinline__ void epi_row(const GemvParams &p, int r, int sel, int
     } else if constexpr (EPI == EPI_RESID_ADD) {
         float *h = p.h + (int64_t)gm * p.d;
         float v = h[rl] + y;
-        if (p.add2) v += p.add2[(int64_t)gm * p.d + rl];
+        if (p.add2) {
+            const int na = p.n_add2 > 1 ? p.n_add2 : 1;
+            for (int j = 0; j < na; ++j) v += p.add2[j * p.add2_sel_stride + (int64_t)gm * p.d + rl];
+        }
         h[rl] = v;
         ssv = fmaf(v, v, ssv);
     } else if constexpr (EPI == EPI_ATTN_OUT) {

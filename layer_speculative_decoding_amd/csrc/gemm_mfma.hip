@@ -67,7 +67,7 @@ __device__ __forceinline__ void group16_argmax(float &v, int &i) {
 // MT: 16-row operand tiles (1: M <= 8, 2: M <= 16).  A unit has NB
 // 16-row blocks (2 for the paired epilogues, else 1); the workgroup runs KS
 // waves per block, wave w streaming block w / KS over K part w % KS.
-template <int MT, int EPI, int KS>
+template <int MT, int EPI, int KS, bool SEG = false>
 __global__ __launch_bounds__(64 * KS * (epi_is_pair(EPI) ? 2 : 1)) void k_gemm_mfma(GemvParams p, int ups) {
     constexpr bool kPair = epi_is_pair(EPI);
     constexpr int NB = kPair ? 2 : 1;       // 16-row blocks per unit
@@ -114,12 +114,26 @@ __global__ __launch_bounds__(64 * KS * (epi_is_pair(EPI) ? 2 : 1)) void k_gemm_m
     // loop-local form at 136 VGPRs, one workgroup per CU).
     uint4 wv[NL];
     bool have_first = false;   // wv already holds this unit's first tile
+    // K in segments (set members' matrices side by side; Ks a multiple of the
+    // tile): where tile tt starts within a row of a segmented layout
+    // (SEG instances: the down projection over a set's members)
+    constexpr bool kSegOk = SEG;
+    const int Ks = (kSegOk && p.kseg > 1) ? K / p.kseg : K;
+    auto tile_off = [&](int tt, int64_t seg_stride) -> int64_t {
+        if constexpr (!kSegOk) {
+            return tt * kTK;
+        } else {
+            if (p.kseg <= 1) return tt * kTK;
+            const int k = tt * kTK, sg = k / Ks;
+            return sg * seg_stride + (k - sg * Ks);
+        }
+    };
     for (int u = blockIdx.x; u < p.n_units; u += gridDim.x) {
         int r0b, r1b;
         unit_blocks(u, r0b, r1b);
         const int sel = r0b / p.rows_per_sel;
         const int rb = blk ? r1b : r0b;         // this wave's block
-        const uint16_t *W = reinterpret_cast<const uint16_t *>(p.W) + (int64_t)rb * K;
+        const uint16_t *W = reinterpret_cast<const uint16_t *>(p.W) + (int64_t)rb * Ks;
         const uint16_t *xb = reinterpret_cast<const uint16_t *>(p.X) + (int64_t)sel * p.x_sel_stride;
         bool xok[MT];
         const uint16_t *xr[MT];
@@ -127,17 +141,18 @@ __global__ __launch_bounds__(64 * KS * (epi_is_pair(EPI) ? 2 : 1)) void k_gemm_m
         for (int t = 0; t < MT; ++t) {
             // operand row t * 16 + li carries a piece of call row (t * 16 + li) % (8 * MT)
             xok[t] = (t * 16 + li) % (8 * MT) < p.M;
-            xr[t] = xb + (int64_t)(t * 16 + li) * K + 8 * lg;
+            xr[t] = xb + (int64_t)(t * 16 + li) * Ks + 8 * lg;
         }
         f32x4 acc[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         auto load_from = [&](const uint16_t *Wr, int tt) {
-            const int k = tt * kTK + lcol;
+            const bool in = tt * kTK + lcol < K;
+            const uint16_t *wt0 = Wr + tile_off(tt, p.w_seg_stride) + lcol;
 #pragma unroll
             for (int i = 0; i < NL; ++i)
-                wv[i] = k < K ? ld16_stream(Wr + (int64_t)(2 * i + lrow) * K + k) : make_uint4(0, 0, 0, 0);
+                wv[i] = in ? ld16_stream(wt0 + (int64_t)(2 * i + lrow) * Ks) : make_uint4(0, 0, 0, 0);
         };
         auto load = [&](int tt) { load_from(W, tt); };
         if (t0 < t1 && !have_first) load(t0);
@@ -149,11 +164,12 @@ __global__ __launch_bounds__(64 * KS * (epi_is_pair(EPI) ? 2 : 1)) void k_gemm_m
             // tile's weights, so the matrix cores wait only for them
             const int nsteps = min(kTK, K - tt * kTK) >> 5;     // 32-element MFMA steps in this tile
             uint4 xv[kTK / 32][MT];
+            const int64_t xo = tile_off(tt, p.x_seg_stride);
 #pragma unroll
             for (int s2 = 0; s2 < kTK / 32; ++s2)
 #pragma unroll
                 for (int t = 0; t < MT; ++t)
-                    xv[s2][t] = (xok[t] && s2 < nsteps) ? ld16(xr[t] + tt * kTK + 32 * s2) : make_uint4(0, 0, 0, 0);
+                    xv[s2][t] = (xok[t] && s2 < nsteps) ? ld16(xr[t] + xo + 32 * s2) : make_uint4(0, 0, 0, 0);
             if (tt + 1 < t1) load(tt + 1);
 #pragma unroll
             for (int s2 = 0; s2 < kTK / 32; ++s2) {
@@ -169,7 +185,7 @@ __global__ __launch_bounds__(64 * KS * (epi_is_pair(EPI) ? 2 : 1)) void k_gemm_m
         if (u + (int)gridDim.x < p.n_units && t0 < t1) {
             int n0, n1;
             unit_blocks(u + gridDim.x, n0, n1);
-            load_from(reinterpret_cast<const uint16_t *>(p.W) + (int64_t)(blk ? n1 : n0) * K, t0);
+            load_from(reinterpret_cast<const uint16_t *>(p.W) + (int64_t)(blk ? n1 : n0) * Ks, t0);
             have_first = true;
         }
         // fixed-order sum of the K parts of each block by wave 0; C layout:
@@ -266,6 +282,13 @@ void launch_epi(const GemvParams &p, dim3 g, int ks, int ups, hipStream_t s) {
     if constexpr (epi_is_pair(EPI)) {
         hipLaunchKernelGGL((k_gemm_mfma<MT, EPI, 4>), g, dim3(512), 0, s, p, ups);
     } else {
+        if constexpr (EPI == EPI_RESID_ADD) {
+            if (p.kseg > 1) {
+                if (ks == 4) hipLaunchKernelGGL((k_gemm_mfma<MT, EPI, 4, true>), g, dim3(256), 0, s, p, ups);
+                else hipLaunchKernelGGL((k_gemm_mfma<MT, EPI, 8, true>), g, dim3(512), 0, s, p, ups);
+                return;
+            }
+        }
         if (ks == 4) hipLaunchKernelGGL((k_gemm_mfma<MT, EPI, 4>), g, dim3(256), 0, s, p, ups);
         else hipLaunchKernelGGL((k_gemm_mfma<MT, EPI, 8>), g, dim3(512), 0, s, p, ups);
     }
@@ -315,6 +338,7 @@ int gemm_mfma_splits(const GemvParams &p) {
 
 bool gemm_mfma_supported(const GemvParams &p) {
     if (p.K % 32 != 0 || p.M < 1 || p.M > 16 || p.rows_per_sel % 16 != 0) return false;
+    if (p.kseg > 1 && (p.K % p.kseg != 0 || (p.K / p.kseg) % kTK != 0)) return false;
     if (epi_is_pair(p.epi)) return p.pair_block % 32 == 0;
     return true;
 }

@@ -40,12 +40,14 @@ constexpr int kUnroll = 4;
 // products of the stored weights.
 constexpr int kStageBytes = 32768;
 
-enum : int { XM_PLAIN = 0, XM_STAGED = 1, XM_DIRECT = 2 };
+// plain rows, normalised rows staged in LDS, normalised per step, plain rows
+// with K in segments (the down projection over a set's members)
+enum : int { XM_PLAIN = 0, XM_STAGED = 1, XM_DIRECT = 2, XM_SEG = 3 };
 
 template <typename T, int MR, int EPI, int XM>
 __global__ __launch_bounds__(256) void k_gemv(GemvParams p, int KS) {
     using S = Store<T>;
-    constexpr bool kNorm = XM != XM_PLAIN;
+    constexpr bool kNorm = XM == XM_STAGED || XM == XM_DIRECT;
     constexpr bool staged = XM == XM_STAGED;
     constexpr int E = S::kPer16;
     constexpr bool kPair = epi_is_pair(EPI);
@@ -79,6 +81,16 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, int KS) {
         r1 = r0 + half;
         sel = r0 / p.rows_per_sel;
     };
+    // K in segments (set members' matrices side by side): segment of k and
+    // the offset of element k of row r
+    constexpr bool kSegOk = XM == XM_SEG;
+    const int Ks = (kSegOk && p.kseg > 1) ? K / p.kseg : K;
+    auto seg_of = [&](int k) {
+        int sg = 0;
+#pragma unroll
+        for (int i = 1; i < kMaxSel; ++i) sg += (i < p.kseg && k >= i * Ks) ? 1 : 0;
+        return sg;
+    };
     auto load_w = [&](const T *w0, const T *w1, int k0, uint4 (&wa)[kUnroll], uint4 (&wb)[kUnroll]) {
 #pragma unroll
         for (int q = 0; q < kUnroll; ++q) {
@@ -86,8 +98,14 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, int KS) {
             wa[q] = make_uint4(0, 0, 0, 0);
             wb[q] = make_uint4(0, 0, 0, 0);
             if (k < ke) {
-                wa[q] = ld16_stream(w0 + k);
-                wb[q] = ld16_stream(w1 + k);
+                int64_t off = k;
+                if (kSegOk && p.kseg > 1) {
+                    // w0 / w1 hold row * Ks; segment sg starts sg * w_seg_stride further
+                    const int sg = seg_of(k);
+                    off = sg * p.w_seg_stride + (k - sg * Ks);
+                }
+                wa[q] = ld16_stream(w0 + off);
+                wb[q] = ld16_stream(w1 + off);
             }
         }
     };
@@ -99,7 +117,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, int KS) {
     if (kNorm && blockIdx.x * upb + slot < p.n_units && kb < ke) {
         int r0, r1, sel;
         unit_rows(blockIdx.x * upb + slot, r0, r1, sel);
-        load_w(reinterpret_cast<const T *>(p.W) + (int64_t)r0 * K, reinterpret_cast<const T *>(p.W) + (int64_t)r1 * K,
+        load_w(reinterpret_cast<const T *>(p.W) + (int64_t)r0 * Ks, reinterpret_cast<const T *>(p.W) + (int64_t)r1 * Ks,
                kb, wa, wb);
         have_pf = true;
     }
@@ -116,10 +134,13 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, int KS) {
 #pragma unroll
                 for (int m = 0; m < MR; ++m) {
                     if (m >= p.M) continue;
+                    // members with their own residual rows (parallel MLPs) have their own
+                    // RMS (staged operands only: the host sends such products here)
+                    const float iv = p.xss_sel_stride ? row_inv_rms(p, hrow[m], sel) : inv[m];
                     for (int k = threadIdx.x * E; k < K; k += 256 * E) {
                         float f[E];
-                        if constexpr (E == 8) x_norm8(p, sel, hrow[m], k, inv[m], f);
-                        else x_norm4(p, sel, hrow[m], k, inv[m], f);
+                        if constexpr (E == 8) x_norm8(p, sel, hrow[m], k, iv, f);
+                        else x_norm4(p, sel, hrow[m], k, iv, f);
 #pragma unroll
                         for (int e = 0; e < E; ++e) xs[(sel * MR + m) * K + k + e] = f[e];
                     }
@@ -135,10 +156,11 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, int KS) {
         int r0 = 0, r1 = 0, sel = 0;
         if (active) {
             unit_rows(u, r0, r1, sel);
-            const T *w0 = reinterpret_cast<const T *>(p.W) + (int64_t)r0 * K;
-            const T *w1 = reinterpret_cast<const T *>(p.W) + (int64_t)r1 * K;
-            const float *xp = reinterpret_cast<const float *>(p.X) + (int64_t)sel * p.x_sel_stride + (int64_t)p.m0 * K;
+            const T *w0 = reinterpret_cast<const T *>(p.W) + (int64_t)r0 * Ks;
+            const T *w1 = reinterpret_cast<const T *>(p.W) + (int64_t)r1 * Ks;
+            const float *xp = reinterpret_cast<const float *>(p.X) + (int64_t)sel * p.x_sel_stride + (int64_t)p.m0 * Ks;
             const float *xl = xs + (int64_t)sel * MR * K;
+
             float a0[MR], a1[MR];
 #pragma unroll
             for (int m = 0; m < MR; ++m) { a0[m] = 0.f; a1[m] = 0.f; }
@@ -156,9 +178,13 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, int KS) {
                         for (int e = 0; e < E; ++e) xo[q][m][e] = 0.f;
                         if (m >= p.M || k >= ke) continue;
                         if constexpr (!kNorm) {
+                            int64_t off = (int64_t)m * Ks + k;
+                            if (kSegOk && p.kseg > 1) {
+                                const int sg = seg_of(k);
+                                off = sg * p.x_seg_stride + (int64_t)m * Ks + (k - sg * Ks);
+                            }
 #pragma unroll
-                            for (int e = 0; e < E; e += 4)
-                                Store<float>::unpack(ld16(xp + (int64_t)m * K + k + e), xo[q][m] + e);
+                            for (int e = 0; e < E; e += 4) Store<float>::unpack(ld16(xp + off + e), xo[q][m] + e);
                         } else if constexpr (staged) {
 #pragma unroll
                             for (int e = 0; e < E; e += 4)
@@ -295,7 +321,8 @@ hipError_t launch_t(const GemvParams &p, int grid, int ks, hipStream_t s) {
         break;
     case EPI_RESID_ADD:
         if (nrm) return hipErrorInvalidValue;
-        launch_tex<T, EPI_RESID_ADD, XM_PLAIN>(p, grid, ks, s);
+        if (p.kseg > 1) launch_tex<T, EPI_RESID_ADD, XM_SEG>(p, grid, ks, s);
+        else launch_tex<T, EPI_RESID_ADD, XM_PLAIN>(p, grid, ks, s);
         break;
     case EPI_LOGITS:
         launch_ten<T, EPI_LOGITS>(p, grid, ks, nrm, s);
@@ -336,7 +363,7 @@ __global__ __launch_bounds__(256) void k_norm_rows(GemvParams p, void *xn, int p
             a1 = *reinterpret_cast<const float4 *>(a + 4);
         }
     }
-    const float inv = row_inv_rms(p, hrow);   // whole wave
+    const float inv = row_inv_rms(p, hrow, sel);   // whole wave
     if (!live) return;
     if (p.xadd) {
         h0.x += a0.x; h0.y += a0.y; h0.z += a0.z; h0.w += a0.w;
@@ -445,7 +472,7 @@ int gemv_grid(const GemvParams &p, int ks) {
 
 int gemv_operand_mode(int dtype, const GemvParams &p) {
     (void)dtype;
-    if (p.xmode != X_NORM) return XM_PLAIN;
+    if (p.xmode != X_NORM) return p.kseg > 1 ? XM_SEG : XM_PLAIN;
     return gemv_staged(p) ? XM_STAGED : XM_DIRECT;
 }
 

@@ -133,7 +133,7 @@ Carve carve(const spec_model *m, int batch, int max_m, int G) {
     c.xn = take((size_t)G * d * arow);
     c.q = take((size_t)G * R * hq * hd * 4);
     c.o = take((size_t)G * hq * hd * arow);
-    c.act = take((size_t)m->d.d_ffn * arow);
+    c.act = take((size_t)G * m->d.d_ffn * arow);   // one block per set member (parallel MLPs)
     c.pacc = take((size_t)attention_split_max() * G * prow * hq * hd * 4);
     c.pml = take((size_t)attention_split_max() * G * prow * hq * 2 * 4);
     c.pval = take((size_t)batch * kPartialsMax * 4);
@@ -388,7 +388,50 @@ hipError_t run_stage(Fwd &f, int l0, int n, int mlp_mode, float *cos_out = nullp
     if ((e = product(f, gp, &grid)) != hipSuccess) return e;
     for (int i = 0; i < gp.n_norm_sel; ++i) f.nparts[i] = grid;
 
-    // 4. MLPs in set order
+    // 4. parallel reading: the set's MLPs as two launches, the N members'
+    //    [gate; up] blocks concatenated in one product (member i normalises
+    //    h0 + a_i with its own gain and RMS) and the N down projections as one
+    //    product over K = N x ffn (the members' matrices side by side), adding
+    //    sum_i (a_i + m_i) to h
+    if (par) {
+        GemvParams gd{};
+        gd.Mtot = R; gd.d = dm; gd.eps = d.rms_eps;
+        gd.W = layer_ptr(m->w.w_down, l0, (size_t)dm * d.d_ffn, xs);
+        gd.K = n * d.d_ffn; gd.kseg = n; gd.w_seg_stride = (int64_t)dm * d.d_ffn;
+        gd.n_units = dm / 2; gd.pair_block = 2; gd.rows_per_sel = dm;
+        gd.xmode = X_PLAIN; gd.X = act; gd.epi = EPI_RESID_ADD;
+        const int pk = packed_rows(m, gd);
+        const int64_t arows = pk ? pk : R;           // act rows per member block
+        gd.x_seg_stride = arows * d.d_ffn;
+        gp = GemvParams{};
+        gp.Mtot = R; gp.d = dm; gp.eps = d.rms_eps;
+        gp.W = layer_ptr(m->w.w_gate_up, l0, (size_t)2 * d.d_ffn * dm, xs);
+        gp.K = dm; gp.n_units = n * d.d_ffn; gp.pair_block = 2 * d.d_ffn; gp.rows_per_sel = 2 * d.d_ffn;
+        gp.xmode = X_NORM; gp.xh = h0; gp.xadd = abuf; gp.xadd_sel_stride = (int64_t)R * dm;
+        gp.xgain = m->w.ffn_norm + (size_t)l0 * dm; gp.xgain_stride = dm;
+        gp.xss = ss; gp.xss_sel_stride = f.c.ss_sel_stride; gp.xnparts = f.nparts[0];
+        gp.epi = EPI_SILU_MUL; gp.act = act; gp.act_ld = d.d_ffn; gp.act_sel_stride = arows * d.d_ffn;
+        gp.act_packed = pk;
+        // the float32 GEMV takes members with their own RMS only with staged
+        // operands; the tiled kernel takes no K segments
+        GemvParams tv = gp;
+        tv.M = R < gemv_max_rows() ? R : gemv_max_rows();
+        const ProdPath pu = product_path(m, gp), pd = product_path(m, gd);
+        const bool ok = pu != PP_TILED && pd != PP_TILED &&
+                        (pu != PP_VALU || gemv_operand_mode(d.dtype, tv) == 1);
+        if (ok) {
+            if ((e = product(f, gp)) != hipSuccess) return e;
+            gd.h = h;
+            gd.add2 = abuf; gd.n_add2 = n; gd.add2_sel_stride = (int64_t)R * dm;
+            gd.n_norm_sel = 1;
+            if ((e = product(f, gd, &grid)) != hipSuccess) return e;
+            f.nparts[0] = grid;
+            return hipSuccess;
+        }
+    }
+
+    // 4. MLPs in set order (sequential reading; parallel reading where the
+    //    concatenated products above do not apply)
     for (int i = 0; i < n; ++i) {
         const int l = l0 + i;
         const int si = par ? i : 0;

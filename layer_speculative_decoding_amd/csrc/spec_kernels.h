@@ -58,6 +58,11 @@ struct GemvParams {
     int64_t xgain_stride;
     const float *xss;     // X_NORM: sum-of-squares partials of residual row hrow at
     int xnparts;          //   xss[hrow * xnparts + 0 .. xnparts-1] (summed in order)
+    int64_t xss_sel_stride;   // X_NORM: member sel's partials start at xss + sel * xss_sel_stride
+                              //   (0: every member normalises with the same partials)
+    int kseg;             // > 1: K is kseg equal segments (the set members' matrices side by side):
+    int64_t w_seg_stride; //   segment s of weight row r at W + s * w_seg_stride + r * (K / kseg),
+    int64_t x_seg_stride; //   of activation row m at X + s * x_seg_stride + m * (K / kseg)
     int act_packed;       // SILU_MUL: 0 -> float32 act rows; PR -> packed bf16
                           //   operand rows (hi at row m, lo at row m + PR / 2)
     int xgather_mseq;     // > 0: activation row m reads residual row
@@ -68,10 +73,13 @@ struct GemvParams {
     int64_t out_ld, out_sel_stride;
     void *act;
     int64_t act_ld;
+    int64_t act_sel_stride;   // SILU_MUL: member sel's rows start at act + sel * act_sel_stride
     // RESID_ADD / ATTN_OUT
     float *h;             // [Mtot][d]
     float *h0;            // [Mtot][d] (parallel MLPs)
-    const float *add2;    // RESID_ADD: nullable extra addend [Mtot][d]
+    const float *add2;    // RESID_ADD: nullable extra addends [n_add2][Mtot][d] (n_add2 0 or 1: one)
+    int n_add2;
+    int64_t add2_sel_stride;
     int par_mlp;          // ATTN_OUT: parallel-MLP reading
     // row-norm partials of the updated residual: ss[sel * ss_sel_stride +
     // m * gridDim.x + block]; consumers sum a row's partials in block order

@@ -17,7 +17,7 @@ import pytest
 import torch
 
 from oracle import philox
-from oracle.model import KVCache, OracleModel, forward, fuzzy_step
+from oracle.model import MLP_PARALLEL, MLP_SEQUENTIAL, KVCache, OracleModel, forward, fuzzy_step
 from oracle.plan import default_group_plan, plan_offsets
 from oracle.sampling import accept_resample, sample_from_logits
 from synth import get_config, make_weights
@@ -95,18 +95,21 @@ def test_fullsize_forward_entry_points(cfg_name, which, ctx, batch, layers):
         tok = rng.integers(0, V, size=batch).astype(np.int32)
         logits = torch.zeros(batch, V, device="cuda")
         out = torch.zeros(batch, dtype=torch.int32, device="cuda")
-        api.spec_draft_group_step(gm, gkv, offs, 0, batch, i32(tok), 1, i32(pos), int(pos.max()), inv_t, 77,
-                                  logits, V, out, 1, wsb)
-        torch.cuda.synchronize()
-        zg, tg = logits.cpu().numpy(), out.cpu().numpy()
-        for b in range(batch):
-            zo = fuzzy_step(om, okv, b, int(tok[b]), int(pos[b]), sets)
-            err = rel_linf(zg[b], zo)
-            say(f"  draft step b={b} logits rel {err:.2e}")
-            assert err < TOL_BF16
-            t_or, mg = sample_from_logits(zo, inv_t, 77, b, int(pos[b]) + 1, philox.DRAFT)
-            if mg >= exclusion(zg[b], zo, inv_t):
-                assert tg[b] == t_or
+        # both MLP readings at the same positions (each step writes the fuzzy
+        # K/V there before its attention reads them)
+        for mlp in (MLP_SEQUENTIAL, MLP_PARALLEL):
+            api.spec_draft_group_step(gm, gkv, offs, mlp, batch, i32(tok), 1, i32(pos), int(pos.max()), inv_t, 77,
+                                      logits, V, out, 1, wsb)
+            torch.cuda.synchronize()
+            zg, tg = logits.cpu().numpy(), out.cpu().numpy()
+            for b in range(batch):
+                zo = fuzzy_step(om, okv, b, int(tok[b]), int(pos[b]), sets, mlp)
+                err = rel_linf(zg[b], zo)
+                say(f"  draft step ({'parallel' if mlp else 'sequential'} MLPs) b={b} logits rel {err:.2e}")
+                assert err < TOL_BF16
+                t_or, mg = sample_from_logits(zo, inv_t, 77, b, int(pos[b]) + 1, philox.DRAFT)
+                if mg >= exclusion(zg[b], zo, inv_t):
+                    assert tg[b] == t_or
         # ragged calibration over the same positions (rewrites the fuzzy entries)
         ntok = np.array([min(k + 1, 1 + (b * 2) % (k + 1)) for b in range(batch)], dtype=np.int32)
         toks = rng.integers(0, V, size=(batch, k + 1)).astype(np.int32)
