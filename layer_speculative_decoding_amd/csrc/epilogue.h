@@ -34,22 +34,26 @@ __device__ __forceinline__ int x_row(const GemvParams &p, int gm) {
 }
 
 // 1/rms of residual row hrow from its p.xnparts sum-of-squares partials.
-// Lane i adds partials i, i + 64, ... in that order (eight loads in flight),
+// Lane i adds partials i, i + 64, ... in that order,
 // then a fixed xor tree: every caller forms the same bits.  Whole wave.
 __device__ __forceinline__ float row_inv_rms(const GemvParams &p, int hrow, int sel = 0) {
     const int lane = threadIdx.x & 63;
     const float *src = p.xss + (int64_t)sel * p.xss_sel_stride + (int64_t)hrow * p.xnparts;
     const int n = p.xnparts;
+    // every load of up to 2048 partials in flight at once (one round trip;
+    // out-of-range slots add zero, so the order of the sum is unchanged)
+    constexpr int NB = 32;
     float s = 0.f;
-    int i = lane;
-    for (; i + 7 * 64 < n; i += 8 * 64) {
-        float v[8];
+    for (int i0 = 0; i0 < n; i0 += NB * 64) {
+        float v[NB];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = src[i + 64 * j];
+        for (int j = 0; j < NB; ++j) {
+            const int i = i0 + lane + 64 * j;
+            v[j] = i < n ? src[i] : 0.f;
+        }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) s += v[j];
+        for (int j = 0; j < NB; ++j) s += v[j];
     }
-    for (; i < n; i += 64) s += src[i];
     s = wave_sum(s);
     return 1.0f / sqrtf(s / (float)p.K + p.eps);
 }

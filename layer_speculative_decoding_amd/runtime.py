@@ -23,6 +23,7 @@ import torch
 
 from . import api
 from ._lib import SPEC_MLP_SEQUENTIAL
+from .trace import rng
 
 
 @dataclass
@@ -96,6 +97,10 @@ class SpecDecoder:
 
     # ---------------------------------------------------------------- prefill
     def prefill(self, prompts: np.ndarray):
+        with rng("prefill"):
+            self._prefill(prompts)
+
+    def _prefill(self, prompts: np.ndarray):
         B, P = prompts.shape
         assert B == self.B and P >= 1
         toks = torch.from_numpy(np.ascontiguousarray(prompts, dtype=np.int32)).to(self.dev)
@@ -143,6 +148,10 @@ class SpecDecoder:
                                  self.commit, self.ws)
 
     def step(self, new_tokens: int, marks=None) -> bool:
+        with rng("round"):
+            return self._step(new_tokens, marks)
+
+    def _step(self, new_tokens: int, marks=None) -> bool:
         """One round; returns True while some sequence still needs tokens.
 
         marks: optional list of 5 timing events recorded on the stream at the
@@ -152,10 +161,12 @@ class SpecDecoder:
         self._upload_positions()
         if marks:
             marks[0].record()
-        self.draft_phase()
+        with rng("draft"):
+            self.draft_phase()
         if marks:
             marks[1].record()
-        self.verify_phase()
+        with rng("verify"):
+            self.verify_phase()
         if marks:
             marks[2].record()
         if self.separate:
@@ -164,7 +175,8 @@ class SpecDecoder:
             tok_before = self.vtok.to("cpu").numpy().copy()
             ql = self.q_logits.cpu().numpy().copy()
             pl = self.p_logits.cpu().numpy().copy()
-        self.accept_phase()
+        with rng("accept"):
+            self.accept_phase()
         if marks:
             marks[3].record()
         bh = self.back_host
@@ -213,6 +225,13 @@ class SpecDecoder:
         rows = max(1, max(int(th[k + 1, b]) for b in range(B)))
         if not self.calibrate:
             self.caltok.copy_(self.nocal_host, non_blocking=True)
+        with rng("calibrate"):
+            self._calibrate(th, rows, k, B)
+        if marks:
+            marks[4].record()
+        return True
+
+    def _calibrate(self, th, rows, k, B):
         if self.separate:
             self.caltok[:, 0].copy_(self.xt)
             self.caltok[:, 1:].copy_(self.vtok[:, 1:])
@@ -224,9 +243,6 @@ class SpecDecoder:
             api.spec_calibrate_kv(self.draft, self.dkv, B, toks, self.tab[k], self.tab[k + 1], rows,
                                   max(self.t), self.inv_temp, self.seed, self.q_logits[:, 0], k * self.V,
                                   self.vtok[:, 1], k + 1, self.ws, tokens_stride=k + 1)
-        if marks:
-            marks[4].record()
-        return True
 
     def generate(self, prompts: np.ndarray, new_tokens: int) -> List[List[int]]:
         self.prefill(prompts)

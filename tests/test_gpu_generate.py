@@ -33,9 +33,9 @@ def test_tiny_config_lockstep(inv_temp, plan_kind):
                       plan_offsets(sets), cfg.prompt_len, inv_temp, cfg.sample_seed)
     st = lockstep(dec, OracleModel.from_torch(cfg.draft, dw), OracleModel.from_torch(cfg.base, bw), prompts,
                   cfg.k, sets, cfg.new_tokens, dec.inv_temp, cfg.sample_seed, MLP_SEQUENTIAL, TOL_F32)
-    say(f"  checked {st['checked']} excluded {st['excluded']} max rel err {st['err']:.2e}; "
+    say(f"  checked {st['checked']} flipped {st['flipped']} excluded {st['excluded']} max rel err {st['err']:.2e}; "
         f"rounds {len(dec.records)} accepted {sum(int(r.n_acc[0]) for r in dec.records)}")
-    assert st["excluded"] <= max(2, st["checked"] // 50)
+    assert st["excluded"] + st["flipped"] <= max(2, st["checked"] // 50)
 
 
 # the near-copy pairs' 4-layer plan with a real layer-parallel set (the default
@@ -70,11 +70,10 @@ def test_near_copy_lockstep_batch(dtype, mlp, inv_temp):
     st = lockstep(dec, OracleModel.from_torch(sh, dw), OracleModel.from_torch(sh, bw), prompts, k, sets, new,
                   dec.inv_temp, 4242, mlp, tol)
     acc = sum(int(a) for r in dec.records for a in r.n_acc)
-    say(f"  checked {st['checked']} excluded {st['excluded']} max rel err {st['err']:.2e}; accepted {acc}")
+    say(f"  checked {st['checked']} flipped {st['flipped']} excluded {st['excluded']} max rel err {st['err']:.2e}; "
+        f"accepted {acc}")
     assert acc > 0
-    # bf16 logits carry ~1e-2 absolute error, so near-tied greedy picks are
-    # legitimately excluded; every decision outside the bound matched
-    assert st["excluded"] <= max(3, st["checked"] // 3)
+    assert st["excluded"] + st["flipped"] <= 2 + st["checked"] // 50
 
 
 @pytest.mark.parametrize("dtype", [0, BF16])
@@ -95,9 +94,10 @@ def test_no_calibration_ablation_lockstep(dtype, inv_temp):
     st = lockstep(dec, OracleModel.from_torch(sh, dw), OracleModel.from_torch(sh, bw), prompts, k, sets, new,
                   dec.inv_temp, 515, MLP_SEQUENTIAL, tol, calibrate=False)
     acc = sum(int(a) for r in dec.records for a in r.n_acc)
-    say(f"  checked {st['checked']} excluded {st['excluded']} max rel err {st['err']:.2e}; accepted {acc}")
+    say(f"  checked {st['checked']} flipped {st['flipped']} excluded {st['excluded']} max rel err {st['err']:.2e}; "
+        f"accepted {acc}")
     assert acc > 0
-    assert st["excluded"] <= max(3, st["checked"] // 3)
+    assert st["excluded"] + st["flipped"] <= 2 + st["checked"] // 50
 
 
 @pytest.mark.parametrize("dtype", [0, BF16])
@@ -118,9 +118,10 @@ def test_separate_calibration_lockstep(dtype, inv_temp):
     st = lockstep(dec, OracleModel.from_torch(sh, dw), OracleModel.from_torch(sh, bw), prompts, k, sets, new,
                   dec.inv_temp, 616, MLP_SEQUENTIAL, tol, separate=True)
     acc = sum(int(a) for r in dec.records for a in r.n_acc)
-    say(f"  checked {st['checked']} excluded {st['excluded']} max rel err {st['err']:.2e}; accepted {acc}")
+    say(f"  checked {st['checked']} flipped {st['flipped']} excluded {st['excluded']} max rel err {st['err']:.2e}; "
+        f"accepted {acc}")
     assert acc > 0
-    assert st["excluded"] <= max(3, st["checked"] // 3)
+    assert st["excluded"] + st["flipped"] <= 2 + st["checked"] // 50
 
 
 @pytest.mark.parametrize("dtype", [0, BF16])

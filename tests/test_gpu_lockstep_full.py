@@ -70,12 +70,12 @@ def test_lockstep_at_workload_shapes(cfg_name, dl, bl, P, new, temps):
             for r in dec.records:
                 finished_early += int((done >= new).any() and (done < new).any())
                 done += np.minimum(r.n_acc + 1, new - done)
-        say(f"  T={T}: rounds {st['rounds']}, checked {st['checked']}, excluded {st['excluded']} "
-            f"(band {st['band']}, flipped {st['flipped']}), max logit rel err {st['err']:.2e}, "
+        say(f"  T={T}: rounds {st['rounds']}, checked {st['checked']}, flipped by the logit difference "
+            f"{st['flipped']}, excluded {st['excluded']}, max logit rel err {st['err']:.2e}, "
             f"accept counts {acc[:24]}{' ...' if len(acc) > 24 else ''}, rounds with frozen lanes "
             f"{finished_early}, {time.time() - t1:.1f}s")
         assert st["rounds"] >= 8
-        assert st["excluded"] <= 2 + st["checked"] // 8
+        assert st["excluded"] + st["flipped"] <= 2 + st["checked"] // 25
         if B > 1 and T > 0:
             assert len(set(acc)) > 1            # ragged accept counts
         del dec
