@@ -74,7 +74,7 @@ enum { SPEC_MLP_SEQUENTIAL = 0, SPEC_MLP_PARALLEL = 1 };
 
 /* Decoder shape.  head_dim must be 16, 32, 64 or 128; d_model, d_ffn and
  * n_q_heads*head_dim must be multiples of 8; n_q_heads a multiple of
- * n_kv_heads with at most 32 q heads per kv head (else
+ * n_kv_heads with at most 16 q heads per kv head (else
  * SPEC_ERR_UNSUPPORTED).  rope_theta: base of the rotate-half RoPE (pairs (j, j+hd/2),
  * angle pos * theta^(-2j/hd)); rms_eps: RMSNorm epsilon. */
 typedef struct {

@@ -33,6 +33,8 @@
 // waves' (max, sum, output) are merged in wave order through LDS; with several
 // key splits the workgroup publishes them and k_attn_merge combines the splits
 // in split order.
+#include <cstdlib>
+
 #include "spec_device.h"
 #include "spec_kernels.h"
 
@@ -41,13 +43,19 @@ namespace spec {
 namespace {
 
 constexpr int kKB = 16;        // keys per block (one MFMA row block)
+constexpr int kSplitMax = 64;
 constexpr int kWaves = 4;
 constexpr int kSpan = kKB * kWaves;   // keys per round of the four waves
-constexpr int kSplitMax = 64;
-constexpr int kMaxQV = 32;     // query vectors per workgroup at most
+constexpr int kMaxQV = 16;     // query vectors per workgroup (and q heads per kv head) at most
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8u(const uint4 &v) {
+    bf16x8 r;
+    __builtin_memcpy(&r, &v, 16);
+    return r;
+}
 
 // Eight float32 values as three bfloat16 pieces hi + mid + lo whose sum
 // carries the value to float32 precision (each piece is the round-to-nearest
@@ -537,7 +545,10 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
     }
 }
 
-// Merge the key splits of one (layer, row, q head) per wave: out = sum_s w_s
+// Merge the key splits of one (layer, row, q head) per wave (a separate
+// launch: merging in the last split's workgroup behind an agent-scope fence
+// and a counter measured 3 us slower per call, the fence writing the XCD's
+// L2 back): out = sum_s w_s
 // acc_s / sum_s w_s l_s with w_s = exp(m_s - max_s m_s).  Lane s reads split
 // s's (m, l); the weights' sum uses a fixed reduction tree and the outputs
 // accumulate in split order.
@@ -579,6 +590,294 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnParams p) {
     }
 }
 
+// ---------------------------------------------------------------- prompt
+// Causal attention of many consecutive rows (prompt prefills, long
+// calibrations) over a bfloat16 cache, flash style: a workgroup owns QR
+// consecutive rows of one sequence and all G q heads of one kv head (layer gi
+// of the group).  Its 16-vector blocks are (head, 16 consecutive rows); wave w
+// takes blocks w and w + 4.  Key tiles of 64 go once through LDS per
+// workgroup and serve every block: K key-major (the A operand of QK, 16
+// contiguous bytes per lane), V transposed to dim-major (the B operand of PV,
+// a lane's eight keys in two 8-byte runs; PREF: the next tile is requested into
+// registers during this tile's products).  q and the probabilities enter the
+// bfloat16 matrix instructions as hi + lo pieces (split2_bf16: within 2^-16 of
+// the float32 value), the products accumulate in float32, the softmax is online
+// in float32 as in the decode kernel.  The key loop reads the K operand once
+// per (key block, dim step) for both of a wave's blocks and the V operand once
+// per (key chunk, dim block), and runs both blocks' products without branches
+// (a wave's unused block, for G that does not divide 8, computes on zeros).
+template <int HD, bool PREF>
+__global__ __launch_bounds__(256, 2) void k_attn_prompt(AttnParams p, int QR) {
+    constexpr int KT = 64;                 // keys per LDS tile
+    constexpr int NQB = 2;                 // 16-vector blocks per wave
+    constexpr int NS = HD / 32;            // 32-dim steps of QK
+    constexpr int NJ = HD / 16;            // 16-dim blocks of PV
+    constexpr int KLD = HD + 8;            // K row stride in LDS (elements)
+    constexpr int VLD = KT + 4;            // transposed V row stride (elements)
+    __shared__ __align__(16) uint16_t ks[KT * KLD];
+    __shared__ __align__(16) uint16_t vt[HD * VLD];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 15, lg = lane >> 4;
+    const int G = p.hq / p.hkv;
+    const int NBK = G * (QR / 16);         // 16-vector blocks of the workgroup (<= 8)
+    // Same-K/V workgroups eight apart in linear id (one XCD), heaviest query
+    // tiles (latest rows) first.
+    int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+    {
+        const int nqb = gridDim.x, ny = gridDim.y;
+        const int lin = bx + nqb * (by + ny * bz);
+        const int span = 8 * nqb;
+        const int full = (nqb * ny * (int)gridDim.z) / span * span;
+        if (nqb > 1 && lin < full) {
+            const int off = lin % span;
+            const int grp = (lin / span) * 8 + (off & 7);
+            bx = off >> 3;
+            by = grp % ny;
+            bz = grp / ny;
+        }
+        bx = nqb - 1 - bx;
+    }
+    const int gi = by / p.hkv, kvh = by - gi * p.hkv, b = bz;
+    const int mseq = p.rows.mseq;
+    const int i0 = bx * QR;
+    const int ntok = p.rows.n_tok ? p.rows.n_tok[b] : mseq;
+    const int pos0 = p.rows.start_pos[b];
+    // scores in log2 units: q carries 1/sqrt(hd) * log2(e), exp2 forms the weights
+    const float qscale = 1.4426950408889634f / sqrtf((float)HD);
+    const int last = min(min(i0 + QR, ntok), mseq) - 1;
+    int kend = last >= 0 ? pos0 + last + 1 : 0;
+    if (kend > p.capacity) kend = p.capacity;
+    const int64_t cache_off = ((((int64_t)(p.layer0 + gi) * p.batch + b) * p.hkv + kvh) * p.capacity) * HD;
+    const uint16_t *Kc = reinterpret_cast<const uint16_t *>(p.kc) + cache_off;
+    const uint16_t *Vc = reinterpret_cast<const uint16_t *>(p.vc) + cache_off;
+
+    // this wave's blocks: head, first row, q operand pieces of row li, position
+    bool bok[NQB];
+    int head[NQB], rb0[NQB], qpos[NQB], qfull[NQB];
+    uint4 qh[NQB][NS], ql[NQB][NS];
+#pragma unroll
+    for (int nb = 0; nb < NQB; ++nb) {
+        const int blk = wave + 4 * nb;
+        bok[nb] = blk < NBK;
+        head[nb] = kvh * G + (bok[nb] ? blk % G : 0);
+        rb0[nb] = i0 + 16 * (bok[nb] ? blk / G : 0);
+        const int row = rb0[nb] + li;
+        int pos = -1;
+        if (bok[nb] && row < mseq && row < ntok) {
+            pos = pos0 + row;
+            if (pos < 0 || pos >= p.capacity) pos = -1;
+        }
+        qpos[nb] = pos;
+        const bool rok = bok[nb] && row < mseq;
+        const float *qp = p.q + (int64_t)gi * p.q_sel_stride + (((int64_t)b * mseq + row) * p.hq + head[nb]) * HD;
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            float x[8];
+            if (rok) {
+                load_span<8>(qp + 32 * st + 8 * lg, x);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] *= qscale;
+            split2_bf16_hw(x, qh[nb][st], ql[nb][st]);
+        }
+        // no row of the block masks a key below its first row's position
+        // (and every row is a valid one): tiles ending there skip the mask
+        const int nval = min(ntok, mseq) - rb0[nb];
+        qfull[nb] = bok[nb] && nval >= 16 && pos0 + rb0[nb] + 15 < p.capacity ? pos0 + rb0[nb] : -1;
+    }
+
+    float m_run[NQB], l_run[NQB];
+    f32x4 acc[NQB][NJ];
+#pragma unroll
+    for (int nb = 0; nb < NQB; ++nb) {
+        m_run[nb] = -INFINITY;
+        l_run[nb] = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[nb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // K / V of a tile: 16-byte pieces per thread, requested one tile ahead
+    // (global -> registers during the previous tile's products)
+    constexpr int NKL = KT * HD / 8 / 256;          // K pieces per thread
+    constexpr int NVL = (KT / 2) * (HD / 8) / 256;  // V key-pair pieces per thread
+    static_assert(NKL * 256 * 8 == KT * HD && NVL * 256 * 16 == KT * HD, "tile split");
+    // (keys past kend read row kend - 1, a written row: the mask gives them
+    // weight 0 and 0 times a finite V is 0)
+    uint4 kreg[NKL], vreg[NVL][2];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < NKL; ++i) {
+            const int e = tid + 256 * i, key = e / (HD / 8), c8 = e - key * (HD / 8);
+            kreg[i] = ld16(Kc + (int64_t)min(k0 + key, kend - 1) * HD + 8 * c8);
+        }
+#pragma unroll
+        for (int i = 0; i < NVL; ++i) {
+            const int e = tid + 256 * i, kp = e / (HD / 8), c8 = e - kp * (HD / 8), key = 2 * kp;
+            vreg[i][0] = ld16(Vc + (int64_t)min(k0 + key, kend - 1) * HD + 8 * c8);
+            vreg[i][1] = ld16(Vc + (int64_t)min(k0 + key + 1, kend - 1) * HD + 8 * c8);
+        }
+    };
+    if constexpr (PREF) {
+        if (kend > 0) fetch(0);
+    }
+
+    for (int kt0 = 0; kt0 < kend; kt0 += KT) {
+        if constexpr (!PREF) fetch(kt0);
+        __syncthreads();   // the previous tile is consumed
+        // K tile key-major; V tile transposed: two keys' 8 dims -> 8 (key pair) words
+#pragma unroll
+        for (int i = 0; i < NKL; ++i) {
+            const int e = tid + 256 * i, key = e / (HD / 8), c8 = e - key * (HD / 8);
+            *reinterpret_cast<uint4 *>(&ks[key * KLD + 8 * c8]) = kreg[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NVL; ++i) {
+            const int e = tid + 256 * i, kp = e / (HD / 8), c8 = e - kp * (HD / 8), key = 2 * kp;
+            const uint4 v0 = vreg[i][0], v1 = vreg[i][1];
+            const uint32_t a[4] = {v0.x, v0.y, v0.z, v0.w}, c[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                *reinterpret_cast<uint32_t *>(&vt[(8 * c8 + 2 * w) * VLD + key]) = (a[w] & 0xFFFFu) | (c[w] << 16);
+                *reinterpret_cast<uint32_t *>(&vt[(8 * c8 + 2 * w + 1) * VLD + key]) =
+                    (a[w] >> 16) | (c[w] & 0xFFFF0000u);
+            }
+        }
+        __syncthreads();
+        if constexpr (PREF) {
+            if (kt0 + KT < kend) fetch(kt0 + KT);
+        }
+
+        // QK: lane (li, lg), register r of key block kb holds S[key 16 kb + 4 lg + r][row li]
+        f32x4 sc[NQB][4];
+#pragma unroll
+        for (int nb = 0; nb < NQB; ++nb)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) sc[nb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+                const uint4 kv = *reinterpret_cast<const uint4 *>(&ks[(16 * kb + li) * KLD + 32 * st + 8 * lg]);
+#pragma unroll
+                for (int nb = 0; nb < NQB; ++nb) {
+                    sc[nb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8u(kv), as_bf16x8u(ql[nb][st]),
+                                                                         sc[nb][kb], 0, 0, 0);
+                    sc[nb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8u(kv), as_bf16x8u(qh[nb][st]),
+                                                                         sc[nb][kb], 0, 0, 0);
+                }
+            }
+
+        // online softmax; the probabilities of chunk c (keys 32 c + 4 lg + r
+        // and 32 c + 16 + 4 lg + r) become the A operand of PV as they sit
+        uint4 ph[NQB][2], pl[NQB][2];
+#pragma unroll
+        for (int nb = 0; nb < NQB; ++nb) {
+            float pr[16];
+            float mx = -INFINITY;
+            if (kt0 + KT - 1 <= qfull[nb] && kt0 + KT <= kend) {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        pr[4 * kb + r] = sc[nb][kb][r];
+                        mx = fmaxf(mx, pr[4 * kb + r]);
+                    }
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int key = kt0 + 16 * kb + 4 * lg + r;
+                        const float v = (key < kend && key <= qpos[nb]) ? sc[nb][kb][r] : -INFINITY;
+                        pr[4 * kb + r] = v;
+                        mx = fmaxf(mx, v);
+                    }
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+            const float m_new = fmaxf(m_run[nb], mx);
+            const bool none = m_new == -INFINITY;
+            const float msub = none ? 0.f : m_new;   // exp2(-inf - 0) = 0
+            float sum = 0.f;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                pr[t] = __builtin_amdgcn_exp2f(pr[t] - msub);
+                sum += pr[t];
+            }
+            sum += __shfl_xor(sum, 16, kWave);
+            sum += __shfl_xor(sum, 32, kWave);
+            const float corr = none ? 1.f : __builtin_amdgcn_exp2f(m_run[nb] - m_new);
+            l_run[nb] = l_run[nb] * corr + sum;
+            m_run[nb] = m_new;
+            f32x4 cr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * lg + r, kWave);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) acc[nb][j] *= cr;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) split2_bf16_hw(&pr[8 * c], ph[nb][c], pl[nb][c]);
+        }
+
+        // PV: B = V[the same eight keys][dim 16 j + li]
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const uint16_t *vr = &vt[(16 * j + li) * VLD + 32 * c + 4 * lg];
+                const uint2 v0 = *reinterpret_cast<const uint2 *>(vr);
+                const uint2 v1 = *reinterpret_cast<const uint2 *>(vr + 16);
+                const uint4 vb = make_uint4(v0.x, v0.y, v1.x, v1.y);
+#pragma unroll
+                for (int nb = 0; nb < NQB; ++nb) {
+                    acc[nb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8u(pl[nb][c]), as_bf16x8u(vb),
+                                                                         acc[nb][j], 0, 0, 0);
+                    acc[nb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8u(ph[nb][c]), as_bf16x8u(vb),
+                                                                         acc[nb][j], 0, 0, 0);
+                }
+            }
+    }
+
+    // lane (li, lg), register r of dim block j holds O[row 4 lg + r][dim 16 j + li]
+#pragma unroll
+    for (int nb = 0; nb < NQB; ++nb) {
+        if (!bok[nb]) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rr = 4 * lg + r;
+            const float L = __shfl(l_run[nb], rr, kWave);
+            const int row = rb0[nb] + rr;
+            if (row >= mseq) continue;
+            const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const float v = L > 0.f ? acc[nb][j][r] * inv : 0.f;
+                store_out<1>(p, gi, b * mseq + row, head[nb], 16 * j + li, &v);
+            }
+        }
+    }
+}
+
+// Rows per workgroup of the prompt kernel: blocks of 16 rows per q head, at
+// most 8 blocks (two per wave).
+int prompt_rows(int G) { return 16 * (8 / G >= 1 ? 8 / G : 1); }
+
+// Calls of at least this many rows per sequence (and no key splits) use the
+// prompt kernel on bfloat16 caches with head_dim 64 or 128 and at most 8 q
+// heads per kv head (SPEC_ATTN_PROMPT=0: the decode kernel throughout).
+constexpr int kPromptMinRows = 32;
+bool prompt_kernel_enabled() {
+    static const bool on = [] {
+        const char *e = getenv("SPEC_ATTN_PROMPT");
+        return !(e && e[0] == '0');
+    }();
+    return on;
+}
+
 // 16 query vectors per workgroup: measured against 32 (two blocks), the
 // smaller register footprint and the doubled workgroup count win at every
 // decode shape (8B verify, 6 rows, context 560: 12.9 vs 15.5 us; 8B verify,
@@ -608,6 +907,20 @@ template <typename T>
 hipError_t launch_t(const AttnParams &p, hipStream_t s) {
     if (p.hkv < 1 || p.hq % p.hkv || p.hq / p.hkv > kMaxQV || p.splits < 1 || p.splits > kSplitMax)
         return hipErrorInvalidValue;
+    if constexpr (sizeof(T) == 2) {
+        const int G = p.hq / p.hkv;
+        if (p.splits == 1 && p.rows.mseq >= kPromptMinRows && G <= 8 && (p.hd == 64 || p.hd == 128) &&
+            prompt_kernel_enabled()) {
+            const int QR = prompt_rows(G);
+            dim3 grid((p.rows.mseq + QR - 1) / QR, p.n_group * p.hkv, p.batch);
+            // head_dim 128 fetches each tile after the barrier: requesting it a
+            // tile ahead needs 32 more VGPRs and spills (8B layer, 2047 rows:
+            // 172 vs 137 us); head_dim 64 has the room (1B layer: 74 us)
+            if (p.hd == 64) hipLaunchKernelGGL((k_attn_prompt<64, true>), grid, dim3(256), 0, s, p, QR);
+            else hipLaunchKernelGGL((k_attn_prompt<128, false>), grid, dim3(256), 0, s, p, QR);
+            return hipGetLastError();
+        }
+    }
     switch (p.hd) {
     case 16: return launch_nqb<T, 16>(p, s);
     case 32: return launch_nqb<T, 32>(p, s);
@@ -643,6 +956,7 @@ int attention_splits(int dtype, int hd, int n_group, int batch, int hq, int hkv,
 }
 
 int attention_max_group() { return kMaxQV; }
+
 
 hipError_t launch_attention(int dtype, const AttnParams &p, hipStream_t s) {
     return dtype ? launch_t<uint16_t>(p, s) : launch_t<float>(p, s);

@@ -64,54 +64,60 @@ __device__ __forceinline__ void group16_argmax(float &v, int &i) {
     }
 }
 
-// MT: 16-row operand tiles (1: M <= 8, 2: M <= 16).  A unit has NB
-// 16-row blocks (2 for the paired epilogues, else 1); the workgroup runs KS
-// waves per block, wave w streaming block w / KS over K part w % KS.
+// MT: 16-row operand tiles (1: M <= 8, 2: M <= 16).  A unit is NBU 16-row
+// blocks of W: the two blocks of a pair for the paired epilogues, one block
+// otherwise.  Each of the workgroup's KS waves streams every block of the
+// unit over its own contiguous part of K, in tiles of 8 KB of weights (NBU
+// blocks x kTK / NBU elements), so one activation fragment feeds NBU matrix
+// instructions: the activation reads per weight byte fall by NBU, which
+// matters once the operand carries two pieces per row.  One weight tile per
+// wave is in flight while the previous one is consumed (two, at about 190
+// VGPRs, measured slower: 8B down at 6 rows 29.0 -> 30.5 us, O 14.6 -> 15.5,
+// lm head 175 -> 196).
 template <int MT, int EPI, int KS, bool SEG = false>
-__global__ __launch_bounds__(64 * KS * (epi_is_pair(EPI) ? 2 : 1)) void k_gemm_mfma(GemvParams p, int ups) {
+__global__ __launch_bounds__(64 * KS) void k_gemm_mfma(GemvParams p, int ups) {
     constexpr bool kPair = epi_is_pair(EPI);
-    constexpr int NB = kPair ? 2 : 1;       // 16-row blocks per unit
-    constexpr int NW = NB * KS;             // waves per workgroup
-    constexpr int NL = 8;                   // 16-byte loads per lane per tile
-    constexpr int TILE = 16 * kLD;          // elements of one wave's LDS tile
-    __shared__ __align__(16) uint16_t smem[NW * TILE];
+    constexpr int NBU = kPair ? 2 : 1;      // 16-row blocks per unit
+    constexpr int TKL = kTK / NBU;          // K elements per tile
+    constexpr int LDK = TKL + 8;            // LDS row stride (16 bytes of padding)
+    constexpr int RPL = 512 / TKL;          // weight rows per 16-byte-per-lane load
+    constexpr int NL = 8;                   // loads per lane per tile
+    constexpr int BL = NL / NBU;            // of them per block
+    constexpr int NS = TKL / 32;            // matrix steps per tile
+    constexpr int TILE = 16 * NBU * LDK;    // elements of one wave's LDS tile
+    static_assert(NBU * MT * 64 * 16 <= TILE * 2, "reduction area");
+    __shared__ __align__(16) uint16_t smem[KS * TILE];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int blk = wave / KS, part = wave - blk * KS;
     const int li = lane & 15, lg = lane >> 4;
     uint16_t *tile = smem + (size_t)wave * TILE;
     const int K = p.K;
-    const int ntile = (K + kTK - 1) / kTK;
+    const int ntile = (K + TKL - 1) / TKL;
     const int per = (ntile + KS - 1) / KS;
-    const int t0 = part * per, t1 = min(ntile, t0 + per);
+    const int t0 = wave * per, t1 = min(ntile, t0 + per);
     const int half = p.pair_block >> 1;
     const int bph = half >> 4;              // 16-row blocks per half (paired)
-    const int lrow = lane >> 5, lcol = 8 * (lane & 31);   // load lane -> (row of a pair, element)
+    const int lrow = lane / (TKL / 8), lcol = 8 * (lane % (TKL / 8));   // load lane -> (row, element)
 
-    float best_v[MT][4];
-    int best_i[MT][4];
+    float best_v[4];
+    int best_i[4];
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) { best_v[t][r] = -INFINITY; best_i[t][r] = 0x7FFFFFFF; }
+    for (int r = 0; r < 4; ++r) { best_v[r] = -INFINITY; best_i[r] = 0x7FFFFFFF; }
 
-    // first weight rows of unit u's two blocks
-    auto unit_blocks = [&](int u, int &r0b, int &r1b) {
-        if (kPair) {
+    // first weight row of each block of unit u
+    auto unit_blocks = [&](int u, int (&rb)[NBU]) {
+        if constexpr (kPair) {
             const int bb = u / bph, jb = u - bb * bph;
-            r0b = bb * p.pair_block + jb * 16;
-            r1b = r0b + half;
+            rb[0] = bb * p.pair_block + jb * 16;
+            rb[1] = rb[0] + half;
         } else {
-            r0b = u * 16;
-            r1b = r0b;
+#pragma unroll
+            for (int j = 0; j < NBU; ++j) rb[j] = (u * NBU + j) * 16;
         }
     };
     // The weight tile in flight lives outside the unit loop, and a workgroup
     // that takes several units (sampling products) requests its next unit's
-    // first tile before the current unit's reduction.  In this form the
-    // paired products compile to about 124 VGPRs, so two 8-wave workgroups
-    // share a CU (measured: 8B gate/up at 6 rows 47.1 -> 43.2 us against the
-    // loop-local form at 136 VGPRs, one workgroup per CU).
+    // first tile before the current unit's reduction.
     uint4 wv[NL];
     bool have_first = false;   // wv already holds this unit's first tile
     // K in segments (set members' matrices side by side; Ks a multiple of the
@@ -121,19 +127,27 @@ __global__ __launch_bounds__(64 * KS * (epi_is_pair(EPI) ? 2 : 1)) void k_gemm_m
     const int Ks = (kSegOk && p.kseg > 1) ? K / p.kseg : K;
     auto tile_off = [&](int tt, int64_t seg_stride) -> int64_t {
         if constexpr (!kSegOk) {
-            return tt * kTK;
+            return (int64_t)tt * TKL;
         } else {
-            if (p.kseg <= 1) return tt * kTK;
-            const int k = tt * kTK, sg = k / Ks;
+            if (p.kseg <= 1) return (int64_t)tt * TKL;
+            const int k = tt * TKL, sg = k / Ks;
             return sg * seg_stride + (k - sg * Ks);
         }
     };
+    const uint16_t *W0 = reinterpret_cast<const uint16_t *>(p.W);
+    auto load_from = [&](uint4 (&w)[NL], const int (&rb)[NBU], int tt) {
+        const bool in = tt * TKL + lcol < K;
+        const int64_t off = tile_off(tt, p.w_seg_stride) + lcol;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int j = i / BL, r = RPL * (i % BL) + lrow;
+            w[i] = in ? ld16_stream(W0 + (int64_t)(rb[j] + r) * Ks + off) : make_uint4(0, 0, 0, 0);
+        }
+    };
     for (int u = blockIdx.x; u < p.n_units; u += gridDim.x) {
-        int r0b, r1b;
-        unit_blocks(u, r0b, r1b);
-        const int sel = r0b / p.rows_per_sel;
-        const int rb = blk ? r1b : r0b;         // this wave's block
-        const uint16_t *W = reinterpret_cast<const uint16_t *>(p.W) + (int64_t)rb * Ks;
+        int rb[NBU];
+        unit_blocks(u, rb);
+        const int sel = rb[0] / p.rows_per_sel;
         const uint16_t *xb = reinterpret_cast<const uint16_t *>(p.X) + (int64_t)sel * p.x_sel_stride;
         bool xok[MT];
         const uint16_t *xr[MT];
@@ -143,75 +157,72 @@ __global__ __launch_bounds__(64 * KS * (epi_is_pair(EPI) ? 2 : 1)) void k_gemm_m
             xok[t] = (t * 16 + li) % (8 * MT) < p.M;
             xr[t] = xb + (int64_t)(t * 16 + li) * Ks + 8 * lg;
         }
-        f32x4 acc[MT];
+        f32x4 acc[NBU][MT];
 #pragma unroll
-        for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NBU; ++j)
+#pragma unroll
+            for (int t = 0; t < MT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        auto load_from = [&](const uint16_t *Wr, int tt) {
-            const bool in = tt * kTK + lcol < K;
-            const uint16_t *wt0 = Wr + tile_off(tt, p.w_seg_stride) + lcol;
-#pragma unroll
-            for (int i = 0; i < NL; ++i)
-                wv[i] = in ? ld16_stream(wt0 + (int64_t)(2 * i + lrow) * Ks) : make_uint4(0, 0, 0, 0);
-        };
-        auto load = [&](int tt) { load_from(W, tt); };
-        if (t0 < t1 && !have_first) load(t0);
+        if (t0 < t1 && !have_first) load_from(wv, rb, t0);
         have_first = false;
-        for (int tt = t0; tt < t1; ++tt) {
+        {
+            for (int tt = t0; tt < t1; ++tt) {
 #pragma unroll
-            for (int i = 0; i < NL; ++i) *reinterpret_cast<uint4 *>(&tile[(2 * i + lrow) * kLD + lcol]) = wv[i];
-            // the tile's activation operands are requested before the next
-            // tile's weights, so the matrix cores wait only for them
-            const int nsteps = min(kTK, K - tt * kTK) >> 5;     // 32-element MFMA steps in this tile
-            uint4 xv[kTK / 32][MT];
-            const int64_t xo = tile_off(tt, p.x_seg_stride);
+                for (int i = 0; i < NL; ++i) {
+                    const int j = i / BL, r = RPL * (i % BL) + lrow;
+                    *reinterpret_cast<uint4 *>(&tile[(16 * j + r) * LDK + lcol]) = wv[i];
+                }
+                // the tile's activation operands are requested before the
+                // next weight tile, so the matrix cores wait only for them
+                const int nsteps = min(TKL, K - tt * TKL) >> 5;     // 32-element steps in this tile
+                uint4 xv[NS][MT];
+                const int64_t xo = tile_off(tt, p.x_seg_stride);
 #pragma unroll
-            for (int s2 = 0; s2 < kTK / 32; ++s2)
-#pragma unroll
-                for (int t = 0; t < MT; ++t)
-                    xv[s2][t] = (xok[t] && s2 < nsteps) ? ld16(xr[t] + xo + 32 * s2) : make_uint4(0, 0, 0, 0);
-            if (tt + 1 < t1) load(tt + 1);
-#pragma unroll
-            for (int s2 = 0; s2 < kTK / 32; ++s2) {
-                if (s2 < nsteps) {
-                    const uint4 wt = *reinterpret_cast<const uint4 *>(&tile[li * kLD + 32 * s2 + 8 * lg]);
+                for (int s2 = 0; s2 < NS; ++s2)
 #pragma unroll
                     for (int t = 0; t < MT; ++t)
-                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xv[s2][t]), as_bf16x8(wt), acc[t],
-                                                                          0, 0, 0);
+                        xv[s2][t] = (xok[t] && s2 < nsteps) ? ld16(xr[t] + xo + 32 * s2) : make_uint4(0, 0, 0, 0);
+                if (tt + 1 < t1) load_from(wv, rb, tt + 1);
+#pragma unroll
+                for (int s2 = 0; s2 < NS; ++s2) {
+                    if (s2 < nsteps) {
+#pragma unroll
+                        for (int j = 0; j < NBU; ++j) {
+                            const uint4 wt =
+                                *reinterpret_cast<const uint4 *>(&tile[(16 * j + li) * LDK + 32 * s2 + 8 * lg]);
+#pragma unroll
+                            for (int t = 0; t < MT; ++t)
+                                acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    as_bf16x8(xv[s2][t]), as_bf16x8(wt), acc[j][t], 0, 0, 0);
+                        }
+                    }
                 }
             }
         }
         if (u + (int)gridDim.x < p.n_units && t0 < t1) {
-            int n0, n1;
-            unit_blocks(u + gridDim.x, n0, n1);
-            load_from(reinterpret_cast<const uint16_t *>(p.W) + (int64_t)(blk ? n1 : n0) * Ks, t0);
+            int nb[NBU];
+            unit_blocks(u + gridDim.x, nb);
+            load_from(wv, nb, t0);
             have_first = true;
         }
-        // fixed-order sum of the K parts of each block by wave 0; C layout:
-        // lane l, register r holds C[4 * (l / 16) + r][l % 16] = (activation
-        // row, weight row of the block)
-        f32x4 res[NB][MT];
-#pragma unroll
-        for (int t = 0; t < MT; ++t) res[0][t] = acc[t];
-        if (NW > 1) {
+        // fixed-order sum of the K parts by wave 0; C layout: lane l,
+        // register r holds C[4 * (l / 16) + r][l % 16] = (activation row,
+        // weight row of the block)
+        if (KS > 1) {
             __syncthreads();   // every wave is done with its tile
             f32x4 *red = reinterpret_cast<f32x4 *>(tile);
 #pragma unroll
-            for (int t = 0; t < MT; ++t) red[t * 64 + lane] = acc[t];
+            for (int j = 0; j < NBU; ++j)
+#pragma unroll
+                for (int t = 0; t < MT; ++t) red[(j * MT + t) * 64 + lane] = acc[j][t];
             __syncthreads();
             if (wave == 0) {
+                for (int q = 1; q < KS; ++q) {
+                    const f32x4 *o = reinterpret_cast<const f32x4 *>(smem + (size_t)q * TILE);
 #pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    for (int q = (j == 0 ? 1 : 0); q < KS; ++q) {
-                        const f32x4 *o = reinterpret_cast<const f32x4 *>(smem + (size_t)(j * KS + q) * TILE);
+                    for (int j = 0; j < NBU; ++j)
 #pragma unroll
-                        for (int t = 0; t < MT; ++t) {
-                            if (j == 0) res[0][t] += o[t * 64 + lane];
-                            else if (q == 0) res[j][t] = o[t * 64 + lane];
-                            else res[j][t] += o[t * 64 + lane];
-                        }
-                    }
+                        for (int t = 0; t < MT; ++t) acc[j][t] += o[(j * MT + t) * 64 + lane];
                 }
             }
             __syncthreads();
@@ -220,41 +231,42 @@ __global__ __launch_bounds__(64 * KS * (epi_is_pair(EPI) ? 2 : 1)) void k_gemm_m
         // hi and lo halves of each output: rows m and m + 8 of one tile sit in
         // lane groups g and g + 2 (lanes l and l ^ 32); with two tiles they
         // sit in the same lane and register of tiles 0 and 1
+        f32x4 res[NBU];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
+        for (int j = 0; j < NBU; ++j) {
             if constexpr (MT == 1) {
+                res[j] = acc[j][0];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) res[j][0][r] += __shfl_xor(res[j][0][r], 32, kWave);
+                for (int r = 0; r < 4; ++r) res[j][r] += __shfl_xor(res[j][r], 32, kWave);
             } else {
-                res[j][0] += res[j][1];
+                res[j] = acc[j][0] + acc[j][MT - 1];
             }
         }
-#pragma unroll
-        for (int t = 0; t < 1; ++t) {
-            float ssv[4] = {0.f, 0.f, 0.f, 0.f};
-            // one activation row at a time (keeps the epilogue's registers
-            // out of the streaming loop's budget)
+        float ssv[4] = {0.f, 0.f, 0.f, 0.f};
+        // one activation row at a time (keeps the epilogue's registers out of
+        // the streaming loop's budget)
 #pragma unroll 1
-            for (int r = 0; r < 4; ++r) {
-                const int m = t * 16 + 4 * lg + r;
-                if (m >= p.M) continue;
-                if constexpr (kPair) {
-                    epi_pair<uint16_t, EPI>(p, r0b + li, r0b + li, r1b + li, sel, m, res[0][t][r], res[NB - 1][t][r]);
-                } else {
-                    epi_row<uint16_t, EPI>(p, r0b + li, sel, m, res[0][t][r], ssv[r], best_v[t][r], best_i[t][r]);
-                }
-            }
-            if constexpr (epi_has_ss(EPI)) {
-                // one unit per workgroup: partial index = unit within its set member
-                if (p.n_norm_sel > 0 && (EPI == EPI_RESID_ADD || p.par_mlp || sel == 0)) {
-                    const int si = (EPI == EPI_ATTN_OUT && p.par_mlp) ? sel : 0;
+        for (int r = 0; r < 4; ++r) {
+            const int m = 4 * lg + r;
+            if (m >= p.M) continue;
+            if constexpr (kPair) {
+                epi_pair<uint16_t, EPI>(p, rb[0] + li, rb[0] + li, rb[1] + li, sel, m, res[0][r], res[1][r]);
+            } else {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float s = group16_sum(ssv[r]);
-                        const int m = t * 16 + 4 * lg + r;
-                        if (li == 0 && m < p.M)
-                            p.ss[(int64_t)si * p.ss_sel_stride + (int64_t)(p.m0 + m) * ups + (u - sel * ups)] = s;
-                    }
+                for (int j = 0; j < NBU; ++j)
+                    epi_row<uint16_t, EPI>(p, rb[j] + li, sel, m, res[j][r], ssv[r], best_v[r], best_i[r]);
+            }
+        }
+        if constexpr (epi_has_ss(EPI)) {
+            // one unit per workgroup: partial index = unit within its set member
+            if (p.n_norm_sel > 0 && (EPI == EPI_RESID_ADD || p.par_mlp || sel == 0)) {
+                const int si = (EPI == EPI_ATTN_OUT && p.par_mlp) ? sel : 0;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float s = group16_sum(ssv[r]);
+                    const int m = 4 * lg + r;
+                    if (li == 0 && m < p.M)
+                        p.ss[(int64_t)si * p.ss_sel_stride + (int64_t)(p.m0 + m) * ups + (u - sel * ups)] = s;
                 }
             }
         }
@@ -262,36 +274,34 @@ __global__ __launch_bounds__(64 * KS * (epi_is_pair(EPI) ? 2 : 1)) void k_gemm_m
     if constexpr (EPI == EPI_LOGITS) {
         if (wave != 0) return;
 #pragma unroll
-        for (int t = 0; t < 1; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float v = best_v[t][r];
-                int i = best_i[t][r];
-                group16_argmax(v, i);
-                const int m = t * 16 + 4 * lg + r;
-                if (li == 0 && m < p.M) {
-                    p.part_val[(int64_t)(p.m0 + m) * gridDim.x + blockIdx.x] = v;
-                    p.part_idx[(int64_t)(p.m0 + m) * gridDim.x + blockIdx.x] = i;
-                }
+        for (int r = 0; r < 4; ++r) {
+            float v = best_v[r];
+            int i = best_i[r];
+            group16_argmax(v, i);
+            const int m = 4 * lg + r;
+            if (li == 0 && m < p.M) {
+                p.part_val[(int64_t)(p.m0 + m) * gridDim.x + blockIdx.x] = v;
+                p.part_idx[(int64_t)(p.m0 + m) * gridDim.x + blockIdx.x] = i;
             }
+        }
     }
+}
+
+template <int MT, int EPI, int KS>
+void launch_ks(const GemvParams &p, dim3 g, int ups, hipStream_t s) {
+    if constexpr (EPI == EPI_RESID_ADD) {
+        if (p.kseg > 1) {
+            hipLaunchKernelGGL((k_gemm_mfma<MT, EPI, KS, true>), g, dim3(64 * KS), 0, s, p, ups);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((k_gemm_mfma<MT, EPI, KS>), g, dim3(64 * KS), 0, s, p, ups);
 }
 
 template <int MT, int EPI>
 void launch_epi(const GemvParams &p, dim3 g, int ks, int ups, hipStream_t s) {
-    if constexpr (epi_is_pair(EPI)) {
-        hipLaunchKernelGGL((k_gemm_mfma<MT, EPI, 4>), g, dim3(512), 0, s, p, ups);
-    } else {
-        if constexpr (EPI == EPI_RESID_ADD) {
-            if (p.kseg > 1) {
-                if (ks == 4) hipLaunchKernelGGL((k_gemm_mfma<MT, EPI, 4, true>), g, dim3(256), 0, s, p, ups);
-                else hipLaunchKernelGGL((k_gemm_mfma<MT, EPI, 8, true>), g, dim3(512), 0, s, p, ups);
-                return;
-            }
-        }
-        if (ks == 4) hipLaunchKernelGGL((k_gemm_mfma<MT, EPI, 4>), g, dim3(256), 0, s, p, ups);
-        else hipLaunchKernelGGL((k_gemm_mfma<MT, EPI, 8>), g, dim3(512), 0, s, p, ups);
-    }
+    if (ks == 4) launch_ks<MT, EPI, 4>(p, g, ups, s);
+    else launch_ks<MT, EPI, 8>(p, g, ups, s);
 }
 
 template <int MT>
@@ -308,12 +318,24 @@ hipError_t launch_mt(const GemvParams &p, dim3 g, int ks, int ups, hipStream_t s
     return hipGetLastError();
 }
 
+int env_int(const char *name, int dflt) {
+    const char *e = getenv(name);
+    return e ? atoi(e) : dflt;
+}
+
 }  // namespace
 
 int gemm_mfma_max_rows() { return 16; }
 
-// One unit per workgroup, except sampling products, which keep a fixed grid
-// (their arg-max partials are per workgroup).
+// Weight rows of a unit: the two 16-row blocks of a pair for the paired
+// epilogues, one block otherwise (two consecutive blocks per unit, measured:
+// 8B verify 4.12 vs 3.87 ms, since the unpaired products then have half the
+// workgroups).
+int gemm_mfma_unit_rows(int epi, int rows, int rows_per_sel) {
+    (void)rows; (void)rows_per_sel;
+    return epi_is_pair(epi) ? 32 : 16;
+}
+
 // One unit per workgroup (measured against one or two persistent workgroups
 // per CU that take several units each with the next unit's first tile
 // requested early: 8B gate/up at 6 rows 43.2 vs 45.0-45.4 us), except
@@ -324,12 +346,15 @@ int gemm_mfma_grid(const GemvParams &p) {
     return p.epi == EPI_LOGITS && n > kLogitGrid ? kLogitGrid : n;
 }
 
-// Waves per block (4 or 8): 8 when the launch would otherwise have fewer than
-// about 3K waves and every wave keeps at least one tile.  Paired units keep 4
-// (8, in 1024-thread workgroups, measured slower: 8B QKV 16.2 -> 18.6 us,
-// gate/up 43.2 -> 51.5 us at 6 rows).
+// Waves per workgroup (4 or 8), each streaming its own part of K: paired
+// units take 8 (SPEC_MFMA_PAIR_KS overrides); other products 8 when the
+// launch would otherwise have fewer than about 3K waves and every wave keeps
+// at least one tile.
 int gemm_mfma_splits(const GemvParams &p) {
-    if (epi_is_pair(p.epi)) return 4;
+    if (epi_is_pair(p.epi)) {
+        static const int pk = env_int("SPEC_MFMA_PAIR_KS", 8) == 4 ? 4 : 8;
+        return pk;
+    }
     const int ntile = (p.K + kTK - 1) / kTK;
     int ks = 4;
     while (ks < kMaxKS && (int64_t)p.n_units * ks < 3072 && ks * 2 <= ntile) ks *= 2;
@@ -345,10 +370,14 @@ bool gemm_mfma_supported(const GemvParams &p) {
 
 int gemm_mfma_packed_rows(int M) { return M <= 8 ? 16 : 32; }
 
-hipError_t launch_gemm_mfma(const GemvParams &p, int grid, int ks, hipStream_t s) {
-    if ((ks != 4 && ks != 8) || (epi_is_pair(p.epi) && ks != 4)) return hipErrorInvalidValue;
+// p.n_units counts units of unit_rows weight rows (gemm_mfma_unit_rows).
+hipError_t launch_gemm_mfma(const GemvParams &p, int grid, int ks, int unit_rows, hipStream_t s) {
+    if (ks != 4 && ks != 8) return hipErrorInvalidValue;
+    if (epi_is_pair(p.epi) ? unit_rows != 32 : (unit_rows != 16 && unit_rows != 32)) return hipErrorInvalidValue;
+    const int ur = unit_rows;
+    if (ur != gemm_mfma_unit_rows(p.epi, 0, 0) || p.rows_per_sel % ur != 0) return hipErrorInvalidValue;
     // partial index of a residual writer: the unit within its set member
-    const int ups = p.rows_per_sel / 16;
+    const int ups = p.rows_per_sel / ur;
     if (epi_has_ss(p.epi) && p.n_norm_sel > 0 && grid != p.n_units) return hipErrorInvalidValue;
     // every row of the call in one launch, operand packed as gemm_mfma_packed_rows says
     if (p.m0 != 0 || p.M > 16) return hipErrorInvalidValue;

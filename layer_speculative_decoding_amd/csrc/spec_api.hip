@@ -101,12 +101,18 @@ std::string gemv_name(int dtype, const GemvParams &p) {
            std::to_string(p.epi) + ", " + std::to_string(gemv_operand_mode(dtype, p)) + ">";
 }
 
-std::string mfma_name(int M, int epi, int ks) {
-    return std::string("k_gemm_mfma<") + (M <= 8 ? "1" : "2") + ", " + std::to_string(epi) + ", " +
-           std::to_string(ks) + ">";
+constexpr bool epi_is_pair_host(int epi) { return epi == EPI_QKV_ROPE || epi == EPI_SILU_MUL; }
+
+// the instance launch_gemm_mfma takes for product q (all template arguments,
+// as the profiler prints them)
+std::string mfma_name(const GemvParams &q, int ks, int unit_rows) {
+    const bool pair = epi_is_pair_host(q.epi);
+    const bool seg = !pair && q.epi == EPI_RESID_ADD && q.kseg > 1;
+    (void)unit_rows;
+    return std::string("k_gemm_mfma<") + (q.M <= 8 ? "1" : "2") + ", " + std::to_string(q.epi) + ", " +
+           std::to_string(ks) + ", " + (seg ? "true" : "false") + ">";
 }
 
-constexpr bool epi_is_pair_host(int epi) { return epi == EPI_QKV_ROPE || epi == EPI_SILU_MUL; }
 
 // Workspace layout for R activation rows and sets of at most G layers.
 struct Carve {
@@ -193,10 +199,14 @@ int tiled_min_rows() {
 // or the tiled matrix-core GEMM (17 rows and more, float32 operand rows).
 enum ProdPath { PP_VALU, PP_MFMA, PP_TILED };
 
+// Weight rows per unit of the skinny matrix-core kernel for product p.
+int mfma_unit_rows(const GemvParams &p) {
+    return gemm_mfma_unit_rows(p.epi, p.n_units * 2, p.rows_per_sel);
+}
+
 GemvParams mfma_params(const GemvParams &p) {
-    const bool pair = epi_is_pair_host(p.epi);
     GemvParams q = p;
-    q.n_units = pair ? p.n_units * 2 / 32 : p.n_units * 2 / 16;   // 16-row blocks (pairs of them when paired)
+    q.n_units = p.n_units * 2 / mfma_unit_rows(p);
     q.m0 = 0;
     q.M = p.Mtot;
     return q;
@@ -262,7 +272,8 @@ hipError_t product(const Fwd &f, GemvParams p, int *parts_out = nullptr) {
         GemvParams q = mfma_params(p);
         const int grid = gemm_mfma_grid(q);
         const int ks = gemm_mfma_splits(q);
-        if (parts_out) *parts_out = (p.epi == EPI_LOGITS) ? grid : p.rows_per_sel / 16;
+        const int ur = mfma_unit_rows(p);
+        if (parts_out) *parts_out = (p.epi == EPI_LOGITS) ? grid : p.rows_per_sel / ur;
         double xbytes = (double)Mtot * p.K * 4;
         if (p.xmode == X_NORM) {
             // normalise once into packed operand rows, then stream the weights
@@ -277,8 +288,8 @@ hipError_t product(const Fwd &f, GemvParams p, int *parts_out = nullptr) {
             xbytes *= n_sel;
         }
         ProfScope ps(f.s);
-        hipError_t e = launch_gemm_mfma(q, grid, ks, f.s);
-        ps.done(mfma_name(Mtot, p.epi, ks), wbytes + xbytes, 2.0 * Mtot * rows * (double)p.K);
+        hipError_t e = launch_gemm_mfma(q, grid, ks, ur, f.s);
+        ps.done(mfma_name(q, ks, ur), wbytes + xbytes, 2.0 * Mtot * rows * (double)p.K);
         return e;
     }
     const int mr = gemv_max_rows();

@@ -69,6 +69,28 @@ __device__ __forceinline__ void split2_bf16(const uint4 &a, const uint4 &b, uint
     hi = make_uint4(h[0], h[1], h[2], h[3]);
     lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
+// Two floats to packed bfloat16, round to nearest even (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+    const f32x2_t v = {a, b};
+    const bf16x2_t r = __builtin_convertvector(v, bf16x2_t);
+    uint32_t u;
+    __builtin_memcpy(&u, &r, 4);
+    return u;
+}
+// split2_bf16 of x[0..7] with the hardware conversion for the lo pieces
+__device__ __forceinline__ void split2_bf16_hw(const float *x, uint4 &hi, uint4 &lo) {
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t x0 = __float_as_uint(x[2 * i]) & 0xFFFF0000u, x1 = __float_as_uint(x[2 * i + 1]) & 0xFFFF0000u;
+        h[i] = (x0 >> 16) | x1;
+        l[i] = cvt_pk_bf16(x[2 * i] - __uint_as_float(x0), x[2 * i + 1] - __uint_as_float(x1));
+    }
+    hi = make_uint4(h[0], h[1], h[2], h[3]);
+    lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // Streaming (non-temporal) 16-byte load for data read once per step.
 __device__ __forceinline__ uint4 ld16_stream(const void *p) {

@@ -121,13 +121,14 @@ int gemv_operand_mode(int dtype, const GemvParams &p);
 // MFMA skinny GEMM (bf16) over all M <= 16 rows of a call in one launch (m0
 // = 0), K a multiple of 32.  X is the packed operand: gemm_mfma_packed_rows(M)
 // bf16 rows per set member, hi(x_m) in row m and lo(x_m) in row m + PR / 2
-// (see split2_bf16; PR = 16 for M <= 8, else 32).  Units:
-// pairs of 16-row blocks for the paired epilogues (QKV RoPE, SiLU; n_units =
-// rows / 32, pair_block a multiple of 32), single 16-row blocks otherwise
-// (n_units = rows / 16).  ks waves per workgroup (4, 8 or 16).  Residual
-// writers run one unit per workgroup and leave rows_per_sel / 16 partials
-// per row and set member.
-hipError_t launch_gemm_mfma(const GemvParams &p, int grid, int ks, hipStream_t s);
+// (see split2_bf16; PR = 16 for M <= 8, else 32).  Units of unit_rows =
+// gemm_mfma_unit_rows(epi, rows, rows_per_sel) weight rows: pairs of 16-row
+// blocks for the paired epilogues (QKV RoPE, SiLU; pair_block a multiple of
+// 32), single 16-row blocks otherwise; n_units = rows / unit_rows.  ks waves per workgroup (4 or 8), each over its own part of K.
+// Residual writers run one unit per workgroup and leave rows_per_sel /
+// unit_rows partials per row and set member.
+hipError_t launch_gemm_mfma(const GemvParams &p, int grid, int ks, int unit_rows, hipStream_t s);
+int gemm_mfma_unit_rows(int epi, int rows, int rows_per_sel);
 // Tiled matrix-core GEMM (bf16) for more than 16 rows: every row of
 // the call in one launch (p.m0 = 0, p.M = rows), K a multiple of 64, no
 // LOGITS epilogue, a set member's rows a whole number of 64-row tiles (32

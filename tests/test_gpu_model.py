@@ -274,6 +274,39 @@ def test_prompt_prefill_matches_oracle(name, tile, monkeypatch):
     assert ek < tol and ev < tol
 
 
+@pytest.mark.parametrize("hq,hkv,hd", [(4, 4, 64), (8, 4, 128), (14, 2, 64), (16, 2, 128), (16, 1, 64)])
+def test_prompt_attention_group_sizes(hq, hkv, hd):
+    """Prompt-length prefills through the flash-style prompt attention (one
+    workgroup per 16 * (8 / G) rows of one kv head, two 16-row blocks per
+    wave; G = 16 falls back to the decode kernel) at q heads per kv head
+    G = 1, 2, 7, 8, 16, ragged last row tile, a ragged second sequence."""
+    from layer_speculative_decoding_amd import api
+    shape = tiny_shape(2, hq * hd // 2, hq, hkv, hd, 256, 512, dtype=BF16)
+    w = make_weights(shape, 11, gain_std=0.1, std=0.05)
+    om = OracleModel.from_torch(shape, w)
+    gm = api.SpecModel(shape, to_dev(w))
+    B, P = 2, 83
+    gkv = api.KVCache(shape, B, P + 4)
+    okv = KVCache(shape, B, P + 4)
+    prompts = np.random.default_rng(3).integers(0, shape.vocab, size=(B, P)).astype(np.int32)
+    say(f"prompt attention hq={hq} hkv={hkv} hd={hd} B={B} P={P}")
+    wsb = ws(api.spec_workspace_bytes(gm, B, P, 1))
+    lens = np.array([P, P - 30], dtype=np.int32)
+    last = torch.zeros(B, shape.vocab, device="cuda")
+    tok = torch.zeros(B, dtype=torch.int32, device="cuda")
+    api.spec_calibrate_kv(gm, gkv, B, i32(prompts), i32([0, 0]), i32(lens), P, P - 1, 0.0, 5, last, shape.vocab,
+                          tok, 1, wsb)
+    torch.cuda.synchronize()
+    zg = last.cpu().numpy()
+    for b in range(B):
+        zo = forward(om, okv, b, prompts[b, :lens[b]], range(lens[b]), logits="last")
+        err = rel_linf(zg[b], zo)
+        say(f"  b={b} n={lens[b]} logits rel {err:.2e}")
+        assert err < TOL_BF16
+    ek, ev = _kv_rel(gkv, okv, int(lens[1]))
+    assert ek < TOL_BF16 and ev < TOL_BF16
+
+
 @pytest.mark.parametrize("name", list(SHAPES))
 def test_attention_input_cosine_matches_oracle(name):
     """The cosine diagnostic of the fuzzy inputs against the oracle's trace of

@@ -48,8 +48,8 @@ def test_paired_matrix_core_products_fit_two_workgroups_per_cu():
     the weight-streaming loop: no scratch access may sit between the first and
     the last matrix instruction."""
     res = _resources("gemm_mfma.hip")
-    # k_gemm_mfma<1, EPI, 4> for EPI 1 (QKV + RoPE) and 2 (SiLU gate/up)
-    names = [n for n in res if re.search(r"k_gemm_mfmaILi1ELi[12]ELi4E", n)]
+    # k_gemm_mfma<1, EPI, 8, ...> for EPI 1 (QKV + RoPE) and 2 (SiLU gate/up)
+    names = [n for n in res if re.search(r"k_gemm_mfmaILi1ELi[12]ELi8E", n)]
     assert len(names) == 2, sorted(res)
     asm = _assembly("gemm_mfma.hip")
     for n in names:
