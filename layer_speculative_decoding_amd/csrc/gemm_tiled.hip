@@ -17,7 +17,9 @@
 //  * the float32 activations enter the matrix cores as two bfloat16 pieces
 //    hi + lo (split when the step's rows are written to LDS), so every
 //    fragment pair takes two matrix instructions and the products carry the
-//    activations to within 2^-16 of their magnitude;
+//    activations to within 2^-16 of their magnitude; a tile with fewer call
+//    rows than its 128 (verify rows of a few sequences) stashes and
+//    multiplies only the 16-row blocks that hold rows;
 //  * K advances in 64-element steps through one LDS stage (rows padded by 16
 //    bytes, so the fragment reads of a wave spread over all banks); each
 //    lane moves 16 bytes of weights per row (128 contiguous bytes per row per
@@ -44,8 +46,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBK = 64;           // K elements per step
 constexpr int kLDK = kBK + 8;     // LDS row stride in elements (16 bytes of padding)
-constexpr int kWMB = 4;           // 16-row activation blocks per wave
-constexpr int kBM = 128;          // activation rows per tile (2 wave rows)
+// activation rows per tile: 2 wave rows of WMB 16-row blocks (WMB = 4: 128
+// rows for prompt-length calls, WMB = 1: 32 rows for calls of at most 32)
 constexpr int kMaxSplit = 8;
 
 __device__ __forceinline__ bf16x8 as_bf8(const uint4 &v) {
@@ -62,6 +64,7 @@ __device__ __forceinline__ float sum16(float v) {
 
 struct TileArgs {
     int gm, gn;        // activation tiles, weight tiles
+    int bm;            // activation rows per tile (32 WMB)
     int parts;         // sum-of-squares partials per row and set member
     int ks;            // K slices (1: no split)
     int kc;            // K steps per slice
@@ -77,7 +80,7 @@ template <int EPI, int BN>
 __device__ __forceinline__ TilePos tile_pos(const GemvParams &p, const TileArgs &ta, int t) {
     TilePos q;
     const int mt = t % ta.gm, nt = t / ta.gm;
-    q.m0 = mt * kBM;
+    q.m0 = mt * ta.bm;
     q.u0 = nt * (BN / 2);
     q.n0 = nt * BN;
     if (epi_is_pair(EPI)) q.sel = ((q.u0 / (p.pair_block / 2)) * p.pair_block) / p.rows_per_sel;
@@ -88,9 +91,9 @@ __device__ __forceinline__ TilePos tile_pos(const GemvParams &p, const TileArgs 
 // The fused epilogue of one tile.  Lane (li, lg) of wave (wm, wn), register r
 // of block (a, c) holds activation row 64 wm + 16 a + 4 lg + r and unit
 // (NH / 2) wn + 16 (c % HB) + li of member c / HB.
-template <int EPI, int WNB>
+template <int EPI, int WNB, int WMB>
 __device__ __forceinline__ void tile_epilogue(const GemvParams &p, const TileArgs &ta, const TilePos &q,
-                                              const f32x4 (&acc)[kWMB][WNB]) {
+                                              const f32x4 (&acc)[WMB][WNB]) {
     constexpr bool kPair = epi_is_pair(EPI);
     constexpr int BN = 32 * WNB, NH = BN / 2, HB = WNB / 2;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -99,11 +102,11 @@ __device__ __forceinline__ void tile_epilogue(const GemvParams &p, const TileArg
     float best_v = -INFINITY;
     int best_i = 0;
 #pragma unroll
-    for (int a = 0; a < kWMB; ++a) {
+    for (int a = 0; a < WMB; ++a) {
         float ssv[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int m = q.m0 + 64 * wm + 16 * a + 4 * lg + r;
+            const int m = q.m0 + 16 * WMB * wm + 16 * a + 4 * lg + r;
             if (m >= p.M) continue;
 #pragma unroll
             for (int c = 0; c < HB; ++c) {
@@ -125,7 +128,7 @@ __device__ __forceinline__ void tile_epilogue(const GemvParams &p, const TileArg
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float s = sum16(ssv[r]);
-                    const int m = q.m0 + 64 * wm + 16 * a + 4 * lg + r;
+                    const int m = q.m0 + 16 * WMB * wm + 16 * a + 4 * lg + r;
                     if (li == 0 && m < p.M)
                         p.ss[(int64_t)si * p.ss_sel_stride + (int64_t)(p.m0 + m) * ta.parts + part] = s;
                 }
@@ -138,19 +141,21 @@ __device__ __forceinline__ void tile_epilogue(const GemvParams &p, const TileArg
 // 64 through one LDS stage, the weights of step k + DIST requested before
 // step k's matrix instructions, the activations of step k + 1.  SPLIT: workgroup
 // b covers tile b % T over K slice b / T and stores its accumulators.
-template <int EPI, int WNB, bool SPLIT>
+template <int EPI, int WNB, bool SPLIT, int WMB>
 __global__ __launch_bounds__(256, 2) void k_gemm_tile(GemvParams p, TileArgs ta) {
+    constexpr int BM = 32 * WMB;
     constexpr bool kPair = epi_is_pair(EPI);
     constexpr int BN = 32 * WNB, NH = BN / 2;
     constexpr int HB = WNB / 2;                  // 16-unit blocks per wave per member
     constexpr int RPP = 32;                      // rows per load pass (8 lanes x 16 bytes per row)
-    constexpr int LA = kBM / RPP, LB = BN / RPP; // load passes per step
+    constexpr int LA = BM / RPP, LB = BN / RPP;  // load passes per step
     // weight steps in flight: three for 64-row tiles (their per-step bytes are
     // half, and three workgroups share a CU), two for 128-row tiles (whose
-    // register budget has no room for a third)
-    constexpr int DIST = WNB == 2 ? 3 : 2;
+    // register budget has no room for a third); four with 32 activation rows
+    // (few accumulators: the weight stream is all there is)
+    constexpr int DIST = WMB == 1 ? 4 : (WNB == 2 ? 3 : 2);
     // activation hi pieces, lo pieces, weights
-    __shared__ __align__(16) uint16_t lds[(2 * kBM + BN) * kLDK];
+    __shared__ __align__(16) uint16_t lds[(2 * BM + BN) * kLDK];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;
@@ -206,28 +211,37 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(GemvParams p, TileArgs ta)
             ra[i][1] = va[i] ? ld16(x + 16) : make_uint4(0, 0, 0, 0);
         }
     };
+    // activation rows any wave reads (16-row blocks that hold call rows)
+    const int mneed = min(BM, (p.M - q.m0 + 15) / 16 * 16);
     auto stash = [&](const uint4 (&xa)[LA][2], const uint4 (&xb)[LB]) {
 #pragma unroll
         for (int i = 0; i < LA; ++i) {
+            if (RPP * i >= mneed) continue;
+            const float x[8] = {__uint_as_float(xa[i][0].x), __uint_as_float(xa[i][0].y), __uint_as_float(xa[i][0].z),
+                                __uint_as_float(xa[i][0].w), __uint_as_float(xa[i][1].x), __uint_as_float(xa[i][1].y),
+                                __uint_as_float(xa[i][1].z), __uint_as_float(xa[i][1].w)};
             uint4 hi, lo;
-            split2_bf16(xa[i][0], xa[i][1], hi, lo);
+            split2_bf16_hw(x, hi, lo);
             *reinterpret_cast<uint4 *>(&lds[(lr + RPP * i) * kLDK + lc]) = hi;
-            *reinterpret_cast<uint4 *>(&lds[(kBM + lr + RPP * i) * kLDK + lc]) = lo;
+            *reinterpret_cast<uint4 *>(&lds[(BM + lr + RPP * i) * kLDK + lc]) = lo;
         }
 #pragma unroll
-        for (int i = 0; i < LB; ++i) *reinterpret_cast<uint4 *>(&lds[(2 * kBM + lr + RPP * i) * kLDK + lc]) = xb[i];
+        for (int i = 0; i < LB; ++i) *reinterpret_cast<uint4 *>(&lds[(2 * BM + lr + RPP * i) * kLDK + lc]) = xb[i];
     };
 
-    f32x4 acc[kWMB][WNB];
+    f32x4 acc[WMB][WNB];
 #pragma unroll
-    for (int a = 0; a < kWMB; ++a)
+    for (int a = 0; a < WMB; ++a)
 #pragma unroll
         for (int c = 0; c < WNB; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // LDS rows of this lane's fragments: activation block a, weight block c
     // (member c / HB, unit block c % HB of this wave column)
-    const int arow = (64 * wm + li) * kLDK + 8 * lg;
-    const int brow = (2 * kBM + (NH / 2) * wn + li) * kLDK + 8 * lg;
+    const int arow = (16 * WMB * wm + li) * kLDK + 8 * lg;
+    const int brow = (2 * BM + (NH / 2) * wn + li) * kLDK + 8 * lg;
+    // 16-row activation blocks of this wave that hold call rows (a tile of a
+    // few verify rows leaves most of them empty: their products are skipped)
+    const int nva = __builtin_amdgcn_readfirstlane(min(WMB, max(0, (p.M - q.m0 - 16 * WMB * wm + 15) / 16)));
     auto compute = [&]() {
 #pragma unroll
         for (int ks = 0; ks < kBK / 32; ++ks) {
@@ -238,16 +252,40 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(GemvParams p, TileArgs ta)
                     &lds[brow + ((c / HB) * NH + 16 * (c % HB)) * kLDK + 32 * ks]);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                uint4 av[kWMB];
+                uint4 av[WMB];
 #pragma unroll
-                for (int a = 0; a < kWMB; ++a)
-                    av[a] = *reinterpret_cast<const uint4 *>(&lds[arow + (h * kBM + 16 * a) * kLDK + 32 * ks]);
+                for (int a = 0; a < WMB; ++a)
+                    av[a] = *reinterpret_cast<const uint4 *>(&lds[arow + (h * BM + 16 * a) * kLDK + 32 * ks]);
 #pragma unroll
-                for (int a = 0; a < kWMB; ++a)
+                for (int a = 0; a < WMB; ++a)
 #pragma unroll
                     for (int c = 0; c < WNB; ++c)
                         acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(av[a]), as_bf8(bv[c]),
                                                                             acc[a][c], 0, 0, 0);
+            }
+        }
+    };
+    // the same for the first nva blocks only
+    auto compute_part = [&]() {
+#pragma unroll
+        for (int ks = 0; ks < kBK / 32; ++ks) {
+            uint4 bv[WNB];
+#pragma unroll
+            for (int c = 0; c < WNB; ++c)
+                bv[c] = *reinterpret_cast<const uint4 *>(
+                    &lds[brow + ((c / HB) * NH + 16 * (c % HB)) * kLDK + 32 * ks]);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int a = 0; a < WMB; ++a) {
+                    if (a < nva) {
+                        const uint4 av = *reinterpret_cast<const uint4 *>(&lds[arow + (h * BM + 16 * a) * kLDK + 32 * ks]);
+#pragma unroll
+                        for (int c = 0; c < WNB; ++c)
+                            acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(av), as_bf8(bv[c]),
+                                                                                acc[a][c], 0, 0, 0);
+                    }
+                }
             }
         }
     };
@@ -266,7 +304,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(GemvParams p, TileArgs ta)
                 __syncthreads();
                 if (k + DIST < nk) load_w((k + DIST) * kBK, rb[d]);
                 if (k + 1 < nk) load_x((k + 1) * kBK);
-                compute();
+                if (nva == WMB) compute();
+                else if (nva > 0) compute_part();
             }
         }
     }
@@ -274,67 +313,73 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(GemvParams p, TileArgs ta)
     if constexpr (SPLIT) {
         // 16-row activation blocks past the call's rows hold nothing; they
         // are neither stored here nor read back by the slice sum
-        float4 *dst = reinterpret_cast<float4 *>(ta.part) + ((int64_t)slice * T + t) * (kWMB * WNB) * 256 + tid;
+        float4 *dst = reinterpret_cast<float4 *>(ta.part) + ((int64_t)slice * T + t) * (WMB * WNB) * 256 + tid;
 #pragma unroll
-        for (int a = 0; a < kWMB; ++a)
-            if (q.m0 + 64 * wm + 16 * a < p.M)
+        for (int a = 0; a < WMB; ++a)
+            if (q.m0 + 16 * WMB * wm + 16 * a < p.M)
 #pragma unroll
                 for (int c = 0; c < WNB; ++c)
                     dst[(a * WNB + c) * 256] = make_float4(acc[a][c][0], acc[a][c][1], acc[a][c][2], acc[a][c][3]);
     } else {
-        tile_epilogue<EPI, WNB>(p, ta, q, acc);
+        tile_epilogue<EPI, WNB, WMB>(p, ta, q, acc);
     }
 }
 
 // Sum of a split product's K slices (in slice order) and its epilogue; one
 // workgroup per tile, lanes as in the product kernel.
-template <int EPI, int WNB>
+template <int EPI, int WNB, int WMB>
 __global__ __launch_bounds__(256) void k_gemm_tile_epi(GemvParams p, TileArgs ta) {
     constexpr int BN = 32 * WNB;
     const int T = ta.gm * ta.gn, t = blockIdx.x;
     const TilePos q = tile_pos<EPI, BN>(p, ta, t);
     const int wm = (threadIdx.x >> 6) & 1;
-    const float4 *src = reinterpret_cast<const float4 *>(ta.part) + (int64_t)t * (kWMB * WNB) * 256 + threadIdx.x;
+    const float4 *src = reinterpret_cast<const float4 *>(ta.part) + (int64_t)t * (WMB * WNB) * 256 + threadIdx.x;
     // the blocks of up to SG slices are requested together, then added in
     // slice order (the sum's order is fixed: slice 0, 1, 2, ...)
     constexpr int SG = WNB == 2 ? 4 : 2;
-    const int64_t sstride = (int64_t)T * (kWMB * WNB) * 256;
-    f32x4 acc[kWMB][WNB];
+    const int64_t sstride = (int64_t)T * (WMB * WNB) * 256;
+    f32x4 acc[WMB][WNB];
 #pragma unroll
-    for (int a = 0; a < kWMB; ++a)
+    for (int a = 0; a < WMB; ++a)
 #pragma unroll
         for (int c = 0; c < WNB; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int k0 = 0; k0 < ta.ks; k0 += SG) {
-        float4 v[SG][kWMB][WNB];
+        float4 v[SG][WMB][WNB];
 #pragma unroll
         for (int g = 0; g < SG; ++g)
 #pragma unroll
-            for (int a = 0; a < kWMB; ++a)
+            for (int a = 0; a < WMB; ++a)
 #pragma unroll
                 for (int c = 0; c < WNB; ++c)
-                    v[g][a][c] = (k0 + g < ta.ks && q.m0 + 64 * wm + 16 * a < p.M)
+                    v[g][a][c] = (k0 + g < ta.ks && q.m0 + 16 * WMB * wm + 16 * a < p.M)
                                      ? src[(k0 + g) * sstride + (a * WNB + c) * 256]
                                      : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int g = 0; g < SG; ++g)
 #pragma unroll
-            for (int a = 0; a < kWMB; ++a)
+            for (int a = 0; a < WMB; ++a)
 #pragma unroll
                 for (int c = 0; c < WNB; ++c)
                     if (k0 + g < ta.ks) acc[a][c] += f32x4{v[g][a][c].x, v[g][a][c].y, v[g][a][c].z, v[g][a][c].w};
     }
-    tile_epilogue<EPI, WNB>(p, ta, q, acc);
+    tile_epilogue<EPI, WNB, WMB>(p, ta, q, acc);
+}
+
+template <int WNB, int EPI, int WMB>
+void launch_wmb(const GemvParams &p, const TileArgs &ta, hipStream_t s) {
+    const int T = ta.gm * ta.gn;
+    if (ta.ks > 1) {
+        hipLaunchKernelGGL((k_gemm_tile<EPI, WNB, true, WMB>), dim3(T * ta.ks), dim3(256), 0, s, p, ta);
+        hipLaunchKernelGGL((k_gemm_tile_epi<EPI, WNB, WMB>), dim3(T), dim3(256), 0, s, p, ta);
+    } else {
+        hipLaunchKernelGGL((k_gemm_tile<EPI, WNB, false, WMB>), dim3(T), dim3(256), 0, s, p, ta);
+    }
 }
 
 template <int WNB, int EPI>
 void launch_one(const GemvParams &p, const TileArgs &ta, hipStream_t s) {
-    const int T = ta.gm * ta.gn;
-    if (ta.ks > 1) {
-        hipLaunchKernelGGL((k_gemm_tile<EPI, WNB, true>), dim3(T * ta.ks), dim3(256), 0, s, p, ta);
-        hipLaunchKernelGGL((k_gemm_tile_epi<EPI, WNB>), dim3(T), dim3(256), 0, s, p, ta);
-    } else {
-        hipLaunchKernelGGL((k_gemm_tile<EPI, WNB, false>), dim3(T), dim3(256), 0, s, p, ta);
-    }
+    if (ta.bm == 32) launch_wmb<WNB, EPI, 1>(p, ta, s);
+    else launch_wmb<WNB, EPI, 4>(p, ta, s);
 }
 
 template <int WNB>
@@ -361,9 +406,19 @@ bool fits(const GemvParams &p, int bn) {
 struct Pick {
     int bn, ks;
 };
+// Activation rows per tile: 32 for calls of at most 32 rows (SPEC_TILE_SMALL=0:
+// always 128).
+int tile_rows(int M) {
+    static const bool small = [] {
+        const char *e = getenv("SPEC_TILE_SMALL");
+        return !(e && e[0] == '0');
+    }();
+    return (small && M <= 32) ? 32 : 128;
+}
 Pick pick(const GemvParams &p, size_t part_bytes) {
     const int rows = p.n_units * 2, nk = p.K / kBK;
-    const int gm = (p.M + kBM - 1) / kBM;
+    const int bm = tile_rows(p.M);
+    const int gm = (p.M + bm - 1) / bm;
     Pick k{0, 1};
     if (const char *e = getenv("SPEC_TILE")) {
         Pick f{0, 1};
@@ -383,7 +438,7 @@ Pick pick(const GemvParams &p, size_t part_bytes) {
     k.ks = k.ks < 1 ? 1 : (k.ks > kMaxSplit ? kMaxSplit : k.ks);
     if (k.ks > nk / 2) k.ks = nk / 2 < 1 ? 1 : nk / 2;
     // the partial buffer bounds the slices
-    const int64_t tile_bytes = (int64_t)gm * (rows / k.bn) * kBM * k.bn * 4;
+    const int64_t tile_bytes = (int64_t)gm * (rows / k.bn) * bm * k.bn * 4;
     while (k.ks > 1 && (size_t)(tile_bytes * k.ks) > part_bytes) --k.ks;
     return k;
 }
@@ -391,7 +446,8 @@ Pick pick(const GemvParams &p, size_t part_bytes) {
 TileArgs tile_args(const GemvParams &p, Pick k, float *part) {
     TileArgs ta;
     const int nk = p.K / kBK;
-    ta.gm = (p.M + kBM - 1) / kBM;
+    ta.bm = tile_rows(p.M);
+    ta.gm = (p.M + ta.bm - 1) / ta.bm;
     ta.gn = (p.n_units * 2) / k.bn;
     ta.parts = (p.rows_per_sel / k.bn) * 2;
     ta.kc = (nk + k.ks - 1) / k.ks;
@@ -420,8 +476,8 @@ int gemm_tiled_parts(const GemvParams &p) { return (p.rows_per_sel / pick(p, 0).
 std::string gemm_tiled_name(const GemvParams &p, size_t part_bytes) {
     const Pick k = pick(p, part_bytes);
     const TileArgs ta = tile_args(p, k, nullptr);
-    return "k_gemm_tile<" + std::to_string(p.epi) + ", " + std::to_string(k.bn / 32) +
-           (ta.ks > 1 ? ", split " + std::to_string(ta.ks) + ">" : ">");
+    return "k_gemm_tile<" + std::to_string(p.epi) + ", " + std::to_string(k.bn / 32) + ", " +
+           std::to_string(ta.bm / 32) + (ta.ks > 1 ? ", split " + std::to_string(ta.ks) + ">" : ">");
 }
 
 size_t gemm_tiled_part_bytes() { return (size_t)64 << 20; }
