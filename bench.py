@@ -373,6 +373,7 @@ def main():
     P = cfg.prompt_len
     rounds_cap = W + K + 4
     cap = P + rounds_cap * (k + 1) + k + 2
+    cap = max(cap, P + 64 + 2 * k + 4)     # the fixed-context draft step and calibration at P + 64
     prompts = make_prompts(cfg.draft.vocab, P, cfg.batch, cfg.prompt_seed)
     inv_t = 0.0 if args.temperature == 0 else 1.0 / args.temperature
     mlp_mode = 1 if args.mlp_parallel else 0
