@@ -155,6 +155,15 @@ __device__ __noinline__ float gumbel_one(uint64_t seed, uint32_t b, uint32_t pos
     return pick_word(w, v & 3);
 }
 
+// The next RMSNorm's operand (gain-scaled, packed hi / lo) of residual
+// value v at (row gm, column col).
+__device__ __forceinline__ void store_nx(const GemvParams &p, int gm, int col, float v) {
+    uint16_t hi, lo;
+    split2_one(v * p.nx_gain[col], hi, lo);
+    p.nx[(int64_t)gm * p.d + col] = hi;
+    p.nx[(int64_t)(gm + p.nx_packed / 2) * p.d + col] = lo;
+}
+
 // Epilogues of single output rows.  ssv: this row's contribution to the
 // sum of squares of the residual row the epilogue wrote (set member `sel`
 // for parallel-MLP attention outputs, else member 0); best_v / best_i: the
@@ -176,6 +185,7 @@ __device__ __forceinline__ void epi_row(const GemvParams &p, int r, int sel, int
         }
         h[rl] = v;
         ssv = fmaf(v, v, ssv);
+        if (p.nx) store_nx(p, gm, rl, v);
     } else if constexpr (EPI == EPI_ATTN_OUT) {
         const int64_t row = (int64_t)gm * p.d;
         if (!p.par_mlp) {
@@ -184,6 +194,7 @@ __device__ __forceinline__ void epi_row(const GemvParams &p, int r, int sel, int
                 const float v = h[rl] + y;
                 h[rl] = v;
                 ssv = fmaf(v, v, ssv);
+                if (p.nx) store_nx(p, gm, rl, v);
             } else {
                 p.out[(int64_t)sel * p.out_sel_stride + row + rl] = y;
             }

@@ -42,11 +42,25 @@ constexpr int kTK = 256;          // K elements per staged tile
 constexpr int kLD = kTK + 8;      // LDS row stride in elements (16 bytes of padding)
 constexpr int kMaxKS = 8;         // waves per 16-row block
 constexpr int kLogitGrid = 2048;  // workgroups of a sampling product (= arg-max partials per row)
+constexpr int kInvMax = 1536;     // sum-of-squares partials an x_inv product reads (M x xnparts)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &v) {
     bf16x8 r;
     __builtin_memcpy(&r, &v, 16);
     return r;
+}
+
+// 1 / rms of rows m = first, first + step, ... < M from their n sum-of-squares
+// partials ssl[m * n + 0 .. n - 1] into ssl[kInvMax + m]: lane-strided sums,
+// then a fixed xor tree (every workgroup forms the same bits).  Out of line:
+// inlined, its temporaries raise the register budget of the whole kernel.
+__device__ __noinline__ void rows_inv_rms(float *ssl, int M, int n, int K, float eps, int first, int step, int lane) {
+    for (int m = first; m < M; m += step) {
+        float sm = 0.f;
+        for (int k = lane; k < n; k += 64) sm += ssl[m * n + k];
+        sm = wave_sum(sm);
+        if (lane == 0) ssl[kInvMax + m] = 1.0f / sqrtf(sm / (float)K + eps);
+    }
 }
 
 // sum over the 16 lanes of a lane group (fixed xor tree)
@@ -87,6 +101,10 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_mfma(GemvParams p, int ups) {
     constexpr int TILE = 16 * NBU * LDK;    // elements of one wave's LDS tile
     static_assert(NBU * MT * 64 * 16 <= TILE * 2, "reduction area");
     __shared__ __align__(16) uint16_t smem[KS * TILE];
+    // x_inv: the rows' sum-of-squares partials, requested before the weight
+    // stream (NPL per lane over the workgroup) and summed by wave 0 after it
+    constexpr int NPL = kInvMax / (64 * KS);
+    __shared__ float ssl[kInvMax + 16];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int li = lane & 15, lg = lane >> 4;
@@ -144,6 +162,16 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_mfma(GemvParams p, int ups) {
             w[i] = in ? ld16_stream(W0 + (int64_t)(rb[j] + r) * Ks + off) : make_uint4(0, 0, 0, 0);
         }
     };
+    // (straight from global memory into LDS: no registers held across the
+    // weight stream; slots past the rows' partials receive partial 0, unread)
+    const int nss = p.x_inv ? p.M * p.xnparts : 0;
+    if (nss > 0) {
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) {
+            const int i = threadIdx.x + j * 64 * KS;
+            __builtin_amdgcn_global_load_lds(p.xss + (i < nss ? i : 0), &ssl[wave * 64 + j * 64 * KS], 4, 0, 0);
+        }
+    }
     for (int u = blockIdx.x; u < p.n_units; u += gridDim.x) {
         int rb[NBU];
         unit_blocks(u, rb);
@@ -199,15 +227,19 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_mfma(GemvParams p, int ups) {
                 }
             }
         }
-        if (u + (int)gridDim.x < p.n_units && t0 < t1) {
-            int nb[NBU];
-            unit_blocks(u + gridDim.x, nb);
-            load_from(wv, nb, t0);
-            have_first = true;
+        // (only sampling products take several units per workgroup)
+        if constexpr (EPI == EPI_LOGITS) {
+            if (u + (int)gridDim.x < p.n_units && t0 < t1) {
+                int nb[NBU];
+                unit_blocks(u + gridDim.x, nb);
+                load_from(wv, nb, t0);
+                have_first = true;
+            }
         }
         // fixed-order sum of the K parts by wave 0; C layout: lane l,
         // register r holds C[4 * (l / 16) + r][l % 16] = (activation row,
         // weight row of the block)
+        if (nss > 0) __builtin_amdgcn_s_waitcnt(0);   // this wave's copies into LDS have landed
         if (KS > 1) {
             __syncthreads();   // every wave is done with its tile
             f32x4 *red = reinterpret_cast<f32x4 *>(tile);
@@ -224,6 +256,9 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_mfma(GemvParams p, int ups) {
 #pragma unroll
                         for (int t = 0; t < MT; ++t) acc[j][t] += o[(j * MT + t) * 64 + lane];
                 }
+            } else if (nss > 0) {
+                // meanwhile the other waves form 1 / rms of the rows
+                rows_inv_rms(ssl, p.M, p.xnparts, p.K, p.eps, wave - 1, KS - 1, lane);
             }
             __syncthreads();
         }
@@ -249,12 +284,14 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_mfma(GemvParams p, int ups) {
         for (int r = 0; r < 4; ++r) {
             const int m = 4 * lg + r;
             if (m >= p.M) continue;
+            const float sc = nss > 0 ? ssl[kInvMax + m] : 1.f;
             if constexpr (kPair) {
-                epi_pair<uint16_t, EPI>(p, rb[0] + li, rb[0] + li, rb[1] + li, sel, m, res[0][r], res[1][r]);
+                epi_pair<uint16_t, EPI>(p, rb[0] + li, rb[0] + li, rb[1] + li, sel, m, res[0][r] * sc,
+                                        res[1][r] * sc);
             } else {
 #pragma unroll
                 for (int j = 0; j < NBU; ++j)
-                    epi_row<uint16_t, EPI>(p, rb[j] + li, sel, m, res[j][r], ssv[r], best_v[r], best_i[r]);
+                    epi_row<uint16_t, EPI>(p, rb[j] + li, sel, m, res[j][r] * sc, ssv[r], best_v[r], best_i[r]);
             }
         }
         if constexpr (epi_has_ss(EPI)) {
@@ -369,6 +406,8 @@ bool gemm_mfma_supported(const GemvParams &p) {
 }
 
 int gemm_mfma_packed_rows(int M) { return M <= 8 ? 16 : 32; }
+
+int gemm_mfma_inv_max() { return kInvMax; }
 
 // p.n_units counts units of unit_rows weight rows (gemm_mfma_unit_rows).
 hipError_t launch_gemm_mfma(const GemvParams &p, int grid, int ks, int unit_rows, hipStream_t s) {

@@ -171,6 +171,18 @@ struct Fwd {
     Carve c;
     hipStream_t s;
     int nparts[kMaxSel];
+    // the last residual writer also wrote the next RMSNorm operand (gain
+    // nx_gain) for a skinny matrix-core consumer (section fuse_next_norm)
+    bool nx_ready = false;
+    const float *nx_gain = nullptr;
+};
+
+// The X_NORM consumer that follows a stage's last residual write: the next
+// stage's QKV (when that stage is a single layer) or the lm head; gain NULL
+// when there is none to prepare.
+struct NextNorm {
+    const float *gain = nullptr;
+    int rows = 0, pair_block = 0, epi = 0;
 };
 
 // Activation-row count from which bf16 products use the matrix-core kernel
@@ -236,7 +248,7 @@ int packed_rows(const spec_model *m, const GemvParams &consumer) {
 // (X_PLAIN) operand must already be in the form product_path gives (packed
 // rows for the skinny matrix-core kernel, x_sel_stride in its elements).
 // *parts_out: the sum-of-squares or sampling partials each output row now has.
-hipError_t product(const Fwd &f, GemvParams p, int *parts_out = nullptr) {
+hipError_t product(Fwd &f, GemvParams p, int *parts_out = nullptr) {
     const spec_model *m = f.m;
     const int Mtot = p.Mtot;
     p.ss = at<float>(f.ws, f.c.ss);
@@ -276,12 +288,20 @@ hipError_t product(const Fwd &f, GemvParams p, int *parts_out = nullptr) {
         if (parts_out) *parts_out = (p.epi == EPI_LOGITS) ? grid : p.rows_per_sel / ur;
         double xbytes = (double)Mtot * p.K * 4;
         if (p.xmode == X_NORM) {
-            // normalise once into packed operand rows, then stream the weights
             const int n_sel = rows / p.rows_per_sel;
             const int pr = gemm_mfma_packed_rows(Mtot);
             void *xn = at<char>(f.ws, f.c.xn);
-            hipError_t e = launch_norm_rows(m->d.dtype, q, n_sel, xn, pr, f.s);
-            if (e != hipSuccess) return e;
+            if (f.nx_ready && f.nx_gain == p.xgain && n_sel == 1 && !p.xadd && p.xgather_mseq == 0 &&
+                (int64_t)Mtot * p.xnparts <= gemm_mfma_inv_max()) {
+                // the residual writer left gain * h as packed rows: the 1 / rms
+                // scale moves to this product's epilogue
+                q.x_inv = 1;
+            } else {
+                // normalise once into packed operand rows, then stream the weights
+                hipError_t e = launch_norm_rows(m->d.dtype, q, n_sel, xn, pr, f.s);
+                if (e != hipSuccess) return e;
+            }
+            f.nx_ready = false;
             q.xmode = X_PLAIN;
             q.X = xn;
             q.x_sel_stride = (int64_t)pr * p.K;
@@ -308,6 +328,53 @@ hipError_t product(const Fwd &f, GemvParams p, int *parts_out = nullptr) {
     return hipSuccess;
 }
 
+// Norm fusion switch (SPEC_NORM_FUSION=0: every skinny matrix-core consumer
+// normalises its operand in its own pass).
+bool norm_fusion() {
+    static const bool on = [] {
+        const char *e = getenv("SPEC_NORM_FUSION");
+        return !(e && e[0] == '0');
+    }();
+    return on;
+}
+
+// Residual writer prod is followed by an X_NORM consumer of `rows` weight rows
+// (one set member, gain `gain`, epilogue epi).  When both run on the skinny
+// matrix-core kernel, prod also writes that consumer's operand (gain * h,
+// packed) and the consumer scales by 1 / rms in its epilogue instead of a
+// normalisation pass.
+void fuse_next_norm(Fwd &f, GemvParams &prod, const float *gain, int rows, int pair_block, int epi) {
+    f.nx_ready = false;
+    if (!gain || !norm_fusion()) return;
+    const spec_model *m = f.m;
+    GemvParams c{};
+    c.Mtot = prod.Mtot; c.K = m->d.d_model; c.n_units = rows / 2; c.pair_block = pair_block;
+    c.rows_per_sel = rows; c.epi = epi; c.xmode = X_NORM;
+    if (product_path(m, c) != PP_MFMA || product_path(m, prod) != PP_MFMA) return;
+    const int parts = prod.rows_per_sel / mfma_unit_rows(prod);
+    if ((int64_t)prod.Mtot * parts > gemm_mfma_inv_max()) return;
+    prod.nx = at<uint16_t>(f.ws, f.c.xn);
+    prod.nx_packed = gemm_mfma_packed_rows(prod.Mtot);
+    prod.nx_gain = gain;
+    f.nx_ready = true;
+    f.nx_gain = gain;
+}
+
+NextNorm next_qkv(const spec_model *m, int l, int n) {
+    NextNorm nn;
+    if (n != 1) return nn;
+    nn.gain = m->w.attn_norm + (size_t)l * m->d.d_model;
+    nn.rows = m->D; nn.pair_block = m->d.head_dim; nn.epi = EPI_QKV_ROPE;
+    return nn;
+}
+
+NextNorm head_norm(const spec_model *m, int epi) {
+    NextNorm nn;
+    nn.gain = m->w.final_norm;
+    nn.rows = m->d.vocab; nn.pair_block = 2; nn.epi = epi;
+    return nn;
+}
+
 // Embedding, the sum of squares of every row (one partial), RoPE table.
 hipError_t run_embed(Fwd &f, const int32_t *tokens, int64_t tok_ld, int tok_step) {
     const spec_model *m = f.m;
@@ -325,7 +392,8 @@ hipError_t run_embed(Fwd &f, const int32_t *tokens, int64_t tok_ld, int tok_step
 // cos_out (nullable, sequential MLPs only): cos_out[b * cos_stride + l] for
 // each layer l of the set = the cosine between the input its attention read
 // (h0) and the running state a sequential layer would have read there.
-hipError_t run_stage(Fwd &f, int l0, int n, int mlp_mode, float *cos_out = nullptr, int64_t cos_stride = 0) {
+hipError_t run_stage(Fwd &f, int l0, int n, int mlp_mode, const NextNorm &nn = NextNorm{}, float *cos_out = nullptr,
+                     int64_t cos_stride = 0) {
     const spec_model *m = f.m;
     const spec_model_desc &d = m->d;
     const int R = f.batch * f.mseq;
@@ -396,6 +464,8 @@ hipError_t run_stage(Fwd &f, int l0, int n, int mlp_mode, float *cos_out = nullp
     gp.h = h; gp.h0 = h0; gp.par_mlp = par ? 1 : 0;
     gp.out = abuf; gp.out_sel_stride = (int64_t)R * dm;
     gp.n_norm_sel = par ? n : 1;
+    if (!par && !cos_out) fuse_next_norm(f, gp, m->w.ffn_norm + (size_t)l0 * dm, 2 * d.d_ffn, 2 * d.d_ffn, EPI_SILU_MUL);
+    else f.nx_ready = false;
     if ((e = product(f, gp, &grid)) != hipSuccess) return e;
     for (int i = 0; i < gp.n_norm_sel; ++i) f.nparts[i] = grid;
 
@@ -435,6 +505,7 @@ hipError_t run_stage(Fwd &f, int l0, int n, int mlp_mode, float *cos_out = nullp
             gd.h = h;
             gd.add2 = abuf; gd.n_add2 = n; gd.add2_sel_stride = (int64_t)R * dm;
             gd.n_norm_sel = 1;
+            fuse_next_norm(f, gd, nn.gain, nn.rows, nn.pair_block, nn.epi);
             if ((e = product(f, gd, &grid)) != hipSuccess) return e;
             f.nparts[0] = grid;
             return hipSuccess;
@@ -470,6 +541,10 @@ hipError_t run_stage(Fwd &f, int l0, int n, int mlp_mode, float *cos_out = nullp
         // parallel: h += a_i + m_i
         gp.add2 = par ? abuf + (size_t)i * R * dm : (i + 1 < n ? abuf + (size_t)(i + 1) * R * dm : nullptr);
         gp.n_norm_sel = 1;
+        if (cos_out || (par && i + 1 < n)) f.nx_ready = false;
+        else if (i + 1 < n) fuse_next_norm(f, gp, m->w.ffn_norm + (size_t)(l + 1) * dm, 2 * d.d_ffn, 2 * d.d_ffn,
+                                           EPI_SILU_MUL);
+        else fuse_next_norm(f, gp, nn.gain, nn.rows, nn.pair_block, nn.epi);
         if ((e = product(f, gp, &grid)) != hipSuccess) return e;
         f.nparts[0] = grid;
         if (cos_out && i + 1 < n) {
@@ -723,8 +798,8 @@ spec_status spec_draft_attention_cosine(const spec_model *draft, const spec_kv *
     hipError_t e = run_embed(f, tokens, tokens_stride, 0);
     if (e != hipSuccess) return hip_fail(e, "embed");
     for (int s = 0; s < n_stages; ++s) {
-        e = run_stage(f, plan_offsets[s], plan_offsets[s + 1] - plan_offsets[s], SPEC_MLP_SEQUENTIAL, cos_out,
-                      cos_stride);
+        e = run_stage(f, plan_offsets[s], plan_offsets[s + 1] - plan_offsets[s], SPEC_MLP_SEQUENTIAL, NextNorm{},
+                      cos_out, cos_stride);
         if (e != hipSuccess) return hip_fail(e, "cosine stage");
     }
     return SPEC_OK;
@@ -752,7 +827,9 @@ spec_status spec_draft_group_step(const spec_model *draft, const spec_kv *kv, co
     hipError_t e = run_embed(f, tokens, tokens_stride, 0);
     if (e != hipSuccess) return hip_fail(e, "embed");
     for (int s = 0; s < n_stages; ++s) {
-        e = run_stage(f, plan_offsets[s], plan_offsets[s + 1] - plan_offsets[s], flags);
+        const NextNorm nn = s + 1 < n_stages ? next_qkv(draft, plan_offsets[s + 1], plan_offsets[s + 2] - plan_offsets[s + 1])
+                                             : head_norm(draft, EPI_LOGITS);
+        e = run_stage(f, plan_offsets[s], plan_offsets[s + 1] - plan_offsets[s], flags, nn);
         if (e != hipSuccess) return hip_fail(e, "draft stage");
     }
     // the sampled token is the one at position positions[b] + 1
@@ -787,13 +864,13 @@ spec_status spec_draft_group_step_noalloc(const spec_model *draft, const spec_kv
 static spec_status precise_forward(const spec_model *m, const spec_kv *kv, int batch, const int32_t *tokens,
                                    int tokens_stride, const int32_t *start_pos, const int32_t *n_tokens, int mseq,
                                    int max_pos,
-                                   void *ws, hipStream_t s, Fwd &f) {
+                                   void *ws, hipStream_t s, Fwd &f, const NextNorm &head) {
     f = Fwd{m, kv, batch, mseq, max_pos, RowMap{start_pos, n_tokens, mseq, kv->capacity}, ws,
             carve(m, batch, mseq, 1), s, {0}};
     hipError_t e = run_embed(f, tokens, tokens_stride, 1);
     if (e != hipSuccess) return hip_fail(e, "embed");
     for (int l = 0; l < m->d.n_layers; ++l) {
-        e = run_stage(f, l, 1, SPEC_MLP_SEQUENTIAL);
+        e = run_stage(f, l, 1, SPEC_MLP_SEQUENTIAL, l + 1 < m->d.n_layers ? next_qkv(m, l + 1, 1) : head);
         if (e != hipSuccess) return hip_fail(e, "layer");
     }
     return SPEC_OK;
@@ -817,8 +894,9 @@ spec_status spec_calibrate_kv(const spec_model *draft, const spec_kv *kv, int ba
     if (!(inv_temperature >= 0.f)) return fail(SPEC_ERR_INVALID_ARG, "inv_temperature must be >= 0");
     if ((st = check_ws(draft, batch, max_m, 1, workspace, ws_bytes))) return st;
     Fwd f;
+    // the head reads each sequence's last valid row: no operand to prepare
     if ((st = precise_forward(draft, kv, batch, tokens, tokens_stride, start_pos, n_tokens, max_m, max_pos,
-                              workspace, (hipStream_t)stream, f)))
+                              workspace, (hipStream_t)stream, f, NextNorm{})))
         return st;
     // the sampled token is the one after the last calibrated position:
     // start_pos[b] + n_tokens[b] (n_tokens NULL: every sequence has max_m)
@@ -840,7 +918,7 @@ spec_status spec_verify_forward(const spec_model *base, const spec_kv *kv, int b
     if ((st = check_ws(base, batch, m, 1, workspace, ws_bytes))) return st;
     Fwd f;
     if ((st = precise_forward(base, kv, batch, tokens, m, start_pos, nullptr, m, max_pos, workspace,
-                              (hipStream_t)stream, f)))
+                              (hipStream_t)stream, f, logits_out ? head_norm(base, EPI_STORE) : NextNorm{})))
         return st;
     if (logits_out) {
         hipError_t e = run_head(f, false, nullptr, logits_out, base->d.vocab, 0.f, 0, nullptr, nullptr, 0, nullptr, 1);

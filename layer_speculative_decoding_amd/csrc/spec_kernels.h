@@ -65,6 +65,18 @@ struct GemvParams {
     int64_t x_seg_stride; //   of activation row m at X + s * x_seg_stride + m * (K / kseg)
     int act_packed;       // SILU_MUL: 0 -> float32 act rows; PR -> packed bf16
                           //   operand rows (hi at row m, lo at row m + PR / 2)
+    // RESID_ADD / sequential ATTN_OUT, nx != NULL: also write the next
+    // RMSNorm's operand for a skinny matrix-core consumer, the new residual
+    // value times nx_gain[col] as packed bf16 rows [nx_packed][d] (hi at row
+    // m, lo at row m + nx_packed / 2); the consumer scales its outputs by the
+    // row's 1 / rms (x_inv)
+    uint16_t *nx;
+    int nx_packed;
+    const float *nx_gain;
+    // skinny matrix-core consumer: X holds gain * h rows; every output of row m
+    // is multiplied by 1 / rms(h_m) formed from the xss partials (m * xnparts
+    // + 0 .. xnparts - 1, at most gemm_mfma_inv_max() of them in all)
+    int x_inv;
     int xgather_mseq;     // > 0: activation row m reads residual row
     const int32_t *xgather_ntok;   //   m * mseq + ntok[m] - 1 (last valid row)
     const float *bias;    // [rows] or NULL
@@ -150,6 +162,7 @@ hipError_t launch_norm_rows(int dtype, const GemvParams &p, int n_sel, void *xn,
 bool gemm_mfma_supported(const GemvParams &p);
 int gemm_mfma_max_rows();
 int gemm_mfma_packed_rows(int M);
+int gemm_mfma_inv_max();   // largest M x xnparts an x_inv product takes
 int gemm_mfma_grid(const GemvParams &p);
 int gemm_mfma_splits(const GemvParams &p);
 
