@@ -42,7 +42,9 @@ constexpr int kTK = 256;          // K elements per staged tile
 constexpr int kLD = kTK + 8;      // LDS row stride in elements (16 bytes of padding)
 constexpr int kMaxKS = 8;         // waves per 16-row block
 constexpr int kLogitGrid = 2048;  // workgroups of a sampling product (= arg-max partials per row)
-constexpr int kInvMax = 1536;     // sum-of-squares partials an x_inv product reads (M x xnparts)
+// sum-of-squares partials an x_inv product reads (M x xnparts): 2048 with one
+// operand tile (its LDS beside two paired workgroups per CU), 4096 with two
+constexpr int inv_max(int MT) { return MT == 1 ? 2048 : 4096; }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &v) {
     bf16x8 r;
@@ -51,15 +53,16 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &v) {
 }
 
 // 1 / rms of rows m = first, first + step, ... < M from their n sum-of-squares
-// partials ssl[m * n + 0 .. n - 1] into ssl[kInvMax + m]: lane-strided sums,
+// partials ssl[m * n + 0 .. n - 1] into ssl[off + m]: lane-strided sums,
 // then a fixed xor tree (every workgroup forms the same bits).  Out of line:
 // inlined, its temporaries raise the register budget of the whole kernel.
-__device__ __noinline__ void rows_inv_rms(float *ssl, int M, int n, int K, float eps, int first, int step, int lane) {
+__device__ __noinline__ void rows_inv_rms(float *ssl, int off, int M, int n, int K, float eps, int first, int step,
+                                         int lane) {
     for (int m = first; m < M; m += step) {
         float sm = 0.f;
         for (int k = lane; k < n; k += 64) sm += ssl[m * n + k];
         sm = wave_sum(sm);
-        if (lane == 0) ssl[kInvMax + m] = 1.0f / sqrtf(sm / (float)K + eps);
+        if (lane == 0) ssl[off + m] = 1.0f / sqrtf(sm / (float)K + eps);
     }
 }
 
@@ -103,8 +106,9 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_mfma(GemvParams p, int ups) {
     __shared__ __align__(16) uint16_t smem[KS * TILE];
     // x_inv: the rows' sum-of-squares partials, requested before the weight
     // stream (NPL per lane over the workgroup) and summed by wave 0 after it
-    constexpr int NPL = kInvMax / (64 * KS);
-    __shared__ float ssl[kInvMax + 16];
+    constexpr int INV = inv_max(MT);
+    constexpr int NPL = INV / (64 * KS);
+    __shared__ float ssl[INV + 16];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int li = lane & 15, lg = lane >> 4;
@@ -258,7 +262,7 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_mfma(GemvParams p, int ups) {
                 }
             } else if (nss > 0) {
                 // meanwhile the other waves form 1 / rms of the rows
-                rows_inv_rms(ssl, p.M, p.xnparts, p.K, p.eps, wave - 1, KS - 1, lane);
+                rows_inv_rms(ssl, INV, p.M, p.xnparts, p.K, p.eps, wave - 1, KS - 1, lane);
             }
             __syncthreads();
         }
@@ -284,7 +288,7 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_mfma(GemvParams p, int ups) {
         for (int r = 0; r < 4; ++r) {
             const int m = 4 * lg + r;
             if (m >= p.M) continue;
-            const float sc = nss > 0 ? ssl[kInvMax + m] : 1.f;
+            const float sc = nss > 0 ? ssl[INV + m] : 1.f;
             if constexpr (kPair) {
                 epi_pair<uint16_t, EPI>(p, rb[0] + li, rb[0] + li, rb[1] + li, sel, m, res[0][r] * sc,
                                         res[1][r] * sc);
@@ -407,7 +411,7 @@ bool gemm_mfma_supported(const GemvParams &p) {
 
 int gemm_mfma_packed_rows(int M) { return M <= 8 ? 16 : 32; }
 
-int gemm_mfma_inv_max() { return kInvMax; }
+int gemm_mfma_inv_max(int M) { return inv_max(M <= 8 ? 1 : 2); }
 
 // p.n_units counts units of unit_rows weight rows (gemm_mfma_unit_rows).
 hipError_t launch_gemm_mfma(const GemvParams &p, int grid, int ks, int unit_rows, hipStream_t s) {

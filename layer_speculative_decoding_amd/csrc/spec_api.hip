@@ -292,7 +292,7 @@ hipError_t product(Fwd &f, GemvParams p, int *parts_out = nullptr) {
             const int pr = gemm_mfma_packed_rows(Mtot);
             void *xn = at<char>(f.ws, f.c.xn);
             if (f.nx_ready && f.nx_gain == p.xgain && n_sel == 1 && !p.xadd && p.xgather_mseq == 0 &&
-                (int64_t)Mtot * p.xnparts <= gemm_mfma_inv_max()) {
+                (int64_t)Mtot * p.xnparts <= gemm_mfma_inv_max(Mtot)) {
                 // the residual writer left gain * h as packed rows: the 1 / rms
                 // scale moves to this product's epilogue
                 q.x_inv = 1;
@@ -352,7 +352,7 @@ void fuse_next_norm(Fwd &f, GemvParams &prod, const float *gain, int rows, int p
     c.rows_per_sel = rows; c.epi = epi; c.xmode = X_NORM;
     if (product_path(m, c) != PP_MFMA || product_path(m, prod) != PP_MFMA) return;
     const int parts = prod.rows_per_sel / mfma_unit_rows(prod);
-    if ((int64_t)prod.Mtot * parts > gemm_mfma_inv_max()) return;
+    if ((int64_t)prod.Mtot * parts > gemm_mfma_inv_max(prod.Mtot)) return;
     prod.nx = at<uint16_t>(f.ws, f.c.xn);
     prod.nx_packed = gemm_mfma_packed_rows(prod.Mtot);
     prod.nx_gain = gain;

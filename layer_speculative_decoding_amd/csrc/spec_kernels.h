@@ -75,7 +75,7 @@ struct GemvParams {
     const float *nx_gain;
     // skinny matrix-core consumer: X holds gain * h rows; every output of row m
     // is multiplied by 1 / rms(h_m) formed from the xss partials (m * xnparts
-    // + 0 .. xnparts - 1, at most gemm_mfma_inv_max() of them in all)
+    // + 0 .. xnparts - 1, at most gemm_mfma_inv_max(M) of them in all)
     int x_inv;
     int xgather_mseq;     // > 0: activation row m reads residual row
     const int32_t *xgather_ntok;   //   m * mseq + ntok[m] - 1 (last valid row)
@@ -162,7 +162,7 @@ hipError_t launch_norm_rows(int dtype, const GemvParams &p, int n_sel, void *xn,
 bool gemm_mfma_supported(const GemvParams &p);
 int gemm_mfma_max_rows();
 int gemm_mfma_packed_rows(int M);
-int gemm_mfma_inv_max();   // largest M x xnparts an x_inv product takes
+int gemm_mfma_inv_max(int M);   // largest M x xnparts an x_inv product of M rows takes
 int gemm_mfma_grid(const GemvParams &p);
 int gemm_mfma_splits(const GemvParams &p);
 
