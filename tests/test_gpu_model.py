@@ -274,22 +274,27 @@ def test_prompt_prefill_matches_oracle(name, tile, monkeypatch):
     assert ek < tol and ev < tol
 
 
-@pytest.mark.parametrize("hq,hkv,hd", [(4, 4, 64), (8, 4, 128), (14, 2, 64), (16, 2, 128), (16, 1, 64)])
-def test_prompt_attention_group_sizes(hq, hkv, hd):
+@pytest.mark.parametrize("hq,hkv,hd,tight", [(4, 4, 64, False), (8, 4, 128, False), (14, 2, 64, False),
+                                             (16, 2, 128, False), (16, 1, 64, False), (8, 4, 128, True),
+                                             (14, 2, 64, True)])
+def test_prompt_attention_group_sizes(hq, hkv, hd, tight):
     """Prompt-length prefills through the flash-style prompt attention (one
     workgroup per 16 * (8 / G) rows of one kv head, two 16-row blocks per
     wave; G = 16 falls back to the decode kernel) at q heads per kv head
-    G = 1, 2, 7, 8, 16, ragged last row tile, a ragged second sequence."""
+    G = 1, 2, 7, 8, 16, ragged last row tile, a ragged second sequence;
+    tight: the KV capacity equals the prompt length (the last row's keys end
+    at the cache's last slot)."""
     from layer_speculative_decoding_amd import api
     shape = tiny_shape(2, hq * hd // 2, hq, hkv, hd, 256, 512, dtype=BF16)
     w = make_weights(shape, 11, gain_std=0.1, std=0.05)
     om = OracleModel.from_torch(shape, w)
     gm = api.SpecModel(shape, to_dev(w))
     B, P = 2, 83
-    gkv = api.KVCache(shape, B, P + 4)
-    okv = KVCache(shape, B, P + 4)
+    cap = P if tight else P + 4
+    gkv = api.KVCache(shape, B, cap)
+    okv = KVCache(shape, B, cap)
     prompts = np.random.default_rng(3).integers(0, shape.vocab, size=(B, P)).astype(np.int32)
-    say(f"prompt attention hq={hq} hkv={hkv} hd={hd} B={B} P={P}")
+    say(f"prompt attention hq={hq} hkv={hkv} hd={hd} B={B} P={P} capacity={cap}")
     wsb = ws(api.spec_workspace_bytes(gm, B, P, 1))
     lens = np.array([P, P - 30], dtype=np.int32)
     last = torch.zeros(B, shape.vocab, device="cuda")
