@@ -12,11 +12,14 @@
 //        each lane's K slice is contiguous in memory.  With a bfloat16 cache
 //        and head_dim a multiple of 32 the slices are eight dims, exactly the
 //        operand of v_mfma_f32_16x16x32_bf16: K goes in as loaded and q as
-//        three bfloat16 pieces (hi + mid + lo, float32 precision), three
-//        products per 32 dims instead of eight float32 ones, which matters
-//        where the matrix cores bound the kernel (long contexts, many rows);
-//   softmax  online (running max and sum per query vector) in float32; the
-//        scores of query vector c sit in lane group column c;
+//        two bfloat16 pieces (hi + lo, within 2^-16 of the float32 value: the
+//        products' operand precision), two products per 32 dims instead of
+//        eight float32 ones, which matters where the matrix cores bound the
+//        kernel (long contexts, many rows);
+//   softmax  online (running max and sum per query vector) in float32, the
+//        scores in log2 units (1/sqrt(hd) * log2(e)) so that v_exp_f32 (2^x)
+//        forms the weights; the scores of query vector c sit in lane group
+//        column c;
 //   PV   O[qv][dim] += P[qv][key] V[key][dim]: the probabilities are used in
 //        place as the A operand, lane (c, g) supplies V[key 4g + r][dims
 //        (HD / 16) c ...], so each lane reads HD / 16 contiguous elements.
@@ -26,10 +29,10 @@
 //        summed keys inside one instruction is free as long as B matches);
 //        the chunk's V rows go to a per-wave LDS stage and each lane reads
 //        back the same eight keys of one dim (V is key-major in the cache, the
-//        instruction wants eight keys per lane), P in three bfloat16 pieces.
-// Every product input is exact in float32 (K, V widened from the cache type;
-// q's pieces sum to q up to the last bit of its float32 mantissa), so the
-// result equals the float32 dot products up to summation and that rounding.  The
+//        instruction wants eight keys per lane), P in two bfloat16 pieces.
+// K and V enter exactly (bfloat16 in the cache); each piece times them is
+// exact in float32, so the result equals the float32 dot products of the
+// pieces' sums (within 2^-16 of q and P) up to summation order.  The
 // waves' (max, sum, output) are merged in wave order through LDS; with several
 // key splits the workgroup publishes them and k_attn_merge combines the splits
 // in split order.
@@ -55,28 +58,6 @@ __device__ __forceinline__ bf16x8 as_bf16x8u(const uint4 &v) {
     bf16x8 r;
     __builtin_memcpy(&r, &v, 16);
     return r;
-}
-
-// Eight float32 values as three bfloat16 pieces hi + mid + lo whose sum
-// carries the value to float32 precision (each piece is the round-to-nearest
-// bfloat16 of what the previous pieces leave, and each subtraction is exact).
-// A bfloat16 K times a piece is exact in float32, so three matrix products on
-// the bfloat16 matrix cores give the float32 dot products up to summation
-// order (the float32 matrix instruction takes four dims per step, the
-// bfloat16 one thirty-two).
-__device__ __forceinline__ void split3_bf16(const float *x, bf16x8 &hi, bf16x8 &mid, bf16x8 &lo) {
-    uint16_t h[8], m[8], l[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        h[e] = f32_to_bf16(x[e]);
-        const float r1 = x[e] - bf16_to_f32(h[e]);
-        m[e] = f32_to_bf16(r1);
-        const float r2 = r1 - bf16_to_f32(m[e]);
-        l[e] = f32_to_bf16(r2);
-    }
-    __builtin_memcpy(&hi, h, 16);
-    __builtin_memcpy(&mid, m, 16);
-    __builtin_memcpy(&lo, l, 16);
 }
 
 // N consecutive elements of the cache type, widened to float.
@@ -192,7 +173,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
     constexpr int QVB = 16 * NQB;
     constexpr int NREG = NQB * DV * 4;            // output values per lane
     // bfloat16 caches with 8 dims per lane and piece run both products on the
-    // bfloat16 matrix cores (see split3_bf16): QK with the K slices as loaded,
+    // bfloat16 matrix cores (two pieces per float32 operand): QK with the K slices as loaded,
     // PV over 32-key chunks whose V rows are staged per wave in LDS and read
     // back key-contiguous per lane, the layout of the B operand
     constexpr bool kBf = sizeof(T) == 2 && DK == 8;
@@ -236,7 +217,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
     const int nrows = min(QB, mseq - i0);
     const int ntok = p.rows.n_tok ? p.rows.n_tok[b] : mseq;
     const int pos0 = p.rows.start_pos[b];
-    const float scale = 1.0f / sqrtf((float)HD);
+    // scores in log2 units (1/sqrt(hd) * log2(e)); exp2 forms the weights
+    const float scale = 1.4426950408889634f / sqrtf((float)HD);
     const QvMap qm{G, nrows * G, b * mseq + i0, kvh * G};
 
     // keys 0 .. kmax serve this block (rows hold consecutive positions)
@@ -322,12 +304,12 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
     }
 
     // q as three bfloat16 pieces (B operand of QK on the bfloat16 path)
-    bf16x8 qh[kBf ? NQB : 1][kBf ? NP : 1], qm2[kBf ? NQB : 1][kBf ? NP : 1], ql[kBf ? NQB : 1][kBf ? NP : 1];
+    uint4 qh[kBf ? NQB : 1][kBf ? NP : 1], ql[kBf ? NQB : 1][kBf ? NP : 1];
     if constexpr (kBf) {
 #pragma unroll
         for (int nb = 0; nb < NQB; ++nb)
 #pragma unroll
-            for (int i = 0; i < NP; ++i) split3_bf16(&qreg[nb][DK * i], qh[nb][i], qm2[nb][i], ql[nb][i]);
+            for (int i = 0; i < NP; ++i) split2_bf16_hw(&qreg[nb][DK * i], qh[nb][i], ql[nb][i]);
     }
 
     float m_run[NQB], l_run[NQB];
@@ -369,10 +351,9 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
                     for (int i = 0; i < NP; ++i) {
                         bf16x8 kv;
                         __builtin_memcpy(&kv, kc2[hb][i].w, 16);
-                        // the small pieces first
-                        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, ql[nb][i], sc, 0, 0, 0);
-                        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qm2[nb][i], sc, 0, 0, 0);
-                        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qh[nb][i], sc, 0, 0, 0);
+                        // the small piece first
+                        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, as_bf16x8u(ql[nb][i]), sc, 0, 0, 0);
+                        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, as_bf16x8u(qh[nb][i]), sc, 0, 0, 0);
                     }
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
@@ -388,12 +369,12 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
                 float sum = 0.f;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    pr[j] = none ? 0.f : expf(pr[j] - m_new);
+                    pr[j] = none ? 0.f : __builtin_amdgcn_exp2f(pr[j] - m_new);
                     sum += pr[j];
                 }
                 sum += __shfl_xor(sum, 16, kWave);
                 sum += __shfl_xor(sum, 32, kWave);
-                const float corr = none ? 1.f : expf(m_run[nb] - m_new);
+                const float corr = none ? 1.f : __builtin_amdgcn_exp2f(m_run[nb] - m_new);
                 l_run[nb] = l_run[nb] * corr + sum;
                 m_run[nb] = m_new;
                 f32x4 cr;
@@ -403,8 +384,9 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
                 for (int j = 0; j < DV; ++j) acc[nb][j] *= cr;
                 // PV: A = P[qv c][keys of lane group g: 4g..4g+3, 16+4g..16+4g+3]
                 // (as the QK output holds them), B = V[the same keys][dim DV c + j]
-                bf16x8 ph, pm, pl;
-                split3_bf16(pr, ph, pm, pl);
+                uint4 ph4, pl4;
+                split2_bf16_hw(pr, ph4, pl4);
+                const bf16x8 ph = as_bf16x8u(ph4), pl = as_bf16x8u(pl4);
 #pragma unroll
                 for (int j = 0; j < DV; ++j) {
                     uint16_t vv[8];
@@ -416,7 +398,6 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
                     bf16x8 vb;
                     __builtin_memcpy(&vb, vv, 16);
                     acc[nb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, acc[nb][j], 0, 0, 0);
-                    acc[nb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pm, vb, acc[nb][j], 0, 0, 0);
                     acc[nb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, acc[nb][j], 0, 0, 0);
                 }
             }
@@ -456,12 +437,12 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
                 float sum = 0.f;
     #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    pr[r] = none ? 0.f : expf(pr[r] - m_new);
+                    pr[r] = none ? 0.f : __builtin_amdgcn_exp2f(pr[r] - m_new);
                     sum += pr[r];
                 }
                 sum += __shfl_xor(sum, 16, kWave);
                 sum += __shfl_xor(sum, 32, kWave);
-                const float corr = none ? 1.f : expf(m_run[nb] - m_new);
+                const float corr = none ? 1.f : __builtin_amdgcn_exp2f(m_run[nb] - m_new);
                 l_run[nb] = l_run[nb] * corr + sum;
                 m_run[nb] = m_new;
                 // rescale of the outputs of query vectors 16 nb + 4 g + r (held by lane 4 g + r)
@@ -514,7 +495,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
             float wt[kWaves], L = 0.f;
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) {
-                wt[w] = mw[w] == -INFINITY ? 0.f : expf(mw[w] - M);
+                wt[w] = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - M);
                 L = fmaf(wt[w], l_s[w][qv], L);
             }
             float ov[DV];
@@ -549,7 +530,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
 // launch: merging in the last split's workgroup behind an agent-scope fence
 // and a counter measured 3 us slower per call, the fence writing the XCD's
 // L2 back): out = sum_s w_s
-// acc_s / sum_s w_s l_s with w_s = exp(m_s - max_s m_s).  Lane s reads split
+// acc_s / sum_s w_s l_s with w_s = 2^(m_s - max_s m_s) (scores in log2 units).  Lane s reads split
 // s's (m, l); the weights' sum uses a fixed reduction tree and the outputs
 // accumulate in split order.
 template <typename T>
@@ -566,7 +547,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnParams p) {
         l = p.part_ml[(item + lane * stride_sp) * 2 + 1];
     }
     const float mx = wave_max(m);
-    const float w = (lane < p.splits && m != -INFINITY) ? expf(m - mx) : 0.f;
+    const float w = (lane < p.splits && m != -INFINITY) ? __builtin_amdgcn_exp2f(m - mx) : 0.f;
     const float den = wave_sum(w * l);
     const int gi = (int)(item / ((int64_t)p.Mtot * p.hq));
     const int64_t rh = item - (int64_t)gi * p.Mtot * p.hq;       // row * hq + head
