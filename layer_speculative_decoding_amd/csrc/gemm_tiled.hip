@@ -26,6 +26,9 @@
 //    8 lanes) and 32 bytes of activations, the weights two (128-row tiles) or
 //    three (64-row) steps ahead of the matrix instructions (HBM latency), the
 //    activations one step ahead (they stay in L2);
+//  * workgroups take tiles in an XCD-aware grouped order (tile_of), so the
+//    tiles resident on one XCD at a time share a few activation and weight
+//    tiles in that XCD's L2;
 //  * the 64-row weight tile is chosen when 128-row tiles would leave CUs
 //    without a workgroup, and when even those are too few, K is split: each
 //    K slice stores its float32 accumulators, and a second kernel adds the
@@ -64,12 +67,37 @@ __device__ __forceinline__ float sum16(float v) {
 
 struct TileArgs {
     int gm, gn;        // activation tiles, weight tiles
+    int grp;           // > 0: XCD-aware grouped tile order (activation tiles per group)
     int bm;            // activation rows per tile (32 WMB)
     int parts;         // sum-of-squares partials per row and set member
     int ks;            // K slices (1: no split)
     int kc;            // K steps per slice
     float *part;       // ks > 1: [ks][tile][WMB * WNB][256 lanes] float4
 };
+
+// Tile of workgroup b (0 <= b < T) when several activation tiles share each
+// weight tile.  The dispatcher deals workgroups to the eight XCDs in turn
+// (b % 8), and each XCD has its own L2; so XCD x gets the contiguous run x of
+// the logical order, and that order walks groups of ta.grp activation tiles
+// across all weight tiles, activation tile fastest.  The workgroups one XCD
+// holds at a time then share about grp activation tiles and (resident / grp)
+// weight tiles, where the plain order (activation tile fastest over all of
+// them) gave every XCD a different activation tile for every workgroup of a
+// 256-tile-high product.  A bijection of [0, T): the result is the plain
+// index nt * gm + mt.
+__device__ __forceinline__ int tile_of(const TileArgs &ta, int b) {
+    if (ta.grp <= 0 || ta.gm < 2) return b;
+    const int T = ta.gm * ta.gn;
+    const int xcd = b & 7, i = b >> 3;
+    const int per = T >> 3, extra = T & 7;
+    const int L = xcd * per + min(xcd, extra) + i;
+    const int G = min(ta.gm, ta.grp);
+    const int group = L / (G * ta.gn);
+    const int first = group * G;
+    const int gsz = min(G, ta.gm - first);
+    const int w = L - first * ta.gn;
+    return (w / gsz) * ta.gm + first + w % gsz;
+}
 
 // Where tile t sits: first activation row, first weight row (unpaired), first
 // unit (paired), set member.
@@ -162,7 +190,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(GemvParams p, TileArgs ta)
     const int li = lane & 15, lg = lane >> 4;
     const int K = p.K;
     const int T = ta.gm * ta.gn;
-    const int t = SPLIT ? (int)blockIdx.x % T : (int)blockIdx.x;
+    const int t = tile_of(ta, SPLIT ? (int)blockIdx.x % T : (int)blockIdx.x);
     const int slice = SPLIT ? (int)blockIdx.x / T : 0;
     const TilePos q = tile_pos<EPI, BN>(p, ta, t);
     const int kbeg = slice * ta.kc;
@@ -415,6 +443,16 @@ int tile_rows(int M) {
     }();
     return (small && M <= 32) ? 32 : 128;
 }
+// Activation tiles per group of the XCD-aware tile order (SPEC_TILE_GROUP,
+// read at every call like SPEC_TILE; 0: plain order).  Measured on the
+// 70B-shaped prefill (four 8192-token prompts as one 32768-row call, 256
+// activation tiles per product): 16.1 s in plain order, 12.0-12.3 s with
+// groups of 2 or 4, 12.5 s with 1, 13.4 s with 8; the 2048- and 512-row
+// prefills gain 0.5-2 %.
+int tile_group() {
+    const char *e = getenv("SPEC_TILE_GROUP");
+    return e ? atoi(e) : 4;
+}
 Pick pick(const GemvParams &p, size_t part_bytes) {
     const int rows = p.n_units * 2, nk = p.K / kBK;
     const int bm = tile_rows(p.M);
@@ -448,6 +486,7 @@ TileArgs tile_args(const GemvParams &p, Pick k, float *part) {
     const int nk = p.K / kBK;
     ta.bm = tile_rows(p.M);
     ta.gm = (p.M + ta.bm - 1) / ta.bm;
+    ta.grp = tile_group();
     ta.gn = (p.n_units * 2) / k.bn;
     ta.parts = (p.rows_per_sel / k.bn) * 2;
     ta.kc = (nk + k.ks - 1) / k.ks;
