@@ -593,7 +593,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_prompt(AttnParams p, int QR) {
     constexpr int NQB = 2;                 // 16-vector blocks per wave
     constexpr int NS = HD / 32;            // 32-dim steps of QK
     constexpr int NJ = HD / 16;            // 16-dim blocks of PV
-    constexpr int KLD = HD + 8;            // K row stride in LDS (elements)
+    constexpr int KLD = HD + 16;           // K row stride in LDS (elements: 160 or 288 bytes, where the
+                                           // fragment reads are free of bank conflicts)
     constexpr int VLD = KT + 4;            // transposed V row stride (elements)
     __shared__ __align__(16) uint16_t ks[KT * KLD];
     __shared__ __align__(16) uint16_t vt[HD * VLD];

@@ -96,7 +96,11 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_mfma(GemvParams p, int ups) {
     constexpr bool kPair = epi_is_pair(EPI);
     constexpr int NBU = kPair ? 2 : 1;      // 16-row blocks per unit
     constexpr int TKL = kTK / NBU;          // K elements per tile
-    constexpr int LDK = TKL + 8;            // LDS row stride (16 bytes of padding)
+    // LDS row stride: 544 bytes for the 256-element tiles, where a wave's
+    // fragment reads meet every bank once (at 528 bytes: twice); the paired
+    // tiles keep 272 bytes (two-way conflicts), since 288 would put two
+    // eight-wave workgroups and their partial-sum area past the CU's 160 KB
+    constexpr int LDK = TKL + (kPair ? 8 : 16);
     constexpr int RPL = 512 / TKL;          // weight rows per 16-byte-per-lane load
     constexpr int NL = 8;                   // loads per lane per tile
     constexpr int BL = NL / NBU;            // of them per block

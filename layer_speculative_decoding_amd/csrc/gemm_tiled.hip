@@ -20,7 +20,7 @@
 //    activations to within 2^-16 of their magnitude; a tile with fewer call
 //    rows than its 128 (verify rows of a few sequences) stashes and
 //    multiplies only the 16-row blocks that hold rows;
-//  * K advances in 64-element steps through one LDS stage (rows padded by 16
+//  * K advances in 64-element steps through one LDS stage (rows padded by 32
 //    bytes, so the fragment reads of a wave spread over all banks); each
 //    lane moves 16 bytes of weights per row (128 contiguous bytes per row per
 //    8 lanes) and 32 bytes of activations, the weights two (128-row tiles) or
@@ -48,7 +48,11 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBK = 64;           // K elements per step
-constexpr int kLDK = kBK + 8;     // LDS row stride in elements (16 bytes of padding)
+// LDS row stride in elements: 160 bytes.  A fragment read (16 rows x 16
+// bytes at four K offsets) meets every bank once at a 160-byte stride and
+// twice at 144 (hardware conflict counters on a one-wave probe: 4 cycles per
+// ds_read_b128 against 8); the stash writes are conflict-free at both.
+constexpr int kLDK = kBK + 16;
 // activation rows per tile: 2 wave rows of WMB 16-row blocks (WMB = 4: 128
 // rows for prompt-length calls, WMB = 1: 32 rows for calls of at most 32)
 constexpr int kMaxSplit = 8;
