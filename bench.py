@@ -108,7 +108,12 @@ def pmc_summary(fetch_csv, write_csv, kernels, command):
     print(f"source_sha256: {kernel_source_hash()}")
 
 
-def pmc_mfma_summary(csv_path, command):
+def mfma_profile_name(cfg):
+    """File name of a workload's matrix-core utilisation summary under profiles/."""
+    return "mfma_util.md" if cfg.name == "llama-1b-8b" else f"mfma_util_{cfg.name}.md"
+
+
+def pmc_mfma_summary(csv_path, command, cfg):
     """Markdown summary of one counter run of `bench.py --pmc-probe` with the
     matrix-core counters: per kernel family, the matrix-core flops the
     hardware counted (MOPS x 512), the dispatch durations (the run's own
@@ -144,10 +149,15 @@ def pmc_mfma_summary(csv_path, command):
     for c in command:
         print(f"    {c}")
     print()
-    print("The run covers the llama-1b-8b workload: three prompt prefills (base 511 rows, draft 512 rows:"
-          " k_gemm_tile), then four rounds of draft steps (k_gemv, one row), verify and calibration (k_gemm_mfma,"
-          " 6 rows) and attention (k_attn: bf16 matrix instructions on the bf16 caches, q and the probabilities in three bf16 pieces; k_attn_prompt for the prompt prefills: two pieces).  Flops are what the matrix cores"
-          " executed (padding rows included); the bf16 peak is 2500 TFLOP/s, the float32 one 157.3.")
+    B, P = cfg.batch, cfg.prompt_len
+    print(f"The run covers the {cfg.name} workload ({B} sequence{'s' if B > 1 else ''} of {P} prompt tokens, "
+          f"k = {cfg.k}, N = {cfg.group_size}): three prompt prefills (base {P - 1} rows, draft {P} rows per "
+          f"sequence, {'all sequences in one call; ' if B > 1 else ''}products on k_gemm_tile, attention on "
+          "k_attn_prompt), then the warm-up and three probe rounds: draft steps, verify and calibration on "
+          "k_gemv, k_gemm_mfma or k_gemm_tile by their row count, attention on k_attn (bf16 matrix "
+          "instructions on the bf16 caches; q and the probabilities enter them as two bf16 pieces in both "
+          "attention kernels).  Flops are what the matrix cores executed (padding rows and both pieces "
+          "included); the bf16 peak is 2500 TFLOP/s, the float32 one 157.3.")
     print()
     top, ft = max(fam.items(), key=lambda kv: kv[1]["ns"])
     print(f"GRBM_GUI_ACTIVE / 8 per ns of `{top}` (the longest-running kernel): {ft['gui'] / 8 / ft['ns']:.2f} GHz.")
@@ -192,8 +202,9 @@ def rocprof_summary(stats_csv, trace_csv, command, cfg):
           f"k = {cfg.k}, layer-parallel set size N = {cfg.group_size}, batch {cfg.batch}, greedy; the prompt "
           "prefills (k_gemm_tile), the warm-up, timed and instrumented rounds of the command below, and the "
           "weight generation (the at::native kernels).  Template arguments: k_gemm_mfma<row tiles, epilogue, "
-          "waves per block>, "
-          "k_gemv<type, rows, epilogue, operand mode>, k_gemm_tile<epilogue, 32-row weight blocks, K split>; "
+          "waves per block, K in segments>, "
+          "k_gemv<type, rows, epilogue, operand mode>, k_gemm_tile<epilogue, 32-row weight blocks, K split, "
+          "32-row activation blocks>; "
           "epilogues 0 store, 1 QKV RoPE + KV append, 2 SiLU gate, 3 residual add, 4 logits + arg-max, "
           "5 attention-output routing.")
     print()
@@ -322,11 +333,16 @@ def main():
                         cfg)
         return
     if args.pmc_mfma_summary:
+        from synth import get_config as _cfg
+        cfg = _cfg(args.config)
+        cf = f"--config {args.config} " if args.config != "llama-1b-8b" else ""
         pmc_mfma_summary(args.pmc_mfma_summary, [
-            "timeout -s KILL 240 rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 "
+            f"timeout -s KILL {args.rocprof_timeout if cf else 240} rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+            "SQ_INSTS_VALU_MFMA_MOPS_F32 "
             f"SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d {odir(args.pmc_mfma_summary)} -o run "
-            "-- python bench.py --warmup 1 --pmc-probe",
-            f"python bench.py --pmc-mfma-summary {args.pmc_mfma_summary} > profiles/mfma_util.md"])
+            f"-- python bench.py {cf}--warmup 1 --pmc-probe",
+            f"python bench.py {cf}" + (f"--rocprof-timeout {args.rocprof_timeout} " if cf else "") +
+            f"--pmc-mfma-summary {args.pmc_mfma_summary} > profiles/{mfma_profile_name(cfg)}"], cfg)
         return
     if args.pmc_summary:
         if len(args.pmc_summary) < 3:
