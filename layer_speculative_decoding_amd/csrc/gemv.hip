@@ -9,6 +9,8 @@
 // per row), multiplies them with up to MR activation rows held in L1/L2, and
 // reduces across the wave.  A unit is a *pair* of rows so that the epilogue
 // sees both halves of a RoPE pair (j, j + hd/2) or a (gate, up) pair.
+#include <cstdlib>
+
 #include "epilogue.h"
 #include "spec_device.h"
 #include "spec_kernels.h"
@@ -51,7 +53,9 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, int KS) {
     constexpr bool staged = XM == XM_STAGED;
     constexpr int E = S::kPer16;
     constexpr bool kPair = epi_is_pair(EPI);
-    __shared__ __align__(16) float xs[staged ? kStageBytes / 4 : 4];
+    // staged operand rows: dynamic LDS of exactly n_sel * MR * K floats (the
+    // call's own size rather than a fixed 32 KB stage per workgroup)
+    extern __shared__ __align__(16) float xs[];
     __shared__ float red[kWaves][kMaxRows][2];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -177,7 +181,11 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, int KS) {
 #pragma unroll
                         for (int e = 0; e < E; ++e) xo[q][m][e] = 0.f;
                         if (m >= p.M || k >= ke) continue;
-                        if constexpr (!kNorm) {
+                        if constexpr (staged) {
+#pragma unroll
+                            for (int e = 0; e < E; e += 4)
+                                Store<float>::unpack(*reinterpret_cast<const uint4 *>(xl + m * K + k + e), xo[q][m] + e);
+                        } else if constexpr (!kNorm) {
                             int64_t off = (int64_t)m * Ks + k;
                             if (kSegOk && p.kseg > 1) {
                                 const int sg = seg_of(k);
@@ -185,10 +193,6 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, int KS) {
                             }
 #pragma unroll
                             for (int e = 0; e < E; e += 4) Store<float>::unpack(ld16(xp + off + e), xo[q][m] + e);
-                        } else if constexpr (staged) {
-#pragma unroll
-                            for (int e = 0; e < E; e += 4)
-                                Store<float>::unpack(*reinterpret_cast<const uint4 *>(xl + m * K + k + e), xo[q][m] + e);
                         } else {
                             if constexpr (E == 8) x_norm8(p, sel, hrow[m], k, inv[m], xo[q][m]);
                             else x_norm4(p, sel, hrow[m], k, inv[m], xo[q][m]);
@@ -281,20 +285,24 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, int KS) {
     }
 }
 
-template <typename T, int EPI, int XM>
-void launch_tex(const GemvParams &p, int grid, int ks, hipStream_t s) {
-    dim3 g(grid), b(256);
-    if (p.M <= 1) hipLaunchKernelGGL((k_gemv<T, 1, EPI, XM>), g, b, 0, s, p, ks);
-    else if (p.M <= 2) hipLaunchKernelGGL((k_gemv<T, 2, EPI, XM>), g, b, 0, s, p, ks);
-    else if (p.M <= 4) hipLaunchKernelGGL((k_gemv<T, 4, EPI, XM>), g, b, 0, s, p, ks);
-    else hipLaunchKernelGGL((k_gemv<T, 8, EPI, XM>), g, b, 0, s, p, ks);
+// LDS bytes of the staged operand rows (every set member's MR rows of K floats)
+int64_t gemv_stage_bytes(const GemvParams &p) {
+    const int mr = p.M <= 1 ? 1 : (p.M <= 2 ? 2 : (p.M <= 4 ? 4 : 8));
+    const int64_t n_sel = (int64_t)p.n_units * 2 / p.rows_per_sel;
+    return n_sel * mr * p.K * 4;
 }
 
 // normalised (float32) operands go through LDS when every set member's rows fit
-bool gemv_staged(const GemvParams &p) {
-    const int mr = p.M <= 1 ? 1 : (p.M <= 2 ? 2 : (p.M <= 4 ? 4 : 8));
-    const int64_t n_sel = (int64_t)p.n_units * 2 / p.rows_per_sel;
-    return n_sel * mr * p.K * 4 <= kStageBytes;
+bool gemv_staged(const GemvParams &p) { return gemv_stage_bytes(p) <= kStageBytes; }
+
+template <typename T, int EPI, int XM>
+void launch_tex(const GemvParams &p, int grid, int ks, hipStream_t s) {
+    dim3 g(grid), b(256);
+    const size_t lds = XM == XM_STAGED ? (size_t)gemv_stage_bytes(p) : 0;
+    if (p.M <= 1) hipLaunchKernelGGL((k_gemv<T, 1, EPI, XM>), g, b, lds, s, p, ks);
+    else if (p.M <= 2) hipLaunchKernelGGL((k_gemv<T, 2, EPI, XM>), g, b, lds, s, p, ks);
+    else if (p.M <= 4) hipLaunchKernelGGL((k_gemv<T, 4, EPI, XM>), g, b, lds, s, p, ks);
+    else hipLaunchKernelGGL((k_gemv<T, 8, EPI, XM>), g, b, lds, s, p, ks);
 }
 
 template <typename T, int EPI>
@@ -448,12 +456,45 @@ __global__ __launch_bounds__(256) void k_embed(EmbedParams p) {
 
 int gemv_max_rows() { return kMaxRows; }
 
-// Waves per unit: split K while the launch has fewer than 4096 waves and each
-// part keeps at least one 16-byte step per lane.
+int env_splits(const char *name) {
+    const char *e = getenv(name);
+    const int n = e ? atoi(e) : 0;
+    return (n == 1 || n == 2 || n == 4) ? n : 0;
+}
+
+// Workgroups per CU of the normalised-operand products other than the head
+// (SPEC_GEMV_NORM_WG overrides, 1 .. 8).
+int norm_wg_per_cu() {
+    static const int v = [] {
+        const char *e = getenv("SPEC_GEMV_NORM_WG");
+        const int n = e ? atoi(e) : 4;
+        return n < 1 ? 1 : (n > 8 ? 8 : n);
+    }();
+    return v;
+}
+
+// Waves per unit.  Normalised-operand products other than the head: one wave
+// per unit over the whole of K (measured on the 1B draft step, one row: the
+// QKV launches of one and two layers, 1536 / 3072 units, took 12.4 us on
+// average with two or four waves per unit, which leaves a second round of
+// units for half the workgroups, and 10.8 us with one; the draft step went
+// from 741 to 727 us; the gate/up product already had one).  Plain-operand
+// products split K in two while the launch has fewer than 4096 waves and each
+// part keeps at least one 16-byte step per lane (four-way splits of the
+// one-row down and O products: draft step 724-728 us, two-way 717-721 us);
+// the head as long as both hold and the split is at most four.
+// SPEC_GEMV_KS / SPEC_GEMV_KS_PLAIN (1, 2 or 4) fix the split of the
+// normalised / plain-operand products.
 int gemv_splits(const GemvParams &p, int elem_bytes) {
     const int step = kWave * 16 / elem_bytes;
+    const bool norm = p.xmode == X_NORM && p.epi != EPI_LOGITS;
+    static const int forced_norm = env_splits("SPEC_GEMV_KS");
+    static const int forced_plain = env_splits("SPEC_GEMV_KS_PLAIN");
+    if (norm) return forced_norm ? forced_norm : 1;
+    if (p.xmode != X_NORM && forced_plain) return forced_plain;
+    const int ks_max = p.xmode != X_NORM ? 2 : kWaves;
     int ks = 1;
-    while (ks < kWaves && (int64_t)p.n_units * ks < 4096 && p.K >= 2 * ks * step) ks *= 2;
+    while (ks < ks_max && (int64_t)p.n_units * ks < 4096 && p.K >= 2 * ks * step) ks *= 2;
     return ks;
 }
 
@@ -464,9 +505,12 @@ int gemv_grid(const GemvParams &p, int ks) {
     const int upb = kWaves / ks;
     int g = (p.n_units + upb - 1) / upb;
     // measured at one row (1B draft): four workgroups per CU for the QKV and
-    // gate/up products (11.9 / 16.9 us against 12.3 / 17.5 with three), three
-    // for the sampling head (84.6 us against 100.6 with four)
-    const int cap = p.xmode != X_NORM ? kMaxGrid : (p.epi == EPI_LOGITS ? 3 * 256 : 4 * 256);
+    // gate/up products (11.9 / 16.9 us against 12.3 / 17.5 with three; with
+    // one wave per unit, draft step 727 us against 749 with three, 773 with
+    // six and 772 with eight, whose second dispatch round the 116-VGPR
+    // gate/up kernel cannot hold resident), three for the sampling head (84.6
+    // us against 100.6 with four)
+    const int cap = p.xmode != X_NORM ? kMaxGrid : (p.epi == EPI_LOGITS ? 3 * 256 : norm_wg_per_cu() * 256);
     return g < cap ? (g < 1 ? 1 : g) : cap;
 }
 
