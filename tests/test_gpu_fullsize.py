@@ -17,7 +17,8 @@ import pytest
 import torch
 
 from oracle import philox
-from oracle.model import MLP_PARALLEL, MLP_SEQUENTIAL, KVCache, OracleModel, forward, fuzzy_step
+from oracle.model import (MLP_PARALLEL, MLP_SEQUENTIAL, KVCache, OracleModel, attention, embed, forward,
+                          fuzzy_step, linear, mlp_part, rmsnorm, rope)
 from oracle.plan import default_group_plan, plan_offsets
 from oracle.sampling import accept_resample, sample_from_logits
 from synth import get_config, make_weights
@@ -234,6 +235,69 @@ def test_fullsize_prompt_prefill(cfg_name, which, P, batch, layers):
     del gm, w, om, okv, gkv
     gc.collect()
     torch.cuda.empty_cache()
+
+
+def test_fullsize_70b_prefill_sampled_rows():
+    """The 70B-shaped base prefill in the launch configuration the benchmark
+    times: four sequences of 8191 prompt rows in one call, so 32764 activation
+    rows through the tiled products (their largest grids and the XCD-grouped
+    tile order) and the prompt attention over the whole 8191-row prefix, here
+    on the first two base layers.  Layer 0's keys and values depend on one
+    product only, so the oracle forms them for every row and compares them
+    all; for sampled rows it continues through layer 0's attention, O and MLP
+    (on the oracle's own layer-0 cache) and compares the keys and values layer
+    1 wrote there, which depend on every product of the prefill."""
+    from layer_speculative_decoding_amd import api
+    cfg = get_config("llama-8b-70b")
+    sh = cfg.base.replace(n_layers=2)
+    B, P = cfg.batch, cfg.prompt_len - 1
+    hq, hkv, hd, th = sh.n_q_heads, sh.n_kv_heads, sh.head_dim, sh.rope_theta
+    say(f"fullsize prefill llama-8b-70b base, sampled rows: B={B} x P={P} rows in one call, 2 of "
+        f"{cfg.base.n_layers} layers")
+    w = make_weights(sh, cfg.seed_base, device="cuda")
+    torch.cuda.synchronize()
+    gm = api.SpecModel(sh, w)
+    gkv = api.KVCache(sh, B, P + 2)
+    rng = np.random.default_rng(cfg.seed_base + 11)
+    toks = rng.integers(0, sh.vocab, size=(B, P)).astype(np.int32)
+    wsb = ws(api.spec_workspace_bytes(gm, B, P, 1))
+    api.spec_verify_forward(gm, gkv, B, i32(toks), i32([0] * B), P, P - 1, None, wsb)
+    torch.cuda.synchronize()
+    del wsb
+    kg, vg = gkv.k.float().cpu().numpy(), gkv.v.float().cpu().numpy()    # [L][B][hkv][cap][hd]
+    om = OracleModel.from_torch(sh, w, np.float32)
+    del gm, gkv, w
+    gc.collect()
+    torch.cuda.empty_cache()
+    say("  GPU prefill done, oracle weights ready")
+    # block and tile edges of the prompt kernel and the tiled products, the
+    # last rows, and a few others
+    rows = sorted({0, 1, 15, 16, 31, 32, 127, 128, 1023, 2047, 2048, 4095, 4096, 6143, P - 2, P - 1}
+                  | {int(r) for r in rng.integers(0, P, 8)})
+    n = len(rows)
+    for b in range(B):
+        h0 = embed(om, toks[b])
+        qkv = linear(rmsnorm(h0, om.w["attn_norm"][0], sh.rms_eps), om.w["wqkv"][0])
+        K0 = om.rnd(rope(qkv[:, hq * hd:(hq + hkv) * hd].reshape(P, hkv, hd), range(P), th)).transpose(1, 0, 2)
+        V0 = om.rnd(qkv[:, (hq + hkv) * hd:].reshape(P, hkv, hd)).transpose(1, 0, 2)
+        e0k = rel_linf(kg[0, b, :, :P], K0)
+        e0v = rel_linf(vg[0, b, :, :P], V0)
+        q = rope(qkv[rows, :hq * hd].reshape(n, hq, hd), rows, th)
+        del qkv
+        o = attention(q, K0, V0, rows, hkv).reshape(n, hq * hd)
+        h1 = h0[rows] + linear(o, om.w["wo"][0])
+        h2 = h1 + mlp_part(om, 0, h1)
+        qkv1 = linear(rmsnorm(h2, om.w["attn_norm"][1], sh.rms_eps), om.w["wqkv"][1])
+        K1 = om.rnd(rope(qkv1[:, hq * hd:(hq + hkv) * hd].reshape(n, hkv, hd), rows, th)).transpose(1, 0, 2)
+        V1 = om.rnd(qkv1[:, (hq + hkv) * hd:].reshape(n, hkv, hd)).transpose(1, 0, 2)
+        e1k = rel_linf(kg[1, b][:, rows], K1)
+        e1v = rel_linf(vg[1, b][:, rows], V1)
+        say(f"  b={b}: layer 0 K/V (all {P} rows) rel {e0k:.2e} / {e0v:.2e}; layer 1 K/V at {n} sampled rows "
+            f"rel {e1k:.2e} / {e1v:.2e}")
+        assert e0k < 1e-2 and e0v < 1e-2, (e0k, e0v)
+        assert e1k < TOL_BF16 and e1v < TOL_BF16, (e1k, e1v)
+    del om
+    gc.collect()
 
 
 @pytest.mark.parametrize("cfg_name", ["llama-1b-8b", "llama-1b-8b-n4", "qwen-0.5b-7b", "llama-8b-70b"])
