@@ -17,8 +17,8 @@ import pytest
 import torch
 
 from oracle import philox
-from oracle.model import (MLP_PARALLEL, MLP_SEQUENTIAL, KVCache, OracleModel, attention, embed, forward,
-                          fuzzy_step, linear, mlp_part, rmsnorm, rope)
+from oracle.model import (MLP_PARALLEL, MLP_SEQUENTIAL, KVCache, OracleModel, attention, embed, final_logits,
+                          forward, fuzzy_step, linear, mlp_part, rmsnorm, rope)
 from oracle.plan import default_group_plan, plan_offsets
 from oracle.sampling import accept_resample, sample_from_logits
 from synth import get_config, make_weights
@@ -296,6 +296,65 @@ def test_fullsize_70b_prefill_sampled_rows():
             f"rel {e1k:.2e} / {e1v:.2e}")
         assert e0k < 1e-2 and e0v < 1e-2, (e0k, e0v)
         assert e1k < TOL_BF16 and e1v < TOL_BF16, (e1k, e1v)
+    del om
+    gc.collect()
+
+
+def test_fullsize_70b_draft_calibration_prefill():
+    """The 8B-shaped draft's calibration over the four 8192-token prompts in
+    one call (32768 rows, the benchmark's draft prefill), on the draft's
+    first layer: every row's keys and values against the oracle, then the
+    last row of each sequence through the oracle's attention over the whole
+    prompt, MLP, final norm and head, against the GPU's last-row logits (the
+    gathered-row head) and its sampled d_1."""
+    from layer_speculative_decoding_amd import api
+    cfg = get_config("llama-8b-70b")
+    sh = cfg.draft.replace(n_layers=1)
+    B, P = cfg.batch, cfg.prompt_len
+    hq, hkv, hd, th = sh.n_q_heads, sh.n_kv_heads, sh.head_dim, sh.rope_theta
+    inv_t = float(np.float32(1.0 / cfg.temperatures[-1])) if cfg.temperatures[-1] > 0 else 1.0
+    say(f"fullsize calibration prefill llama-8b-70b draft: B={B} x P={P} rows in one call, 1 of "
+        f"{cfg.draft.n_layers} layers, T={cfg.temperatures[-1]}")
+    w = make_weights(sh, cfg.seed_draft, device="cuda")
+    torch.cuda.synchronize()
+    gm = api.SpecModel(sh, w)
+    gkv = api.KVCache(sh, B, P + 2)
+    rng = np.random.default_rng(cfg.seed_draft + 13)
+    toks = rng.integers(0, sh.vocab, size=(B, P)).astype(np.int32)
+    wsb = ws(api.spec_workspace_bytes(gm, B, P, 1))
+    last = torch.zeros(B, sh.vocab, device="cuda")
+    out = torch.zeros(B, dtype=torch.int32, device="cuda")
+    api.spec_calibrate_kv(gm, gkv, B, i32(toks), i32([0] * B), None, P, P - 1, inv_t, 79, last, sh.vocab, out, 1,
+                          wsb)
+    torch.cuda.synchronize()
+    del wsb
+    kg, vg = gkv.k.float().cpu().numpy(), gkv.v.float().cpu().numpy()
+    zg, tg = last.cpu().numpy(), out.cpu().numpy()
+    om = OracleModel.from_torch(sh, w, np.float32)
+    del gm, gkv, w, last, out
+    gc.collect()
+    torch.cuda.empty_cache()
+    for b in range(B):
+        h0 = embed(om, toks[b])
+        qkv = linear(rmsnorm(h0, om.w["attn_norm"][0], sh.rms_eps), om.w["wqkv"][0])
+        K0 = om.rnd(rope(qkv[:, hq * hd:(hq + hkv) * hd].reshape(P, hkv, hd), range(P), th)).transpose(1, 0, 2)
+        V0 = om.rnd(qkv[:, (hq + hkv) * hd:].reshape(P, hkv, hd)).transpose(1, 0, 2)
+        ek = rel_linf(kg[0, b, :, :P], K0)
+        ev = rel_linf(vg[0, b, :, :P], V0)
+        q = rope(qkv[P - 1:, :hq * hd].reshape(1, hq, hd), [P - 1], th)
+        o = attention(q, K0, V0, [P - 1], hkv).reshape(1, hq * hd)
+        h1 = h0[P - 1:] + linear(o, om.w["wo"][0])
+        h2 = h1 + mlp_part(om, 0, h1)
+        zo = final_logits(om, h2)[0]
+        err = rel_linf(zg[b], zo)
+        t_or, mg = sample_from_logits(zo, inv_t, 79, b, P, philox.DRAFT)
+        decided = mg >= exclusion(zg[b], zo, inv_t)
+        say(f"  b={b}: K/V (all {P} rows) rel {ek:.2e} / {ev:.2e}; last-row logits rel {err:.2e}; d_1 GPU "
+            f"{tg[b]} oracle {t_or} (margin {mg:.2e}{'' if decided else ', excluded'})")
+        assert ek < 1e-2 and ev < 1e-2, (ek, ev)
+        assert err < TOL_BF16
+        if decided:
+            assert tg[b] == t_or
     del om
     gc.collect()
 
