@@ -237,6 +237,40 @@ def test_fullsize_prompt_prefill(cfg_name, which, P, batch, layers):
     torch.cuda.empty_cache()
 
 
+def layer0_kv(om, toks_b):
+    """Layer 0's keys and values [hkv][P][hd] for every prompt row (positions
+    0 .. P-1) and its QKV rows, as the oracle's forward writes them."""
+    sh = om.shape
+    hq, hkv, hd, P = sh.n_q_heads, sh.n_kv_heads, sh.head_dim, len(toks_b)
+    h0 = embed(om, toks_b)
+    qkv = linear(rmsnorm(h0, om.w["attn_norm"][0], sh.rms_eps), om.w["wqkv"][0])
+    K0 = om.rnd(rope(qkv[:, hq * hd:(hq + hkv) * hd].reshape(P, hkv, hd), range(P), sh.rope_theta)).transpose(1, 0, 2)
+    V0 = om.rnd(qkv[:, (hq + hkv) * hd:].reshape(P, hkv, hd)).transpose(1, 0, 2)
+    return h0, qkv, K0, V0
+
+
+def layer0_output(om, h0, qkv, K0, V0, rows):
+    """Layer 0's output at prompt rows `rows` (causal attention over the rows
+    before each), given layer0_kv's results."""
+    sh = om.shape
+    hq, hkv, hd, n = sh.n_q_heads, sh.n_kv_heads, sh.head_dim, len(rows)
+    q = rope(qkv[rows, :hq * hd].reshape(n, hq, hd), rows, sh.rope_theta)
+    o = attention(q, K0, V0, rows, hkv).reshape(n, hq * hd)
+    h1 = h0[rows] + linear(o, om.w["wo"][0])
+    return h1 + mlp_part(om, 0, h1)
+
+
+def layer1_kv_at(om, h2, rows):
+    """Layer 1's keys and values [hkv][n][hd] at prompt rows `rows` from layer
+    0's output h2 there."""
+    sh = om.shape
+    hq, hkv, hd, n = sh.n_q_heads, sh.n_kv_heads, sh.head_dim, len(rows)
+    qkv1 = linear(rmsnorm(h2, om.w["attn_norm"][1], sh.rms_eps), om.w["wqkv"][1])
+    K1 = om.rnd(rope(qkv1[:, hq * hd:(hq + hkv) * hd].reshape(n, hkv, hd), rows, sh.rope_theta)).transpose(1, 0, 2)
+    V1 = om.rnd(qkv1[:, (hq + hkv) * hd:].reshape(n, hkv, hd)).transpose(1, 0, 2)
+    return K1, V1
+
+
 def test_fullsize_70b_prefill_sampled_rows():
     """The 70B-shaped base prefill in the launch configuration the benchmark
     times: four sequences of 8191 prompt rows in one call, so 32764 activation
@@ -251,7 +285,6 @@ def test_fullsize_70b_prefill_sampled_rows():
     cfg = get_config("llama-8b-70b")
     sh = cfg.base.replace(n_layers=2)
     B, P = cfg.batch, cfg.prompt_len - 1
-    hq, hkv, hd, th = sh.n_q_heads, sh.n_kv_heads, sh.head_dim, sh.rope_theta
     say(f"fullsize prefill llama-8b-70b base, sampled rows: B={B} x P={P} rows in one call, 2 of "
         f"{cfg.base.n_layers} layers")
     w = make_weights(sh, cfg.seed_base, device="cuda")
@@ -276,20 +309,12 @@ def test_fullsize_70b_prefill_sampled_rows():
                   | {int(r) for r in rng.integers(0, P, 8)})
     n = len(rows)
     for b in range(B):
-        h0 = embed(om, toks[b])
-        qkv = linear(rmsnorm(h0, om.w["attn_norm"][0], sh.rms_eps), om.w["wqkv"][0])
-        K0 = om.rnd(rope(qkv[:, hq * hd:(hq + hkv) * hd].reshape(P, hkv, hd), range(P), th)).transpose(1, 0, 2)
-        V0 = om.rnd(qkv[:, (hq + hkv) * hd:].reshape(P, hkv, hd)).transpose(1, 0, 2)
+        h0, qkv, K0, V0 = layer0_kv(om, toks[b])
         e0k = rel_linf(kg[0, b, :, :P], K0)
         e0v = rel_linf(vg[0, b, :, :P], V0)
-        q = rope(qkv[rows, :hq * hd].reshape(n, hq, hd), rows, th)
+        h2 = layer0_output(om, h0, qkv, K0, V0, rows)
         del qkv
-        o = attention(q, K0, V0, rows, hkv).reshape(n, hq * hd)
-        h1 = h0[rows] + linear(o, om.w["wo"][0])
-        h2 = h1 + mlp_part(om, 0, h1)
-        qkv1 = linear(rmsnorm(h2, om.w["attn_norm"][1], sh.rms_eps), om.w["wqkv"][1])
-        K1 = om.rnd(rope(qkv1[:, hq * hd:(hq + hkv) * hd].reshape(n, hkv, hd), rows, th)).transpose(1, 0, 2)
-        V1 = om.rnd(qkv1[:, (hq + hkv) * hd:].reshape(n, hkv, hd)).transpose(1, 0, 2)
+        K1, V1 = layer1_kv_at(om, h2, rows)
         e1k = rel_linf(kg[1, b][:, rows], K1)
         e1v = rel_linf(vg[1, b][:, rows], V1)
         say(f"  b={b}: layer 0 K/V (all {P} rows) rel {e0k:.2e} / {e0v:.2e}; layer 1 K/V at {n} sampled rows "
@@ -311,7 +336,6 @@ def test_fullsize_70b_draft_calibration_prefill():
     cfg = get_config("llama-8b-70b")
     sh = cfg.draft.replace(n_layers=1)
     B, P = cfg.batch, cfg.prompt_len
-    hq, hkv, hd, th = sh.n_q_heads, sh.n_kv_heads, sh.head_dim, sh.rope_theta
     inv_t = float(np.float32(1.0 / cfg.temperatures[-1])) if cfg.temperatures[-1] > 0 else 1.0
     say(f"fullsize calibration prefill llama-8b-70b draft: B={B} x P={P} rows in one call, 1 of "
         f"{cfg.draft.n_layers} layers, T={cfg.temperatures[-1]}")
@@ -335,17 +359,10 @@ def test_fullsize_70b_draft_calibration_prefill():
     gc.collect()
     torch.cuda.empty_cache()
     for b in range(B):
-        h0 = embed(om, toks[b])
-        qkv = linear(rmsnorm(h0, om.w["attn_norm"][0], sh.rms_eps), om.w["wqkv"][0])
-        K0 = om.rnd(rope(qkv[:, hq * hd:(hq + hkv) * hd].reshape(P, hkv, hd), range(P), th)).transpose(1, 0, 2)
-        V0 = om.rnd(qkv[:, (hq + hkv) * hd:].reshape(P, hkv, hd)).transpose(1, 0, 2)
+        h0, qkv, K0, V0 = layer0_kv(om, toks[b])
         ek = rel_linf(kg[0, b, :, :P], K0)
         ev = rel_linf(vg[0, b, :, :P], V0)
-        q = rope(qkv[P - 1:, :hq * hd].reshape(1, hq, hd), [P - 1], th)
-        o = attention(q, K0, V0, [P - 1], hkv).reshape(1, hq * hd)
-        h1 = h0[P - 1:] + linear(o, om.w["wo"][0])
-        h2 = h1 + mlp_part(om, 0, h1)
-        zo = final_logits(om, h2)[0]
+        zo = final_logits(om, layer0_output(om, h0, qkv, K0, V0, [P - 1]))[0]
         err = rel_linf(zg[b], zo)
         t_or, mg = sample_from_logits(zo, inv_t, 79, b, P, philox.DRAFT)
         decided = mg >= exclusion(zg[b], zo, inv_t)
