@@ -456,7 +456,7 @@ __global__ __launch_bounds__(256) void k_embed(EmbedParams p) {
 
 int gemv_max_rows() { return kMaxRows; }
 
-static int env_splits(const char *name) {
+int env_splits(const char *name) {
     const char *e = getenv(name);
     const int n = e ? atoi(e) : 0;
     return (n == 1 || n == 2 || n == 4) ? n : 0;
@@ -464,7 +464,7 @@ static int env_splits(const char *name) {
 
 // Workgroups per CU of the normalised-operand products other than the head
 // (SPEC_GEMV_NORM_WG overrides, 1 .. 8).
-static int norm_wg_per_cu() {
+int norm_wg_per_cu() {
     static const int v = [] {
         const char *e = getenv("SPEC_GEMV_NORM_WG");
         const int n = e ? atoi(e) : 4;
